@@ -1,0 +1,189 @@
+"""CPU oracle for the batch-invariant bf16 GEMM -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never does, and shares no code with it.
+
+Contents:
+
+* ``gemm_f64``      fp64 reference y = x W^T over bf16 inputs, plus the
+                    per-element scale a = sum_k |x_k w_k| (``oracle.c``);
+* ``gemm_i64``      exact int64 result for integer-valued inputs;
+* ``grouped_f64``   the MoE expert-grouped variant;
+* ``fold_f32``      the in-order fp32 combine of split partial sums;
+* ``exact``         exact-rational brute force (``oracle/exact.py``).
+
+Each function cites the passage it follows in ``oracle.c``.  Every function is
+pinned by tests that do not re-use it (exact rationals, integer closed forms,
+numpy's fp64 matmul, identity and one-hot special cases).  The specific fp32
+bits the GPU returns are not fixed by the pages (any fixed reduction tree is a
+correct answer); the oracle judges them through the accuracy bound
+``|y - y_ref| <= 1e-4 * a``, and bit-level batch invariance is checked GPU
+against GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+GCC_FLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile one oracle C source into a shared library with gcc."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = False) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        compile_source(_SRC, _LIB)
+    return _LIB
+
+
+def open_library(path: str):
+    """Load an oracle shared library and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    L = ctypes.c_long
+    I = ctypes.c_int
+    lib.oracle_gemm_f64.argtypes = [P, P, L, L, L, P, L, P, P, I]
+    lib.oracle_gemm_i64.argtypes = [P, P, L, L, L, P, L, P, I]
+    lib.oracle_grouped_f64.argtypes = [P, P, L, L, L, P, L, P, L, P, P, I]
+    lib.oracle_fold_f32.argtypes = [P, L, L, P]
+    lib.oracle_max_threads.argtypes = []
+    for f in (lib.oracle_gemm_f64, lib.oracle_gemm_i64, lib.oracle_grouped_f64,
+              lib.oracle_fold_f32, lib.oracle_max_threads):
+        f.restype = ctypes.c_int
+    return lib
+
+
+def _load(lib=None):
+    global _lib
+    if lib is not None:
+        return lib
+    with _lock:
+        if _lib is None:
+            _lib = open_library(build())
+    return _lib
+
+
+def _u16(a, ndim):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16 or a.ndim != ndim:
+        raise TypeError("expected a uint16 (bf16 bits) array of rank %d, got %s %s" % (ndim, a.dtype, a.shape))
+    return a
+
+
+def _rows(rows, m):
+    if rows is None:
+        return None, m
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    return r, int(r.size)
+
+
+def max_threads(lib=None) -> int:
+    """Threads an OpenMP region of the oracle uses by default."""
+    return int(_load(lib).oracle_max_threads())
+
+
+def gemm_f64(x_bits, w_bits, rows=None, threads: int = 0, lib=None):
+    """fp64 ``y[r] = x[rows[r]] @ w.T`` and ``a[r] = |x[rows[r]]| @ |w|.T``.
+
+    ``x_bits`` [M,K] and ``w_bits`` [N,K] are bf16 bit patterns (uint16).
+    ``rows`` selects rows of x (default: all).  Returns ``(y, a)`` float64
+    arrays of shape [len(rows), N].
+    """
+    x = _u16(x_bits, 2)
+    w = _u16(w_bits, 2)
+    if x.shape[1] != w.shape[1]:
+        raise ValueError("K mismatch")
+    m, k = x.shape
+    n = w.shape[0]
+    r, nr = _rows(rows, m)
+    y = np.empty((nr, n), np.float64)
+    a = np.empty((nr, n), np.float64)
+    rc = _load(lib).oracle_gemm_f64(x.ctypes.data, w.ctypes.data, m, n, k,
+                                 None if r is None else r.ctypes.data, nr,
+                                 y.ctypes.data, a.ctypes.data, int(threads))
+    if rc != 0:
+        raise ValueError("oracle_gemm_f64 rejected its arguments (%d)" % rc)
+    return y, a
+
+
+def gemm_i64(x_bits, w_bits, rows=None, threads: int = 0, lib=None):
+    """Exact int64 ``x @ w.T`` for integer-valued bf16 inputs (|v| <= 256)."""
+    x = _u16(x_bits, 2)
+    w = _u16(w_bits, 2)
+    if x.shape[1] != w.shape[1]:
+        raise ValueError("K mismatch")
+    m, k = x.shape
+    n = w.shape[0]
+    r, nr = _rows(rows, m)
+    y = np.empty((nr, n), np.int64)
+    rc = _load(lib).oracle_gemm_i64(x.ctypes.data, w.ctypes.data, m, n, k,
+                                 None if r is None else r.ctypes.data, nr,
+                                 y.ctypes.data, int(threads))
+    if rc == -2:
+        raise ValueError("gemm_i64 needs integer-valued inputs with |v| <= 256")
+    if rc != 0:
+        raise ValueError("oracle_gemm_i64 rejected its arguments (%d)" % rc)
+    return y
+
+
+def grouped_f64(x_bits, w_bits, offsets, rows=None, threads: int = 0, lib=None):
+    """Expert-grouped GEMM: row i of x uses expert e with offsets[e] <= i < offsets[e+1].
+
+    ``w_bits`` is [E,N,K]; ``offsets`` is [E+1] int32, 0 .. R, nondecreasing.
+    Returns ``(y, a)`` of shape [len(rows), N].
+    """
+    x = _u16(x_bits, 2)
+    w = _u16(w_bits, 3)
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    e, n, k = w.shape
+    if x.shape[1] != k or off.shape != (e + 1,):
+        raise ValueError("shape mismatch")
+    rr = x.shape[0]
+    r, nr = _rows(rows, rr)
+    y = np.empty((nr, n), np.float64)
+    a = np.empty((nr, n), np.float64)
+    rc = _load(lib).oracle_grouped_f64(x.ctypes.data, w.ctypes.data, e, n, k, off.ctypes.data, rr,
+                                    None if r is None else r.ctypes.data, nr,
+                                    y.ctypes.data, a.ctypes.data, int(threads))
+    if rc != 0:
+        raise ValueError("oracle_grouped_f64 rejected its arguments (%d)" % rc)
+    return y, a
+
+
+def fold_f32(parts, lib=None):
+    """In-order fp32 fold ``((p[0] + p[1]) + p[2]) + ...`` over axis 0."""
+    p = np.ascontiguousarray(parts, dtype=np.float32)
+    s = p.shape[0]
+    flat = p.reshape(s, -1)
+    out = np.empty(flat.shape[1], np.float32)
+    rc = _load(lib).oracle_fold_f32(flat.ctypes.data, s, flat.shape[1], out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_fold_f32 rejected its arguments (%d)" % rc)
+    return out.reshape(p.shape[1:])
+
+
+def within_bound(y_gpu, y_ref, a, rel: float = 1e-4):
+    """Boolean mask of ``|y_gpu - y_ref| <= rel * a``, evaluated in fp64.
+
+    Where ``a == 0`` every product is zero and ``y_gpu`` must be exactly zero.
+    """
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    return np.abs(y_gpu - y_ref) <= rel * a

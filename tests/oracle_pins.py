@@ -1,0 +1,214 @@
+"""The pin battery for the CPU oracle, shared by the oracle tests and the
+planted-mistake tests (which run it against deliberately broken copies of the
+oracle and expect it to fail).
+
+Every check compares the oracle with something other than itself: exact
+rationals, integer closed forms, numpy's fp64 matmul, hand-worked fixtures,
+identity and one-hot special cases.
+"""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from oracle import exact
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+EPS64 = 2.0 ** -53
+
+
+def wide_bf16(seed, shape, emin=-30, emax=30):
+    """bf16 values spread over many binades, random signs (no subnormals)."""
+    g = synth.rng(seed)
+    mant = g.uniform(1.0, 2.0, size=shape).astype(np.float32)
+    e = g.integers(emin, emax + 1, size=shape)
+    s = np.where(g.random(size=shape) < 0.5, -1.0, 1.0)
+    v = (s * mant * np.exp2(e)).astype(np.float32)
+    zero = g.random(size=shape) < 0.1
+    v[zero] = 0.0
+    return synth.f32_to_bf16_bits(v)
+
+
+def load_gemm_golden():
+    cases, cur, sect = [], None, None
+    for line in open(os.path.join(GOLDEN, "tiny_gemm.txt")):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        if line.startswith("case "):
+            cur = {"name": line[5:], "x": [], "w": [], "y": [], "a": []}
+            cases.append(cur)
+            continue
+        if line in ("x", "w", "y", "a"):
+            sect = line
+            continue
+        cur[sect].append([float(t) for t in line.split()])
+    return cases
+
+
+def load_fold_golden():
+    out = []
+    for line in open(os.path.join(GOLDEN, "fold_fp32.txt")):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        lhs, rhs = line.split("->")
+        parts = np.array([int(t, 16) for t in lhs.split()], dtype=np.uint32).view(np.float32)
+        out.append((parts, int(rhs.strip(), 16)))
+    return out
+
+
+# --- individual pins; each returns None or raises AssertionError -------------
+
+def pin_exact_rationals(lib=None):
+    for seed, (m, n, k) in enumerate([(1, 1, 1), (2, 3, 7), (4, 4, 64), (3, 2, 33), (4, 1, 48)]):
+        x = wide_bf16(100 + seed, (m, k))
+        w = wide_bf16(200 + seed, (n, k))
+        y, a = oracle.gemm_f64(x, w, lib=lib)
+        ye, ae = exact.gemm_exact(x, w)
+        for i in range(m):
+            for j in range(n):
+                bound = Fraction(max(k - 1, 0)) * Fraction(EPS64) * ae[i][j]
+                assert abs(Fraction(y[i, j]) - ye[i][j]) <= bound, (seed, i, j)
+                assert abs(Fraction(a[i, j]) - ae[i][j]) <= bound, (seed, i, j)
+
+
+def pin_golden_gemm(lib=None):
+    for c in load_gemm_golden():
+        x = synth.f32_to_bf16_bits(np.array(c["x"], np.float32))
+        w = synth.f32_to_bf16_bits(np.array(c["w"], np.float32))
+        assert np.array_equal(synth.bf16_bits_to_f32(x), np.array(c["x"], np.float32)), "fixture not exact in bf16"
+        y, a = oracle.gemm_f64(x, w, lib=lib)
+        assert np.array_equal(y, np.array(c["y"])), c["name"]
+        assert np.array_equal(a, np.array(c["a"])), c["name"]
+
+
+def pin_integer_closed_forms(lib=None):
+    # all ones: every entry is K
+    for k in (1, 7, 512, 14336):
+        x = synth.f32_to_bf16_bits(np.ones((2, k), np.float32))
+        w = synth.f32_to_bf16_bits(np.ones((3, k), np.float32))
+        y, a = oracle.gemm_f64(x, w, lib=lib)
+        assert np.all(y == k) and np.all(a == k)
+        assert np.all(oracle.gemm_i64(x, w, lib=lib) == k)
+    # x = 1, w[n][k] = (k mod 7) - 3: whole periods sum to 0, the rest r terms
+    # sum to r(r-1)/2 - 3r
+    for k in (5, 14, 100, 3584):
+        r = k % 7
+        expect = r * (r - 1) // 2 - 3 * r
+        x = synth.f32_to_bf16_bits(np.ones((1, k), np.float32))
+        wv = (np.arange(k) % 7 - 3).astype(np.float32)
+        w = synth.f32_to_bf16_bits(np.stack([wv, -wv]))
+        y, _ = oracle.gemm_f64(x, w, lib=lib)
+        assert y[0, 0] == expect and y[0, 1] == -expect, (k, y, expect)
+        yi = oracle.gemm_i64(x, w, lib=lib)
+        assert yi[0, 0] == expect and yi[0, 1] == -expect
+    # x[i][k] = i+1 (rows scale), w[n][k] = 1 if k <= n else 0: y = (i+1)(n+1)
+    m, n, k = 3, 5, 8
+    x = synth.f32_to_bf16_bits(np.repeat(np.arange(1, m + 1, dtype=np.float32)[:, None], k, 1))
+    w = synth.f32_to_bf16_bits(np.tril(np.ones((n, k), np.float32)))
+    y, _ = oracle.gemm_f64(x, w, lib=lib)
+    assert np.array_equal(y, np.outer(np.arange(1, m + 1), np.arange(1, n + 1)).astype(float))
+
+
+def pin_integer_random(lib=None):
+    for seed, (m, n, k) in enumerate([(5, 7, 512), (3, 16, 14336), (2, 9, 3584)]):
+        x = synth.int_bf16(300 + seed, (m, k))
+        w = synth.int_bf16(400 + seed, (n, k))
+        xi = synth.bf16_bits_to_f32(x).astype(np.int64)
+        wi = synth.bf16_bits_to_f32(w).astype(np.int64)
+        ref = xi @ wi.T  # numpy int64 matmul: an independent routine
+        assert np.array_equal(oracle.gemm_i64(x, w, lib=lib), ref)
+        y, a = oracle.gemm_f64(x, w, lib=lib)
+        assert np.array_equal(y, ref.astype(np.float64))
+        assert np.array_equal(a, (np.abs(xi) @ np.abs(wi).T).astype(np.float64))
+
+
+def pin_numpy_fp64(lib=None):
+    for seed, (m, n, k) in enumerate([(8, 16, 512), (3, 40, 4096), (2, 6, 14336)]):
+        x = synth.normal_bf16(500 + seed, (m, k))
+        w = synth.normal_bf16(600 + seed, (n, k), 0.02)
+        xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+        wf = synth.bf16_bits_to_f32(w).astype(np.float64)
+        y, a = oracle.gemm_f64(x, w, lib=lib)
+        ref = xf @ wf.T
+        aref = np.abs(xf) @ np.abs(wf).T
+        bound = 2 * k * EPS64 * aref
+        assert np.all(np.abs(y - ref) <= bound)
+        assert np.all(np.abs(a - aref) <= bound)
+
+
+def pin_identity_onehot(lib=None):
+    k = 96
+    x = synth.normal_bf16(700, (5, k))
+    eye = synth.f32_to_bf16_bits(np.eye(k, dtype=np.float32))
+    y, _ = oracle.gemm_f64(x, eye, lib=lib)
+    assert np.array_equal(y, synth.bf16_bits_to_f32(x).astype(np.float64))
+    w = synth.normal_bf16(701, (11, k), 0.02)
+    onehot = synth.f32_to_bf16_bits(np.eye(k, dtype=np.float32)[[0, 17, 95]])
+    y, _ = oracle.gemm_f64(onehot, w, lib=lib)
+    wf = synth.bf16_bits_to_f32(w).astype(np.float64)
+    assert np.array_equal(y, wf[:, [0, 17, 95]].T)
+
+
+def pin_row_selection(lib=None):
+    x = synth.normal_bf16(800, (37, 64))
+    w = synth.normal_bf16(801, (9, 64), 0.02)
+    rows = np.array([36, 0, 5, 5, 17])
+    y, a = oracle.gemm_f64(x, w, rows=rows, lib=lib)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)[rows]
+    wf = synth.bf16_bits_to_f32(w).astype(np.float64)
+    assert np.all(np.abs(y - xf @ wf.T) <= 2 * 64 * EPS64 * (np.abs(xf) @ np.abs(wf).T))
+
+
+def pin_grouped(lib=None):
+    # tiny exact case with empty experts and uneven groups
+    e, n, k = 4, 3, 16
+    offsets = np.array([0, 2, 2, 5, 6], np.int32)
+    x = wide_bf16(900, (6, k), -10, 10)
+    w = wide_bf16(901, (e, n, k), -10, 10)
+    y, a = oracle.grouped_f64(x, w, offsets, lib=lib)
+    owner = [0, 0, 2, 2, 2, 3]
+    for r in range(6):
+        ye, ae = exact.gemm_exact(x[r:r + 1], w[owner[r]])
+        for j in range(n):
+            bound = Fraction(k - 1) * Fraction(EPS64) * ae[0][j]
+            assert abs(Fraction(y[r, j]) - ye[0][j]) <= bound, (r, j)
+            assert abs(Fraction(a[r, j]) - ae[0][j]) <= bound, (r, j)
+    # larger: against numpy per expert, from a real routing table
+    tok, off, _ = synth.moe_routing(902, 16, experts=8, topk=2)
+    k = 128
+    xt = synth.normal_bf16(903, (16, k))
+    x = xt[tok]
+    w = synth.normal_bf16(904, (8, 5, k), 0.02)
+    y, _ = oracle.grouped_f64(x, w, off, lib=lib)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    wf = synth.bf16_bits_to_f32(w).astype(np.float64)
+    for ex in range(8):
+        lo, hi = off[ex], off[ex + 1]
+        ref = xf[lo:hi] @ wf[ex].T
+        bound = 2 * k * EPS64 * (np.abs(xf[lo:hi]) @ np.abs(wf[ex]).T)
+        assert np.all(np.abs(y[lo:hi] - ref) <= bound), ex
+
+
+def pin_fold(lib=None):
+    for parts, want in load_fold_golden():
+        got = oracle.fold_f32(parts.reshape(-1, 1), lib=lib)
+        assert int(got.view(np.uint32)[0]) == want, (parts, hex(int(got.view(np.uint32)[0])), hex(want))
+
+
+ALL_PINS = [
+    pin_exact_rationals,
+    pin_golden_gemm,
+    pin_integer_closed_forms,
+    pin_integer_random,
+    pin_numpy_fp64,
+    pin_identity_onehot,
+    pin_row_selection,
+    pin_grouped,
+    pin_fold,
+]

@@ -1,0 +1,53 @@
+"""Planted mistakes in the oracle, on the CPU: each broken copy of oracle.c
+must fail at least one pin.  This shows the pins would catch a dropped term,
+a wrong sign or index, a transposed operand, a narrower accumulator or a
+reordered combine in the oracle itself.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, text to replace, replacement, which occurrence: 0 = first)
+MUTANTS = [
+    ("drop_last_term", "for (long k = 0; k < K; ++k) {", "for (long k = 0; k < K - 1; ++k) {", 0),
+    ("wrong_sign", "        s += prod;", "        s -= prod;", 0),
+    ("no_abs", "abs_s += fabs(prod);", "abs_s += prod;", 0),
+    ("fp32_accumulator", "double s = 0.0, abs_s = 0.0;", "float s = 0.0f; double abs_s = 0.0;", 0),
+    ("ignore_row_list", "long i = rows ? rows[r] : r;", "long i = r < M ? r : 0;", 0),
+    ("weight_row_from_x_index", "const uint16_t *wn = w + n * K;", "const uint16_t *wn = w + (n % (M > 0 ? M : 1)) * K;", 0),
+    ("i64_squares_x", "(int64_t)bf16_to_f64(w[n * K + k])", "(int64_t)bf16_to_f64(x[i * K + k])", 0),
+    ("grouped_inclusive_end", "(offsets[e] <= i && i < offsets[e + 1])", "(offsets[e] <= i && i <= offsets[e + 1])", 0),
+    ("grouped_expert_stride", "w + (e * N + n) * K", "w + n * K", 0),
+    ("fold_reversed",
+     "volatile float t = parts[j];\n        for (long s = 1; s < S; ++s)\n            t = t + parts[s * count + j];",
+     "volatile float t = parts[(S - 1) * count + j];\n        for (long s = S - 2; s >= 0; --s)\n            t = t + parts[s * count + j];", 0),
+    ("fold_in_fp64", "volatile float t = parts[j];", "volatile double t = parts[j];", 0),
+]
+
+
+def _mutate(text, old, new, occurrence):
+    pos = -1
+    for _ in range(occurrence + 1):
+        pos = text.index(old, pos + 1)
+    return text[:pos] + new + text[pos + len(old):]
+
+
+@pytest.mark.parametrize("name,old,new,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new, occ):
+    text = open(SRC).read()
+    assert old in text, "mutation site vanished: " + name
+    src = tmp_path / ("oracle_%s.c" % name)
+    src.write_text(_mutate(text, old, new, occ))
+    lib = oracle.open_library(oracle.compile_source(str(src), str(tmp_path / ("lib%s.so" % name))))
+    failures = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib=lib)
+        except (AssertionError, ValueError) as exc:  # noqa: PERF203
+            failures.append((pin.__name__, repr(exc)[:80]))
+    assert failures, "no pin caught the planted mistake " + name
