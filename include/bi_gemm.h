@@ -1,0 +1,171 @@
+/*
+ * bi_gemm.h -- batch-invariant bf16 linear-layer GEMM for AMD MI355X (gfx950).
+ *
+ *   y[M,N] (fp32) = x[M,K] (bf16) . W[N,K]^T (bf16), fp32 accumulation.
+ *
+ * Batch invariance.  Row i of y is a function of row i of x, W and the
+ * layer's pin only: the same bits whatever M is, wherever the row sits in x and
+ * whatever the other rows hold.  This is the kernel property the pages define
+ * (CoRun, §III-B Definition 1: x_i = x'_j implies F_n(X)_i = F_m(X')_j for
+ * all n, m, i, j; Detent, §3 eq. 2 and its "kernel batch invariance").
+ *
+ * How.  Floating-point sums depend on their order (LLM-42 reading notes,
+ * §2.2 Fig. 3; CoRun, §III-A Fig. 3), and GEMMs change that order when they
+ * choose split-K or tiles from the batch.  This library fixes one reduction
+ * tree per layer shape (N, K) -- the "pin" of Detent, §3: a value of the
+ * selection replaced by a constant before deployment -- and never derives it
+ * from M.  The tree is:
+ *   - one MFMA instruction, v_mfma_f32_16x16x32_bf16, for every M;
+ *   - a fixed map from k to the instruction's (lane group, element) slots:
+ *     within MFMA step t of a split, lane group g (= lane / 16) holds
+ *     k = 32 t + 8 g .. 32 t + 8 g + 7;
+ *   - S contiguous equal K splits, each a chain of MFMA steps in ascending
+ *     k, starting from +0;
+ *   - the split partials combined in fp32 round-to-nearest-even in fixed
+ *     order, ((p0 + p1) + p2) + ... (CoRun, §III-A Fig. 3b; Detent, Fig. 2b).
+ * M only chooses among kernels and tilings that realise this same tree
+ * (Detent, §2 Observation 2: agreement of such kernels is established by
+ * measurement, here the library's invariance tests).
+ *
+ * Errors.  Every call validates its arguments on the host before any HIP
+ * call; on failure it returns an error code, launches nothing and never falls
+ * back to another tree (Detent, §5: a failed check stops the engine with an
+ * error and runs no other kernel).
+ *
+ * Threading.  A handle may be used from several host threads for `run` calls
+ * on the same or different streams: `run` keeps no per-call state in the
+ * handle.  `destroy` must not race with any other call on that handle.
+ */
+#ifndef BI_GEMM_H
+#define BI_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BI_OK = 0,
+    BI_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad handle kind      */
+    BI_ERR_MISALIGNED = 2,       /* a device pointer is not 16-byte aligned      */
+    BI_ERR_NO_PIN = 3,           /* strict mode and no pin for (arch, N, K)      */
+    BI_ERR_UNSUPPORTED_DEVICE = 4, /* the current device is not gfx950           */
+    BI_ERR_OUT_OF_MEMORY = 5,    /* a host allocation failed                     */
+    BI_ERR_HIP = 6,              /* a HIP runtime call failed                    */
+    BI_ERR_BAD_PIN_TABLE = 7     /* the pin table file could not be parsed       */
+} bi_status_t;
+
+typedef struct bi_gemm *bi_gemm_t;
+
+/* Tree and tiling a handle runs with (introspection for tests and benches). */
+typedef struct bi_pin_info {
+    int32_t n, k;                 /* layer shape                                 */
+    int32_t experts;              /* 0 for a dense handle, E for a grouped one   */
+    int32_t mfma_m, mfma_n, mfma_k; /* 16, 16, 32                                */
+    int32_t k_map;                /* 0: lane group g holds k = 32t+8g .. +7      */
+    int32_t splits;               /* S: contiguous equal K splits                */
+    int32_t split_len;            /* K / S                                       */
+    int32_t fold;                 /* 0: in-order left fold in fp32 RNE           */
+    int32_t stream_max_m;         /* tiling: rows at or below which the
+                                     weight-streaming kernel runs                */
+    int32_t from_table;           /* 1: pin read from the pin table; 0: default  */
+    int32_t table_version;        /* version line of the pin table (0: none)     */
+} bi_pin_info;
+
+/*
+ * Load the pin table (text file; see the package's pins/ directory) used by
+ * later create calls.  Passing NULL clears the table.  The environment
+ * variable BI_GEMM_PINS names a table that is loaded on first use when this
+ * is never called.  Not thread-safe with concurrent create calls.
+ * Returns BI_OK, BI_ERR_INVALID_ARGUMENT (unreadable file) or
+ * BI_ERR_BAD_PIN_TABLE (with the offending line in bi_last_error()).
+ */
+bi_status_t bi_gemm_load_pins(const char *path);
+
+/*
+ * Strict mode: when nonzero, create fails with BI_ERR_NO_PIN for a shape the
+ * pin table does not list, instead of using the built-in default tree
+ * (S = 1).  The environment variable BI_GEMM_STRICT=1 sets it on first use.
+ */
+void bi_gemm_set_strict(int strict);
+
+/*
+ * Create a dense handle for a layer with weight W.
+ *   N, K: layer shape; N % 16 == 0, K % 64 == 0, both > 0, N*K < 2^31.
+ *   W:    device pointer, bf16 [N,K] row-major (nn.Linear layout, K
+ *         contiguous), 16-byte aligned.  BORROWED: the caller keeps it alive
+ *         and unchanged until bi_gemm_destroy.
+ *   out:  receives the handle.
+ * The tree is looked up by (device arch, N, K) and frozen here.  No kernel
+ * runs and no device memory is allocated.  The current HIP device must be a
+ * gfx950; the handle is bound to it.
+ */
+bi_status_t bi_gemm_create(int N, int K, const void *W, bi_gemm_t *out);
+
+/*
+ * Create a dense handle with an explicit pin instead of the table's.  For the
+ * offline tuner, which measures each legal candidate by swapping the pin's
+ * constants (Detent, §6 "Search": a repin regenerates the selector without
+ * solving again), and for tests that force a kernel path.  Only pin->splits
+ * and pin->stream_max_m are read; the pin must be legal for (N, K)
+ * (splits == 1, K % (64 * splits) == 0, 0 <= stream_max_m <= 4096), else
+ * BI_ERR_INVALID_ARGUMENT.  Otherwise as bi_gemm_create.
+ */
+bi_status_t bi_gemm_create_pinned(int N, int K, const void *W, const bi_pin_info *pin,
+                                  bi_gemm_t *out);
+
+/*
+ * y = x W^T for M rows.
+ *   x: device bf16 [M,K] row-major, 16-byte aligned; rows are K apart.
+ *   y: device fp32 [M,N] row-major, 16-byte aligned.
+ *   M: 0 <= M <= 2^31/max(N,K); M == 0 returns BI_OK and launches nothing.
+ *   stream: HIP stream (hipStream_t) the kernels are enqueued on; NULL is the
+ *           default stream.
+ * Asynchronous: no allocation, no synchronisation, no compilation, so the
+ * call may be captured into a HIP graph.  x and y are borrowed for the
+ * duration of the enqueued work; y must not overlap x or W.
+ */
+bi_status_t bi_gemm_run(bi_gemm_t h, const void *x, int M, float *y, void *stream);
+
+/*
+ * Create a grouped (MoE expert) handle: E experts, each with weight
+ * W[e] = W + e*N*K (bf16 [E,N,K], row-major, 16-byte aligned, BORROWED as
+ * above).  Every expert uses the tree of the dense layer (N, K), so a row
+ * computed here has the bits it would have in a dense handle over W[e].
+ */
+bi_status_t bi_grouped_gemm_create(int E, int N, int K, const void *W, bi_gemm_t *out);
+
+/*
+ * Grouped run.  Rows of x are grouped by expert: expert e owns rows
+ * expert_offsets[e] .. expert_offsets[e+1]-1, and y[r] = x[r] W[e]^T for them.
+ *   x: device bf16 [R,K]; y: device fp32 [R,N]; both 16-byte aligned.
+ *   expert_offsets: DEVICE int32 [E+1], read by the kernels (never by the
+ *       host): offsets[0] == 0, offsets[E] == R, nondecreasing.  Violating
+ *       this is undefined: rows outside any expert are left unwritten, and
+ *       the kernels never read x or write y outside rows 0..R-1.
+ *   R: total rows, 0 <= R; R == 0 returns BI_OK and launches nothing.
+ * Per-expert row counts stay on the device; the kernels choose per expert
+ * between kernels that share one tree.  Asynchronous and allocation-free
+ * like bi_gemm_run.
+ */
+bi_status_t bi_grouped_gemm_run(bi_gemm_t h, const void *x, const int32_t *expert_offsets,
+                                int R, float *y, void *stream);
+
+/* Release a handle (dense or grouped).  NULL is ignored. */
+void bi_gemm_destroy(bi_gemm_t h);
+
+/* The tree and tiling of a handle. */
+bi_status_t bi_gemm_get_pin(bi_gemm_t h, bi_pin_info *out);
+
+/* A static English string for a status code. */
+const char *bi_status_string(bi_status_t s);
+
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char *bi_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_GEMM_H */

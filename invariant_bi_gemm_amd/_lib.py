@@ -1,0 +1,245 @@
+"""ctypes binding of the C ABI declared in include/bi_gemm.h.
+
+Argument marshalling only: every step of the GEMM runs in the HIP library
+``libbigemm.so``.  Tensors are PyTorch device tensors (PyTorch provides device
+memory and streams); their pointers and sizes go straight to the C calls.
+There is no fallback: if the library is missing or the call fails, this
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbigemm.so")
+PIN_TABLE = os.path.join(HERE, "pins", "gfx950.txt")
+
+STATUS = {
+    0: "BI_OK",
+    1: "BI_ERR_INVALID_ARGUMENT",
+    2: "BI_ERR_MISALIGNED",
+    3: "BI_ERR_NO_PIN",
+    4: "BI_ERR_UNSUPPORTED_DEVICE",
+    5: "BI_ERR_OUT_OF_MEMORY",
+    6: "BI_ERR_HIP",
+    7: "BI_ERR_BAD_PIN_TABLE",
+}
+STATUS_CODE = {v: k for k, v in STATUS.items()}
+
+
+class BiPinInfo(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "n", "k", "experts", "mfma_m", "mfma_n", "mfma_k", "k_map", "splits", "split_len",
+        "fold", "stream_max_m", "from_table", "table_version")]
+
+    def as_dict(self):
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+
+class BiGemmError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__("%s: %s" % (self.name, detail))
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def _declare(lib):
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    S = ctypes.c_int  # bi_status_t
+    sig = {
+        "bi_gemm_load_pins": ([ctypes.c_char_p], S),
+        "bi_gemm_set_strict": ([I], None),
+        "bi_gemm_create": ([I, I, P, ctypes.POINTER(P)], S),
+        "bi_gemm_create_pinned": ([I, I, P, ctypes.POINTER(BiPinInfo), ctypes.POINTER(P)], S),
+        "bi_gemm_run": ([P, P, I, P, P], S),
+        "bi_grouped_gemm_create": ([I, I, I, P, ctypes.POINTER(P)], S),
+        "bi_grouped_gemm_run": ([P, P, P, I, P, P], S),
+        "bi_gemm_destroy": ([P], None),
+        "bi_gemm_get_pin": ([P, ctypes.POINTER(BiPinInfo)], S),
+        "bi_status_string": ([S], ctypes.c_char_p),
+        "bi_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+def load(path: str = LIB_PATH, pins: str | None = PIN_TABLE):
+    """Load the HIP library (once) and its pin table.  Raises if missing."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    "the HIP library %s is not built; run __graft_entry__.build() "
+                    "or python invariant_bi_gemm_amd/build.py" % path)
+            lib = _declare(ctypes.CDLL(path))
+            if pins and not os.environ.get("BI_GEMM_PINS"):
+                st = lib.bi_gemm_load_pins(pins.encode())
+                if st != 0:
+                    raise BiGemmError(st, lib.bi_last_error().decode())
+            _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return load().bi_last_error().decode()
+
+
+def check(status: int):
+    if status != 0:
+        raise BiGemmError(status, last_error())
+
+
+def status_string(status: int) -> str:
+    return load().bi_status_string(status).decode()
+
+
+def _stream_ptr(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _need(t, dtype, ndim, what):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % what)
+    if t.dtype != dtype or t.dim() != ndim or not t.is_cuda:
+        raise TypeError("%s must be a %d-d %s CUDA tensor, got %s %s on %s" % (what, ndim, dtype, t.dtype, tuple(t.shape), t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % what)
+
+
+class Gemm:
+    """A dense layer handle: ``y = x @ W.T`` with batch-invariant rows.
+
+    ``W`` is a contiguous bf16 [N, K] CUDA tensor; the handle keeps a reference
+    to it (the C library borrows the memory).  ``pin`` (optional) is a dict
+    with ``splits`` and ``stream_max_m`` to override the pin table.
+    """
+
+    def __init__(self, W, pin: dict | None = None):
+        import torch
+
+        lib = load()
+        _need(W, torch.bfloat16, 2, "W")
+        self.n, self.k = (int(v) for v in W.shape)
+        self._W = W
+        self._lib = lib
+        h = ctypes.c_void_p()
+        with torch.cuda.device(W.device):
+            if pin is None:
+                st = lib.bi_gemm_create(self.n, self.k, ctypes.c_void_p(W.data_ptr()), ctypes.byref(h))
+            else:
+                p = BiPinInfo()
+                p.splits = int(pin.get("splits", 1))
+                p.stream_max_m = int(pin.get("stream_max_m", 16))
+                st = lib.bi_gemm_create_pinned(self.n, self.k, ctypes.c_void_p(W.data_ptr()),
+                                               ctypes.byref(p), ctypes.byref(h))
+        check(st)
+        self._h = h
+
+    @property
+    def pin(self) -> dict:
+        info = BiPinInfo()
+        check(self._lib.bi_gemm_get_pin(self._h, ctypes.byref(info)))
+        return info.as_dict()
+
+    def __call__(self, x, out=None, stream=None):
+        import torch
+
+        _need(x, torch.bfloat16, 2, "x")
+        if x.shape[1] != self.k:
+            raise ValueError("x has K=%d, the layer has K=%d" % (x.shape[1], self.k))
+        m = int(x.shape[0])
+        if out is None:
+            out = torch.empty((m, self.n), dtype=torch.float32, device=x.device)
+        else:
+            _need(out, torch.float32, 2, "out")
+            if tuple(out.shape) != (m, self.n):
+                raise ValueError("out must be [%d, %d]" % (m, self.n))
+        self.run_ptr(x.data_ptr(), m, out.data_ptr(), stream)
+        return out
+
+    def run_ptr(self, x_ptr: int, m: int, y_ptr: int, stream=None):
+        """Raw call: device pointers and the row count, as the C ABI takes them."""
+        check(self._lib.bi_gemm_run(self._h, ctypes.c_void_p(x_ptr), int(m), ctypes.c_void_p(y_ptr),
+                                    _stream_ptr(stream)))
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.bi_gemm_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 (interpreter shutdown)
+            pass
+
+
+class GroupedGemm:
+    """MoE experts: ``W`` is bf16 [E, N, K]; rows of x are grouped by expert."""
+
+    def __init__(self, W):
+        import torch
+
+        lib = load()
+        _need(W, torch.bfloat16, 3, "W")
+        self.e, self.n, self.k = (int(v) for v in W.shape)
+        self._W = W
+        self._lib = lib
+        h = ctypes.c_void_p()
+        with torch.cuda.device(W.device):
+            st = lib.bi_grouped_gemm_create(self.e, self.n, self.k, ctypes.c_void_p(W.data_ptr()), ctypes.byref(h))
+        check(st)
+        self._h = h
+
+    @property
+    def pin(self) -> dict:
+        info = BiPinInfo()
+        check(self._lib.bi_gemm_get_pin(self._h, ctypes.byref(info)))
+        return info.as_dict()
+
+    def __call__(self, x, expert_offsets, out=None, stream=None):
+        import torch
+
+        _need(x, torch.bfloat16, 2, "x")
+        _need(expert_offsets, torch.int32, 1, "expert_offsets")
+        if x.shape[1] != self.k or expert_offsets.shape[0] != self.e + 1:
+            raise ValueError("shape mismatch")
+        r = int(x.shape[0])
+        if out is None:
+            out = torch.empty((r, self.n), dtype=torch.float32, device=x.device)
+        else:
+            _need(out, torch.float32, 2, "out")
+            if tuple(out.shape) != (r, self.n):
+                raise ValueError("out must be [%d, %d]" % (r, self.n))
+        check(self._lib.bi_grouped_gemm_run(self._h, ctypes.c_void_p(x.data_ptr()),
+                                            ctypes.c_void_p(expert_offsets.data_ptr()), r,
+                                            ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)))
+        return out
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.bi_gemm_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001
+            pass

@@ -1,0 +1,480 @@
+// Host side of the batch-invariant GEMM library: handles, validation, the pin
+// table and dispatch.  Every argument check runs on the host before any HIP
+// call, and a failed check returns an error without launching anything
+// (Detent, §5: a failed precondition stops the engine with an error and runs
+// no other kernel).  The tree a handle runs with is frozen at create from
+// (device arch, N, K) only; `run` reads M solely to pick among kernels that
+// realise that tree (Detent, §3: pins depend on the deployment, never on the
+// batch).
+
+#include <hip/hip_runtime.h>
+
+#include <cerrno>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "bigemm_internal.h"
+
+namespace {
+
+constexpr uint32_t kMagic = 0xB16E3A11u;
+constexpr int kMaxDevices = 64;
+
+thread_local std::string g_last_error;
+
+bi_status_t fail(bi_status_t st, const std::string& msg)
+{
+    g_last_error = msg;
+    return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- pin table -------------------------------------------------------------
+
+struct PinRow {
+    std::string arch;
+    int n, k, splits, stream_max_m;
+};
+
+struct PinTable {
+    int version = 0;
+    std::vector<PinRow> rows;
+};
+
+std::mutex g_pin_mu;
+PinTable g_pins;
+bool g_pins_env_checked = false;
+int g_strict = -1;  // -1: read BI_GEMM_STRICT on first use
+
+// The default tiling when the table has no entry: the streaming kernel for
+// up to 16 rows.  The default tree is S = 1.
+constexpr int kDefaultStreamMaxM = 16;
+
+// A pin is legal for (N, K) when its splits divide K into equal parts that
+// are whole 64-wide stages, and the streaming threshold is sane.  Only the
+// S = 1 tree has kernels.
+bool pin_legal(int N, int K, int splits, int stream_max_m, std::string* why)
+{
+    (void)N;
+    if (splits != 1) {
+        *why = "only the single-split tree (S = 1) is built";
+        return false;
+    }
+    if (K % (splits * bigemm::kKGranule) != 0) {
+        *why = "K must split into equal parts that are multiples of 64";
+        return false;
+    }
+    if (stream_max_m < 0 || stream_max_m > 4096) {
+        *why = "stream_max_m must be within 0..4096";
+        return false;
+    }
+    return true;
+}
+
+bi_status_t parse_pins(const char* path, PinTable* out)
+{
+    FILE* f = std::fopen(path, "r");
+    if (!f)
+        return fail(BI_ERR_INVALID_ARGUMENT, std::string("cannot open pin table ") + path + ": " +
+                                                 std::strerror(errno));
+    PinTable t;
+    char line[512];
+    int lineno = 0;
+    bi_status_t st = BI_OK;
+    while (std::fgets(line, sizeof line, f)) {
+        ++lineno;
+        char* hash = std::strchr(line, '#');
+        if (hash)
+            *hash = 0;
+        char a[64];
+        int n, k, s, sm, v;
+        char extra[8];
+        if (std::sscanf(line, " %63s", a) != 1)
+            continue;  // blank
+        if (std::strcmp(a, "version") == 0) {
+            if (std::sscanf(line, " version %d %7s", &v, extra) != 1 || v <= 0) {
+                st = fail(BI_ERR_BAD_PIN_TABLE, "pin table line " + std::to_string(lineno) + ": bad version line");
+                break;
+            }
+            t.version = v;
+            continue;
+        }
+        if (std::sscanf(line, " %63s %d %d %d %d %7s", a, &n, &k, &s, &sm, extra) != 5) {
+            st = fail(BI_ERR_BAD_PIN_TABLE, "pin table line " + std::to_string(lineno) +
+                                                ": expected 'arch N K splits stream_max_m'");
+            break;
+        }
+        std::string why;
+        if (n <= 0 || k <= 0 || n % bigemm::kTile || k % bigemm::kKGranule ||
+            !pin_legal(n, k, s, sm, &why)) {
+            st = fail(BI_ERR_BAD_PIN_TABLE, "pin table line " + std::to_string(lineno) +
+                                                ": illegal pin " + (why.empty() ? "shape" : why));
+            break;
+        }
+        for (const PinRow& r : t.rows)
+            if (r.arch == a && r.n == n && r.k == k) {
+                st = fail(BI_ERR_BAD_PIN_TABLE, "pin table line " + std::to_string(lineno) + ": duplicate shape");
+                break;
+            }
+        if (st != BI_OK)
+            break;
+        t.rows.push_back(PinRow{a, n, k, s, sm});
+    }
+    std::fclose(f);
+    if (st == BI_OK && t.version == 0)
+        st = fail(BI_ERR_BAD_PIN_TABLE, "pin table has no version line");
+    if (st == BI_OK)
+        *out = std::move(t);
+    return st;
+}
+
+void check_env_locked()
+{
+    if (!g_pins_env_checked) {
+        g_pins_env_checked = true;
+        const char* p = std::getenv("BI_GEMM_PINS");
+        if (p && *p) {
+            PinTable t;
+            if (parse_pins(p, &t) == BI_OK)
+                g_pins = std::move(t);
+        }
+    }
+    if (g_strict < 0) {
+        const char* s = std::getenv("BI_GEMM_STRICT");
+        g_strict = (s && std::strcmp(s, "1") == 0) ? 1 : 0;
+    }
+}
+
+// ---- devices ---------------------------------------------------------------
+
+struct DeviceInfo {
+    bool known = false;
+    bool gfx950 = false;
+    int num_cus = 0;
+    std::string arch;
+};
+std::mutex g_dev_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+bi_status_t current_device(int* dev, DeviceInfo* info)
+{
+    hipError_t e = hipGetDevice(dev);
+    if (e != hipSuccess)
+        return fail(BI_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (*dev < 0 || *dev >= kMaxDevices)
+        return fail(BI_ERR_UNSUPPORTED_DEVICE, "device index out of range");
+    std::lock_guard<std::mutex> g(g_dev_mu);
+    DeviceInfo& d = g_dev[*dev];
+    if (!d.known) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, *dev);
+        if (e != hipSuccess)
+            return fail(BI_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+        d.arch = prop.gcnArchName;
+        d.gfx950 = d.arch.compare(0, 6, "gfx950") == 0;
+        d.num_cus = prop.multiProcessorCount;
+        d.known = true;
+    }
+    *info = d;
+    return BI_OK;
+}
+
+}  // namespace
+
+struct bi_gemm {
+    uint32_t magic;
+    int device;
+    const void* W;
+    bigemm::Plan plan;
+    bi_pin_info pin;
+};
+
+namespace {
+
+// Live handles, so that a stale or foreign pointer is rejected instead of
+// being read.
+std::mutex g_live_mu;
+std::unordered_set<const bi_gemm*> g_live;
+
+bi_gemm* handle_of(bi_gemm_t h)
+{
+    if (!h)
+        return nullptr;
+    {
+        std::lock_guard<std::mutex> g(g_live_mu);
+        if (g_live.find(h) == g_live.end())
+            return nullptr;
+    }
+    return h->magic == kMagic ? h : nullptr;
+}
+
+bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info* forced,
+                          bi_gemm_t* out)
+{
+    if (!out)
+        return fail(BI_ERR_INVALID_ARGUMENT, "out is NULL");
+    *out = nullptr;
+    if (!W)
+        return fail(BI_ERR_INVALID_ARGUMENT, "W is NULL");
+    if (N <= 0 || K <= 0)
+        return fail(BI_ERR_INVALID_ARGUMENT, "N and K must be positive");
+    if (N % bigemm::kTile != 0)
+        return fail(BI_ERR_INVALID_ARGUMENT, "N must be a multiple of 16");
+    if (K % bigemm::kKGranule != 0)
+        return fail(BI_ERR_INVALID_ARGUMENT, "K must be a multiple of 64");
+    if ((long long)N * K >= (1LL << 31))
+        return fail(BI_ERR_INVALID_ARGUMENT, "N*K must be below 2^31");
+    if (E < 0 || E > bigemm::kMaxExperts)
+        return fail(BI_ERR_INVALID_ARGUMENT, "E must be within 1..1024");
+    if (!aligned16(W))
+        return fail(BI_ERR_MISALIGNED, "W must be 16-byte aligned");
+
+    // the pin: forced (tuner), table, or default
+    int splits = 1, stream_max_m = kDefaultStreamMaxM, from_table = 0, version = 0;
+    if (forced) {
+        std::string why;
+        if (!pin_legal(N, K, forced->splits, forced->stream_max_m, &why))
+            return fail(BI_ERR_INVALID_ARGUMENT, "illegal pin: " + why);
+        splits = forced->splits;
+        stream_max_m = forced->stream_max_m;
+    }
+
+    int dev;
+    DeviceInfo info;
+    bi_status_t st = current_device(&dev, &info);
+    if (st != BI_OK)
+        return st;
+    if (!info.gfx950)
+        return fail(BI_ERR_UNSUPPORTED_DEVICE, "device " + std::to_string(dev) + " is " + info.arch +
+                                                   ", this library is built for gfx950 only");
+
+    if (!forced) {
+        std::lock_guard<std::mutex> g(g_pin_mu);
+        check_env_locked();
+        const PinRow* row = nullptr;
+        for (const PinRow& r : g_pins.rows)
+            if (r.n == N && r.k == K && info.arch.compare(0, r.arch.size(), r.arch) == 0)
+                row = &r;
+        if (row) {
+            splits = row->splits;
+            stream_max_m = row->stream_max_m;
+            from_table = 1;
+            version = g_pins.version;
+        } else if (g_strict) {
+            return fail(BI_ERR_NO_PIN, "strict mode: no pin for N=" + std::to_string(N) +
+                                           " K=" + std::to_string(K) + " on " + info.arch);
+        }
+    }
+
+    bi_gemm* h = new (std::nothrow) bi_gemm;
+    if (!h)
+        return fail(BI_ERR_OUT_OF_MEMORY, "out of host memory");
+    h->magic = kMagic;
+    h->device = dev;
+    h->W = W;
+    h->plan.n = N;
+    h->plan.k = K;
+    h->plan.experts = E;
+    h->plan.splits = splits;
+    h->plan.stream_max_m = stream_max_m;
+    h->plan.num_cus = info.num_cus;
+    bi_pin_info& p = h->pin;
+    std::memset(&p, 0, sizeof p);
+    p.n = N;
+    p.k = K;
+    p.experts = E;
+    p.mfma_m = bigemm::kTile;
+    p.mfma_n = bigemm::kTile;
+    p.mfma_k = bigemm::kStepK;
+    p.k_map = 0;
+    p.splits = splits;
+    p.split_len = K / splits;
+    p.fold = 0;
+    p.stream_max_m = stream_max_m;
+    p.from_table = from_table;
+    p.table_version = version;
+    try {
+        std::lock_guard<std::mutex> g(g_live_mu);
+        g_live.insert(h);
+    } catch (...) {
+        delete h;
+        return fail(BI_ERR_OUT_OF_MEMORY, "out of host memory");
+    }
+    *out = h;
+    g_last_error.clear();
+    return BI_OK;
+}
+
+bi_status_t check_run_device(const bi_gemm* h)
+{
+    int dev;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(BI_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (dev != h->device)
+        return fail(BI_ERR_INVALID_ARGUMENT, "the current device is not the handle's device");
+    return BI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bi_status_t bi_gemm_load_pins(const char* path)
+{
+    std::lock_guard<std::mutex> g(g_pin_mu);
+    g_pins_env_checked = true;
+    if (!path) {
+        g_pins = PinTable();
+        return BI_OK;
+    }
+    PinTable t;
+    bi_status_t st = parse_pins(path, &t);
+    if (st == BI_OK)
+        g_pins = std::move(t);
+    return st;
+}
+
+void bi_gemm_set_strict(int strict)
+{
+    std::lock_guard<std::mutex> g(g_pin_mu);
+    g_strict = strict ? 1 : 0;
+}
+
+bi_status_t bi_gemm_create(int N, int K, const void* W, bi_gemm_t* out)
+{
+    return create_common(0, N, K, W, nullptr, out);
+}
+
+bi_status_t bi_gemm_create_pinned(int N, int K, const void* W, const bi_pin_info* pin, bi_gemm_t* out)
+{
+    if (!pin) {
+        if (out)
+            *out = nullptr;
+        return fail(BI_ERR_INVALID_ARGUMENT, "pin is NULL");
+    }
+    return create_common(0, N, K, W, pin, out);
+}
+
+bi_status_t bi_grouped_gemm_create(int E, int N, int K, const void* W, bi_gemm_t* out)
+{
+    if (E <= 0) {
+        if (out)
+            *out = nullptr;
+        return fail(BI_ERR_INVALID_ARGUMENT, "E must be within 1..1024");
+    }
+    if ((long long)E * N * K >= (1LL << 40)) {
+        if (out)
+            *out = nullptr;
+        return fail(BI_ERR_INVALID_ARGUMENT, "E*N*K too large");
+    }
+    return create_common(E, N, K, W, nullptr, out);
+}
+
+bi_status_t bi_gemm_run(bi_gemm_t hh, const void* x, int M, float* y, void* stream)
+{
+    bi_gemm* h = handle_of(hh);
+    if (!h)
+        return fail(BI_ERR_INVALID_ARGUMENT, "invalid handle");
+    if (h->plan.experts != 0)
+        return fail(BI_ERR_INVALID_ARGUMENT, "grouped handle passed to bi_gemm_run");
+    if (M < 0)
+        return fail(BI_ERR_INVALID_ARGUMENT, "M must be >= 0");
+    if (M == 0)
+        return BI_OK;
+    if (!x || !y)
+        return fail(BI_ERR_INVALID_ARGUMENT, "x or y is NULL");
+    if (!aligned16(x) || !aligned16(y))
+        return fail(BI_ERR_MISALIGNED, "x and y must be 16-byte aligned");
+    const long long wide = h->plan.n > h->plan.k ? h->plan.n : h->plan.k;
+    if ((long long)M * wide >= (1LL << 31))
+        return fail(BI_ERR_INVALID_ARGUMENT, "M*max(N,K) must be below 2^31");
+    bi_status_t st = check_run_device(h);
+    if (st != BI_OK)
+        return st;
+    hipError_t e = bigemm::launch_dense(h->plan, h->W, x, M, y, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(BI_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return BI_OK;
+}
+
+bi_status_t bi_grouped_gemm_run(bi_gemm_t hh, const void* x, const int32_t* expert_offsets, int R,
+                                float* y, void* stream)
+{
+    bi_gemm* h = handle_of(hh);
+    if (!h)
+        return fail(BI_ERR_INVALID_ARGUMENT, "invalid handle");
+    if (h->plan.experts == 0)
+        return fail(BI_ERR_INVALID_ARGUMENT, "dense handle passed to bi_grouped_gemm_run");
+    if (R < 0)
+        return fail(BI_ERR_INVALID_ARGUMENT, "R must be >= 0");
+    if (R == 0)
+        return BI_OK;
+    if (!x || !y || !expert_offsets)
+        return fail(BI_ERR_INVALID_ARGUMENT, "x, y or expert_offsets is NULL");
+    if (!aligned16(x) || !aligned16(y))
+        return fail(BI_ERR_MISALIGNED, "x and y must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(expert_offsets) & 3u) != 0)
+        return fail(BI_ERR_MISALIGNED, "expert_offsets must be 4-byte aligned");
+    const long long wide = h->plan.n > h->plan.k ? h->plan.n : h->plan.k;
+    if ((long long)R * wide >= (1LL << 31))
+        return fail(BI_ERR_INVALID_ARGUMENT, "R*max(N,K) must be below 2^31");
+    bi_status_t st = check_run_device(h);
+    if (st != BI_OK)
+        return st;
+    hipError_t e = bigemm::launch_grouped(h->plan, h->W, x, expert_offsets, R, y,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(BI_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return BI_OK;
+}
+
+void bi_gemm_destroy(bi_gemm_t hh)
+{
+    if (!hh)
+        return;
+    {
+        std::lock_guard<std::mutex> g(g_live_mu);
+        if (g_live.erase(hh) == 0)
+            return;
+    }
+    hh->magic = 0;
+    delete hh;
+}
+
+bi_status_t bi_gemm_get_pin(bi_gemm_t hh, bi_pin_info* out)
+{
+    bi_gemm* h = handle_of(hh);
+    if (!h)
+        return fail(BI_ERR_INVALID_ARGUMENT, "invalid handle");
+    if (!out)
+        return fail(BI_ERR_INVALID_ARGUMENT, "out is NULL");
+    *out = h->pin;
+    return BI_OK;
+}
+
+const char* bi_status_string(bi_status_t s)
+{
+    switch (s) {
+    case BI_OK: return "success";
+    case BI_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case BI_ERR_MISALIGNED: return "misaligned pointer";
+    case BI_ERR_NO_PIN: return "no pin for this shape (strict mode)";
+    case BI_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 only)";
+    case BI_ERR_OUT_OF_MEMORY: return "out of memory";
+    case BI_ERR_HIP: return "HIP runtime error";
+    case BI_ERR_BAD_PIN_TABLE: return "malformed pin table";
+    }
+    return "unknown status";
+}
+
+const char* bi_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

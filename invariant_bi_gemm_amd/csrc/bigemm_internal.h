@@ -1,0 +1,40 @@
+// Internal declarations shared by the host API and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bi_gemm.h"
+
+namespace bigemm {
+
+// Rows x contributes to one MFMA tile, and the MFMA k depth.  The tree is
+// built from v_mfma_f32_16x16x32_bf16 only.
+constexpr int kTile = 16;
+constexpr int kStepK = 32;
+
+// K granularity the kernels accept (one 64-wide LDS stage of the tiled path).
+constexpr int kKGranule = 64;
+
+// Most experts a grouped handle may have (the streaming kernel keeps a list
+// of them in LDS).
+constexpr int kMaxExperts = 1024;
+
+// What `run` needs from a handle.  The tree (splits) is frozen at create;
+// the tiling fields only choose among kernels that realise that tree.
+struct Plan {
+    int n, k;              // layer shape
+    int experts;           // 0 dense, E grouped
+    int splits;            // S (only 1 is built)
+    int stream_max_m;      // rows per expert/call at or below which the
+                           // weight-streaming kernel runs
+    int num_cus;           // compute units of the bound device
+};
+
+// Launchers (bigemm_kernels.hip).  They assume validated arguments.
+hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, float* y,
+                        hipStream_t stream);
+hipError_t launch_grouped(const Plan& p, const void* W, const void* x,
+                          const int32_t* offsets, int R, float* y, hipStream_t stream);
+
+}  // namespace bigemm

@@ -1,0 +1,110 @@
+"""Grouped (MoE expert) GEMM on the GPU: parity with the oracle on sampled
+rows, and bitwise invariance of each token's rows to the token count, to the
+other tokens' routing and against the dense kernel of the same expert (gpu).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DEV, assert_bits_equal, assert_parity, bits32, to_dev
+
+pytestmark = pytest.mark.gpu
+
+E, TOPK = 128, 8
+SHAPES = {"up": (1536, 2048), "down": (2048, 768)}
+
+
+@pytest.fixture(scope="module")
+def experts(gpu):
+    out = {}
+    for name, (n, k) in SHAPES.items():
+        w = synth.normal_bf16(150 + n, (E, n, k), 0.02)
+        out[name] = (w, to_dev(w))
+    return out
+
+
+def grouped_rows(x_tok, tok_of_row):
+    return x_tok[tok_of_row]
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("tokens", [1, 16, 256, 4096])
+def test_moe_parity_and_invariance(gpu, experts, name, tokens):
+    n, k = SHAPES[name]
+    w, wd = experts[name]
+    g = gpu.GroupedGemm(wd)
+    tok, off, ids = synth.moe_routing(160, tokens, E, TOPK)
+    x_tok = synth.normal_bf16(161 + k, (tokens, k))
+    x = grouped_rows(x_tok, tok)
+    y = g(to_dev(x), torch.as_tensor(off, device=DEV))
+    torch.cuda.synchronize()
+    ybits = bits32(y)
+    # parity on sampled rows
+    rows = synth.probe_rows(162 + tokens, len(tok), 48)
+    yr, a = oracle.grouped_f64(x, w, off, rows=rows)
+    assert_parity(y.cpu().numpy()[rows], yr, a, "moe %s T=%d" % (name, tokens))
+    # invariance: probe tokens computed alone (T = 1) and by the dense kernel
+    row_of = {}
+    for r, t in enumerate(tok):
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        row_of[(int(t), e)] = r
+    for t in synth.probe_rows(163 + tokens, tokens, 6):
+        t = int(t)
+        # the token alone: its 8 rows grouped by expert
+        es = sorted(int(e) for e in ids[t])
+        off1 = np.zeros(E + 1, np.int32)
+        for e in es:
+            off1[e + 1:] += 1
+        x1 = np.stack([x_tok[t]] * TOPK)
+        y1 = bits32(g(to_dev(x1), torch.as_tensor(off1, device=DEV)))
+        for j, e in enumerate(es):
+            assert_bits_equal(ybits[row_of[(t, e)]], y1[j], "token %d expert %d: T=%d vs alone" % (t, e, tokens))
+            dense = gpu.Gemm(wd[e])
+            yd = bits32(dense(to_dev(x_tok[t:t + 1])))[0]
+            assert_bits_equal(y1[j], yd, "token %d expert %d: grouped vs dense" % (t, e))
+
+
+def test_uneven_groups_cross_paths(gpu, experts):
+    """Row counts 0, 1, 15, 16, 17, 300 and one huge expert: both kernels in one call."""
+    n, k = SHAPES["down"]
+    w, wd = experts["down"]
+    g = gpu.GroupedGemm(wd)
+    counts = np.zeros(E, np.int64)
+    counts[[0, 3, 4, 5, 6, 7, 127]] = [1, 15, 16, 17, 300, 2000, 5]
+    off = np.zeros(E + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    r = int(off[-1])
+    x = synth.normal_bf16(170, (r, k))
+    y = g(to_dev(x), torch.as_tensor(off, device=DEV))
+    torch.cuda.synchronize()
+    yr, a = oracle.grouped_f64(x, w, off)
+    assert_parity(y.cpu().numpy(), yr, a, "uneven groups")
+    # every row equals the dense kernel of its expert at M = 1
+    yb = bits32(y)
+    for e in np.nonzero(counts)[0]:
+        dense = gpu.Gemm(wd[int(e)])
+        lo, hi = int(off[e]), int(off[e + 1])
+        for rr in (lo, hi - 1):
+            yd = bits32(dense(to_dev(x[rr:rr + 1])))[0]
+            assert_bits_equal(yb[rr], yd, "expert %d row %d" % (e, rr))
+
+
+def test_grouped_empty_and_single_expert(gpu, experts):
+    n, k = SHAPES["up"]
+    w, wd = experts["up"]
+    g = gpu.GroupedGemm(wd)
+    off = torch.zeros(E + 1, dtype=torch.int32, device=DEV)
+    y = g(torch.zeros((0, k), dtype=torch.bfloat16, device=DEV), off)
+    assert y.shape == (0, n)
+    # every row routed to the last expert
+    r = 700
+    offs = np.zeros(E + 1, np.int32)
+    offs[E] = r
+    x = synth.normal_bf16(171, (r, k))
+    y = g(to_dev(x), torch.as_tensor(offs, device=DEV))
+    torch.cuda.synchronize()
+    rows = synth.probe_rows(172, r, 32)
+    yr, a = oracle.grouped_f64(x, w, offs, rows=rows)
+    assert_parity(y.cpu().numpy()[rows], yr, a, "single expert")

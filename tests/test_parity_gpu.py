@@ -1,0 +1,117 @@
+"""HIP path against the CPU oracle, element by element (gpu).
+
+Bar: |y - y_ref| <= 1e-4 * sum_k |x_k w_k| for floating inputs; exact for
+integer-valued inputs (every summation order gives the exact integer).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DEV, assert_parity, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run(bg, w_bits, x_bits, pin=None):
+    g = bg.Gemm(to_dev(w_bits), pin=pin)
+    y = g(to_dev(x_bits))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def test_tiny_all_m(gpu):
+    """256x512 layer, every M in 1..32 (the tiny invariance workload)."""
+    w = synth.normal_bf16(43, (256, 512), 0.02)
+    xs = synth.normal_bf16(44, (32, 512))
+    yr, a = oracle.gemm_f64(xs, w)
+    g = gpu.Gemm(to_dev(w))
+    for m in range(1, 33):
+        y = g(to_dev(xs[:m]))
+        torch.cuda.synchronize()
+        assert_parity(y.cpu().numpy(), yr[:m], a[:m], "tiny M=%d" % m)
+
+
+@pytest.mark.parametrize("n,k", [(256, 512), (4096, 14336), (8192, 3584), (2048, 768)])
+def test_integer_exact(gpu, n, k):
+    """x, W in {-3..3}: the GPU must return the exact integer at every M size class."""
+    w = synth.int_bf16(45, (n, k))
+    mmax = 300 if n * k > 1 << 24 else 1100
+    xs = synth.int_bf16(46, (mmax, k))
+    g = gpu.Gemm(to_dev(w))
+    for m in (1, 5, 16, 17, 40, 129, 300, 1100):
+        if m > mmax:
+            continue
+        y = g(to_dev(xs[:m]))
+        torch.cuda.synchronize()
+        rows = synth.probe_rows(47 + m, m, 24)
+        ref = oracle.gemm_i64(xs[:m], w, rows=rows)
+        got = y.cpu().numpy()[rows]
+        assert np.array_equal(got, ref.astype(np.float32)), "n=%d k=%d M=%d" % (n, k, m)
+        assert np.all(np.abs(got) <= 9 * k)
+
+
+@pytest.mark.parametrize("m", [1, 3, 16, 17, 31, 64, 100, 255, 256, 257, 700, 1024, 1100])
+def test_tiles_and_ragged_tails(gpu, m):
+    """N=768 (three 256-wide or six 128-wide column blocks), K=1024: several
+    tiles in both dimensions with ragged row tails, all rows checked."""
+    w = synth.normal_bf16(48, (768, 1024), 0.02)
+    x = synth.normal_bf16(49, (m, 1024))
+    y = run(gpu, w, x)
+    yr, a = oracle.gemm_f64(x, w)
+    assert_parity(y, yr, a, "N=768 K=1024 M=%d" % m)
+
+
+@pytest.mark.parametrize("smax", [0, 4096])
+def test_forced_paths_parity(gpu, smax):
+    """Both kernel families on their own at awkward sizes."""
+    w = synth.normal_bf16(50, (512, 576), 0.02)
+    for m in (1, 15, 33, 77):
+        x = synth.normal_bf16(51 + m, (m, 576))
+        y = run(gpu, w, x, pin={"splits": 1, "stream_max_m": smax})
+        yr, a = oracle.gemm_f64(x, w)
+        assert_parity(y, yr, a, "stream_max_m=%d M=%d" % (smax, m))
+
+
+WORKLOADS = {
+    # name: (N, K, W std, x maker, M values)
+    "llama8b_down": (4096, 14336, 0.02, synth.silu_mul_bf16, (1, 16, 64, 512, 8192)),
+    "llama8b_gate_up": (28672, 4096, 0.02, synth.rms_rows_bf16, (32, 2080)),
+    "llama70b_down_tp8": (8192, 3584, 0.015, synth.normal_bf16, (1, 8, 512, 16384)),
+}
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_full_size_sampled(gpu, name):
+    """The full workload shapes in the bench's launch configuration; the oracle
+    computes sampled rows (all N columns of each)."""
+    n, k, std, maker, ms = WORKLOADS[name]
+    w = synth.normal_bf16(52, (n, k), std)
+    mmax = max(ms)
+    x = maker(53, (mmax, k))
+    g = gpu.Gemm(to_dev(w))
+    xd = to_dev(x)
+    for m in ms:
+        y = g(xd[:m])
+        torch.cuda.synchronize()
+        rows = synth.probe_rows(54 + m, m, 8)
+        yr, a = oracle.gemm_f64(x[:m], w, rows=rows)
+        assert_parity(y[torch.as_tensor(rows, device=DEV)].cpu().numpy(), yr, a, "%s M=%d" % (name, m))
+        # a property at any size: every element finite, and bounded by a
+        yf = y.float()
+        assert torch.isfinite(yf).all()
+        del y
+
+
+def test_zero_rows_and_empty(gpu):
+    w = synth.normal_bf16(55, (256, 512), 0.02)
+    g = gpu.Gemm(to_dev(w))
+    x = torch.zeros((0, 512), dtype=torch.bfloat16, device=DEV)
+    y = g(x)
+    assert y.shape == (0, 256)
+    # all-zero rows give zero exactly
+    z = torch.zeros((5, 512), dtype=torch.bfloat16, device=DEV)
+    yz = g(z)
+    torch.cuda.synchronize()
+    assert np.all(yz.cpu().numpy() == 0)
