@@ -158,6 +158,14 @@ void bi_gemm_destroy(bi_gemm_t h);
 /* The tree and tiling of a handle. */
 bi_status_t bi_gemm_get_pin(bi_gemm_t h, bi_pin_info *out);
 
+/*
+ * Name of the kernel a run with M rows launches on this handle, e.g.
+ * "bigemm_tiled<256x256>" (a static string; "" for an invalid handle or
+ * M <= 0).  For benches and tests: it launches nothing.  Every name realises
+ * the same tree; the choice only moves work.
+ */
+const char *bi_gemm_kernel_name(bi_gemm_t h, int M);
+
 /* A static English string for a status code. */
 const char *bi_status_string(bi_status_t s);
 

@@ -64,6 +64,7 @@ def _declare(lib):
         "bi_gemm_destroy": ([P], None),
         "bi_gemm_get_pin": ([P, ctypes.POINTER(BiPinInfo)], S),
         "bi_status_string": ([S], ctypes.c_char_p),
+        "bi_gemm_kernel_name": ([P, I], ctypes.c_char_p),
         "bi_last_error": ([], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -157,6 +158,10 @@ class Gemm:
         info = BiPinInfo()
         check(self._lib.bi_gemm_get_pin(self._h, ctypes.byref(info)))
         return info.as_dict()
+
+    def kernel_name(self, m: int) -> str:
+        """The kernel a call with ``m`` rows launches (no launch)."""
+        return self._lib.bi_gemm_kernel_name(self._h, int(m)).decode()
 
     def __call__(self, x, out=None, stream=None):
         import torch

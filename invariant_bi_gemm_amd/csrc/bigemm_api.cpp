@@ -460,6 +460,16 @@ bi_status_t bi_gemm_get_pin(bi_gemm_t hh, bi_pin_info* out)
     return BI_OK;
 }
 
+const char* bi_gemm_kernel_name(bi_gemm_t hh, int M)
+{
+    bi_gemm* h = handle_of(hh);
+    if (!h || M <= 0)
+        return "";
+    if (h->plan.experts != 0)
+        return "bigemm_stream_grouped+bigemm_tiled_grouped<128x128>";
+    return bigemm::dense_kernel_name(bigemm::choose_dense(h->plan, M));
+}
+
 const char* bi_status_string(bi_status_t s)
 {
     switch (s) {

@@ -31,6 +31,11 @@ struct Plan {
     int num_cus;           // compute units of the bound device
 };
 
+// The dense kernels `run` may launch; M picks one, the tree is the same.
+enum class DenseKernel { kStream16, kStream32, kTiled128, kTiled256 };
+DenseKernel choose_dense(const Plan& p, int M);
+const char* dense_kernel_name(DenseKernel k);
+
 // Launchers (bigemm_kernels.hip).  They assume validated arguments.
 hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, float* y,
                         hipStream_t stream);

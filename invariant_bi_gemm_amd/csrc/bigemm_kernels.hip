@@ -549,16 +549,37 @@ hipError_t run_tiled_grouped(const void* W, const void* x, const int32_t* off, i
 
 }  // namespace
 
+DenseKernel choose_dense(const Plan& p, int M)
+{
+    if (M <= p.stream_max_m)
+        return M <= 16 ? DenseKernel::kStream16 : DenseKernel::kStream32;
+    return M >= 1024 ? DenseKernel::kTiled256 : DenseKernel::kTiled128;
+}
+
+const char* dense_kernel_name(DenseKernel k)
+{
+    switch (k) {
+    case DenseKernel::kStream16: return "bigemm_stream<mb=1>";
+    case DenseKernel::kStream32: return "bigemm_stream<mb=2>";
+    case DenseKernel::kTiled128: return "bigemm_tiled<128x128>";
+    case DenseKernel::kTiled256: return "bigemm_tiled<256x256>";
+    }
+    return "?";
+}
+
 hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, float* y,
                         hipStream_t stream)
 {
-    if (M <= p.stream_max_m) {
-        if (M <= 16)
-            return run_stream_k<1, 8>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+    switch (choose_dense(p, M)) {
+    case DenseKernel::kStream16:
+        return run_stream_k<1, 8>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+    case DenseKernel::kStream32:
         return run_stream_k<2, 5>(W, x, M, y, p.n, p.k, p.num_cus, stream);
-    }
-    if (M >= 1024)
+    case DenseKernel::kTiled256:
         return run_tiled<256, 256, 2, 4>(W, x, M, y, p.n, p.k, stream);
+    case DenseKernel::kTiled128:
+        break;
+    }
     return run_tiled<128, 128, 2, 2>(W, x, M, y, p.n, p.k, stream);
 }
 
