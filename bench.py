@@ -129,6 +129,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama8b_down", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate-gib", type=float, default=1.0,
                     help="weight copies to rotate over, in GiB (defeats the Infinity Cache)")
+    ap.add_argument("--m", type=str, default=None,
+                    help="comma-separated M values replacing the workload's sweep (profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
@@ -149,7 +151,9 @@ def main(argv=None):
         print("no GPU visible", file=sys.stderr)
         return 1
     bg.load()
-    wl = WORKLOADS[args.workload]
+    wl = dict(WORKLOADS[args.workload])
+    if args.m:
+        wl["ms"] = [int(v) for v in args.m.split(",")]
     n, k, ms = wl["n"], wl["k"], wl["ms"]
     w_bits, x_bits = make_inputs(wl)
     w0 = to_dev(w_bits)

@@ -17,11 +17,12 @@
 // the batch, only the tiling of the output does.
 //
 // Kernel families:
-//   bigemm_tiled   large M: 2-stage LDS pipeline fed by direct global->LDS
-//                  loads, 256x256 or 128x128 output blocks, MFMA bound.
+//   bigemm_tiled   mid and large M: an NS-stage LDS pipeline fed by direct
+//                  buffer->LDS loads, one barrier per stage, output blocks
+//                  from 64x64 to 256x256 chosen by M.  MFMA bound at large M.
 //   bigemm_stream  small M: a persistent, warp-specialised weight streamer.
 //                  Two producer waves keep a deep LDS ring of W (and x) full
-//                  with direct global->LDS loads; consumer waves run the MFMA
+//                  with direct buffer->LDS loads; consumer waves run the MFMA
 //                  chain of one 16-column tile.  HBM bound.
 // Both have a grouped (MoE) variant whose per-expert row counts stay on the
 // device.
@@ -49,25 +50,28 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane L's bytes land
-// at lds_base + 16 L (lds_base must be the same in every lane of the wave).
-__device__ __forceinline__ void dma16(const void* src, const void* lds_base)
+// A raw buffer resource over `bytes` bytes at `base` (loads past the end
+// return zeros; the kernels never issue such loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
 {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16 bytes per lane from the buffer at voff + soff straight into LDS: lane
+// L's bytes land at lds_base + 16 L (lds_base is wave-uniform; it goes to M0).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                      const void* lds_base)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
 }
 
 // Workgroup barrier for the pipelined loops.  __syncthreads() would add a
-// release fence, and the compiler implements that by draining every
-// outstanding direct-to-LDS load (vmcnt(0)) -- including the prefetch of the
-// next stage.  These barriers order only what the loops need; the "memory"
-// clobber keeps the compiler from moving LDS accesses across them.
-__device__ __forceinline__ void barrier_only()
-{
-    asm volatile("s_barrier" ::: "memory");
-}
-
-// Barrier after this wave's LDS reads have returned (their buffer is about to
-// be refilled by other waves).
+// release fence, which the compiler implements by draining every outstanding
+// direct-to-LDS load (vmcnt(0)) -- including the prefetch of later stages.
+// This barrier first waits for the wave's own LDS reads (their buffer is
+// refilled by other waves after it); the "memory" clobber keeps the compiler
+// from moving memory accesses across it.
 __device__ __forceinline__ void barrier_after_lds_reads()
 {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -76,6 +80,18 @@ __device__ __forceinline__ void barrier_after_lds_reads()
 __device__ __forceinline__ void store4(float* p, const f32x4& v)
 {
     *reinterpret_cast<f32x4*>(p) = v;
+}
+
+// XOR swizzle of 16-byte chunk c of row r in an LDS tile whose rows hold kCh
+// chunks: the 16 lanes that read one MFMA fragment (16 rows, one chunk) hit
+// 16 distinct 16-byte bank groups of a 256-byte bank line.
+template <int kCh>
+__device__ __forceinline__ int swz(int r, int c)
+{
+    if constexpr (kCh >= 16)
+        return c ^ (r & 15);
+    else
+        return c ^ ((r / (16 / kCh)) & (kCh - 1));
 }
 
 // ---------------------------------------------------------------------------
@@ -87,7 +103,7 @@ __device__ __forceinline__ int clamp_off(int v, int R) { return v < 0 ? 0 : (v >
 
 // Which expert owns m-block `slot`.  Experts whose row count c satisfies
 // cmin < c <= cmax each contribute ceil(c / bm) m-blocks, in ascending expert
-// order.  Every thread of the block calls this; `sh` is E + 4 ints of LDS.
+// order.  Every thread of the block calls this; `sh` is E + 3 ints of LDS.
 // Returns the expert (or -1 when slot is past the last m-block), its block
 // index and its row range.
 __device__ int grouped_find(const int32_t* __restrict__ off, int E, int R, int bm, int cmin,
@@ -127,9 +143,11 @@ __device__ int grouped_find(const int32_t* __restrict__ off, int E, int R, int b
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel (large M)
+// Tiled kernel (mid and large M)
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN>
+// BM rows of x by BN rows of W per block, WM x WN waves, BK values of k per
+// LDS stage, NS stages in flight.
+template <int BM, int BN, int WM, int WN, int BK, int NS>
 struct TiledCfg {
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = kWaves * 64;
@@ -137,51 +155,66 @@ struct TiledCfg {
     static constexpr int TN = BN / WN;  // rows of W per wave
     static constexpr int FM = TM / 16;
     static constexpr int FN = TN / 16;
-    // one stage = 64 values of k for BN rows of W then BM rows of x, as
-    // 16-byte units (8 per row)
-    static constexpr int kStageUnits = (BM + BN) * 8;
+    static constexpr int kCh = BK / 8;  // 16-byte chunks per row per stage
+    static constexpr int kStageUnits = (BM + BN) * kCh;  // W rows first, then x rows
     static constexpr int kInstr = kStageUnits / (64 * kWaves);  // loads per wave per stage
-    static constexpr int kLdsBytes = 2 * kStageUnits * 16;
+    static constexpr int kLdsBytes = NS * kStageUnits * 16;
+    static constexpr int kSteps = BK / 32;
+    static_assert(BK == 32 || BK == 64, "a stage holds one or two MFMA k-steps");
+    static_assert(NS >= 2, "at least double buffering");
     static_assert(kStageUnits % (64 * kWaves) == 0, "a stage must split evenly over the waves");
-    static_assert(BN * 8 % 64 == 0, "one load instruction must not straddle W and x");
+    static_assert((BN * kCh) % 64 == 0, "one load instruction must not straddle W and x");
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tiles are whole MFMA tiles");
+    static_assert(kInstr * (NS - 1) < 64, "loads in flight must fit vmcnt");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
-
-// XOR swizzle of the 16-byte chunk c (0..7) of row r in a 64-wide stage:
-// the 16 lanes reading one fragment hit 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // One BM x BN output block: rows m0 .. m0+BM-1 of x/y (rows at or past
 // row_hi are clamped on load and never stored), columns n0 .. n0+BN-1 of y
 // (rows of Wb past N are clamped likewise).
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK, int NS>
 __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ Wb,
                                             float* __restrict__ y, int m0, int row_hi, int n0,
                                             int N, int K)
 {
-    using C = TiledCfg<BM, BN, WM, WN>;
+    using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
+    constexpr int kCh = C::kCh;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave % WM;
     const int wn = wave / WM;
+    const uint32_t rowb = (uint32_t)K * 2;
 
-    // Source of each of this lane's loads in a stage.  Unit u of the stage
-    // (lane-linear in LDS) holds logical chunk swz8(r, u % 8) of row r.
-    const uint16_t* src[C::kInstr];
+    const int wrows = min(BN, N - n0);
+    const int xrows = min(BM, row_hi - m0);
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wb + (size_t)n0 * K, (uint32_t)wrows * rowb);
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(x + (size_t)m0 * K, (uint32_t)xrows * rowb);
+
+    // Byte offset of each of this lane's loads within a stage's rows.  Unit
+    // u of the stage (lane-linear in LDS) holds logical chunk swz(r, u % kCh)
+    // of row r; rows past the valid range re-read the last valid row.
+    uint32_t voff[C::kInstr];
 #pragma unroll
     for (int j = 0; j < C::kInstr; ++j) {
         const int u = (wave * C::kInstr + j) * 64 + lane;
-        if (u < BN * 8) {
-            const int r = u >> 3;
-            const int n = min(n0 + r, N - 1);
-            src[j] = Wb + (size_t)n * K + swz8(r, u & 7) * 8;
+        if (u < BN * kCh) {
+            const int r = u / kCh;
+            voff[j] = (uint32_t)min(r, wrows - 1) * rowb + swz<kCh>(r, u % kCh) * 16;
         } else {
-            const int r = (u - BN * 8) >> 3;
-            const int m = min(m0 + r, row_hi - 1);
-            src[j] = x + (size_t)m * K + swz8(r, (u - BN * 8) & 7) * 8;
+            const int uu = u - BN * kCh;
+            const int r = uu / kCh;
+            voff[j] = (uint32_t)min(r, xrows - 1) * rowb + swz<kCh>(r, uu % kCh) * 16;
         }
     }
+    auto issue = [&](int s, int buf) {
+#pragma unroll
+        for (int j = 0; j < C::kInstr; ++j) {
+            const int u0 = (wave * C::kInstr + j) * 64;
+            dma16(u0 < BN * kCh ? rW : rX, voff[j], (uint32_t)s * (BK * 2),
+                  lds + buf * C::kStageUnits + u0);
+        }
+    };
 
     f32x4 acc[C::FN][C::FM];
 #pragma unroll
@@ -190,38 +223,36 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
         for (int j = 0; j < C::FM; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / 64;
-    auto issue = [&](int s, int buf) {
+    const int nk = K / BK;
 #pragma unroll
-        for (int j = 0; j < C::kInstr; ++j)
-            dma16(src[j] + (size_t)s * 64, lds + buf * C::kStageUnits + (wave * C::kInstr + j) * 64);
-    };
-
-    issue(0, 0);
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nk)
+            issue(s, s);
     for (int s = 0; s < nk; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nk) {
-            issue(s + 1, buf ^ 1);
-            wait_vmcnt<C::kInstr>();  // this wave's loads of stage s have landed
-        } else {
+        // this wave's loads of stage s have landed ...
+        if (s + NS - 2 < nk)
+            wait_vmcnt<C::kInstr * (NS - 2)>();
+        else
             wait_vmcnt<0>();
-        }
-        barrier_only();  // ... and every other wave's
-        const uint4* sW = lds + buf * C::kStageUnits;
-        const uint4* sX = sW + BN * 8;
+        // ... and every wave's; every wave is done reading stage s-1
+        barrier_after_lds_reads();
+        if (s + NS - 1 < nk)
+            issue(s + NS - 1, (s + NS - 1) % NS);  // into the buffer of stage s-1
+        const uint4* sW = lds + (s % NS) * C::kStageUnits;
+        const uint4* sX = sW + BN * kCh;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < C::kSteps; ++ks) {
             const int cl = ks * 4 + (lane >> 4);
             uint4 a[C::FN], b[C::FM];
 #pragma unroll
             for (int t = 0; t < C::FN; ++t) {
                 const int r = wn * C::TN + t * 16 + (lane & 15);
-                a[t] = sW[r * 8 + swz8(r, cl)];
+                a[t] = sW[r * kCh + swz<kCh>(r, cl)];
             }
 #pragma unroll
             for (int t = 0; t < C::FM; ++t) {
                 const int r = wm * C::TM + t * 16 + (lane & 15);
-                b[t] = sX[r * 8 + swz8(r, cl)];
+                b[t] = sX[r * kCh + swz<kCh>(r, cl)];
             }
 #pragma unroll
             for (int i = 0; i < C::FN; ++i)
@@ -229,7 +260,6 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
                 for (int j = 0; j < C::FM; ++j)
                     acc[i][j] = mfma_step(a[i], b[j], acc[i][j]);
         }
-        barrier_after_lds_reads();  // buffer `buf` is refilled at the next iteration
     }
 
 #pragma unroll
@@ -265,28 +295,28 @@ __device__ __forceinline__ void tile_of_block(int b, int nblocks, int tiles_m, i
     *tn = r / rows;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK, int NS>
 __global__ void __launch_bounds__(WM * WN * 64)
     bigemm_tiled(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                  float* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n, int group_m)
 {
-    using C = TiledCfg<BM, BN, WM, WN>;
-    __shared__ uint4 lds[2 * C::kStageUnits];
+    using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
+    __shared__ uint4 lds[NS * C::kStageUnits];
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
-    tiled_block<BM, BN, WM, WN>(lds, x, W, y, tm * BM, M, tn * BN, N, K);
+    tiled_block<BM, BN, WM, WN, BK, NS>(lds, x, W, y, tm * BM, M, tn * BN, N, K);
 }
 
 // Grouped: block (slot, tn) where slot enumerates the m-blocks of experts
 // with more than cmin rows.
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK, int NS>
 __global__ void __launch_bounds__(WM * WN * 64)
     bigemm_tiled_grouped(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                          float* __restrict__ y, const int32_t* __restrict__ off, int E, int R,
                          int N, int K, int tiles_n, int cmin)
 {
-    using C = TiledCfg<BM, BN, WM, WN>;
-    __shared__ uint4 lds[2 * C::kStageUnits];
+    using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
+    __shared__ uint4 lds[NS * C::kStageUnits];
     static_assert(C::kLdsBytes >= (kMaxExperts + 4) * 4, "offsets must fit the stage buffers");
     const int slot = blockIdx.x / tiles_n;
     const int tn = blockIdx.x % tiles_n;
@@ -295,7 +325,8 @@ __global__ void __launch_bounds__(WM * WN * 64)
                                reinterpret_cast<int*>(lds));
     if (e < 0)
         return;
-    tiled_block<BM, BN, WM, WN>(lds, x, W + (size_t)e * N * K, y, lo + lb * BM, hi, tn * BN, N, K);
+    tiled_block<BM, BN, WM, WN, BK, NS>(lds, x, W + (size_t)e * N * K, y, lo + lb * BM, hi,
+                                        tn * BN, N, K);
 }
 
 // ---------------------------------------------------------------------------
@@ -311,15 +342,15 @@ struct StreamCfg {
     static constexpr int kStageUnits = kRows * kChunks;
     static constexpr int kInstr = kStageUnits / (64 * kProducers);  // per producer per stage
     static constexpr int kSteps = BKS / 32;
-    static constexpr int kSwz = kChunks < 16 ? kChunks - 1 : 15;
     static constexpr int kLdsBytes = NR * kStageUnits * 16;
     static_assert(kStageUnits % (64 * kProducers) == 0, "a stage must split evenly");
     static_assert(kInstr * (NR - 1) < 64, "loads in flight must fit vmcnt");
     static_assert((16 * kChunks) % 64 == 0, "one load must not straddle W and x");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
-// Where work item `item` lives: rows m0.. of x/y (row_hi excluded), W rows
-// n0 .. n0+15 of the expert weight *Wb.
+// Where work item `item` lives: rows m0 .. row_hi-1 of x/y, W rows
+// n0 .. n0+15 of the expert weight Wb.
 struct StreamItem {
     int m0, row_hi, n0;
     const uint16_t* Wb;
@@ -329,12 +360,14 @@ template <int MB, int NR, int BKS>
 __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ W, float* __restrict__ y,
                                             int N, int K, int tiles_n, int nitems,
-                                            // dense: M rows; grouped: expert list in LDS
+                                            // dense: M rows; grouped: clamped offsets and
+                                            // the expert list, both in LDS
                                             int M, const int* sh_off, const int* elist)
 {
     using C = StreamCfg<MB, NR, BKS>;
+    constexpr int kCh = C::kChunks;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = gridDim.x;
     const int mine = nitems > (int)blockIdx.x ? (nitems - 1 - (int)blockIdx.x) / G + 1 : 0;
     const int nst = K / BKS;
@@ -359,56 +392,72 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
     };
 
     if (wave >= MB) {
-        // ---- producer ----
+        // ---- producer: keeps NR-1 stages of W and x in flight ----
         const int pw = wave - MB;
+        const uint32_t rowb = (uint32_t)K * 2;
+        __amdgpu_buffer_rsrc_t rW = make_rsrc(W, 16), rX = make_rsrc(x, 16);
+        uint32_t voff[C::kInstr];
+        int cur_it = -1, k_stage = nst;
+        // stages are issued in order q = 0, 1, 2, ...: nst stages per item
         auto issue = [&](int q) {
-            const StreamItem s = item_at(q / nst);
-            const int k0 = (q % nst) * BKS;
+            if (k_stage == nst) {  // entering the next item: its rows, once
+                ++cur_it;
+                k_stage = 0;
+                const StreamItem s = item_at(cur_it);
+                const int xrows = min(16 * MB, s.row_hi - s.m0);
+                rW = make_rsrc(s.Wb + (size_t)s.n0 * K, 16 * rowb);
+                rX = make_rsrc(x + (size_t)s.m0 * K, (uint32_t)xrows * rowb);
+#pragma unroll
+                for (int j = 0; j < C::kInstr; ++j) {
+                    const int u = (pw * C::kInstr + j) * 64 + lane;
+                    const int r = u / kCh;
+                    const int c = swz<kCh>(r, u % kCh);
+                    voff[j] = (r < 16 ? (uint32_t)r : (uint32_t)min(r - 16, xrows - 1)) * rowb + c * 16;
+                }
+            }
             uint4* dst = ring + (q % NR) * C::kStageUnits;
 #pragma unroll
             for (int j = 0; j < C::kInstr; ++j) {
                 const int u0 = (pw * C::kInstr + j) * 64;
-                const int u = u0 + lane;
-                const int r = u / C::kChunks;
-                const int c = (u % C::kChunks) ^ (r & C::kSwz);
-                const uint16_t* src;
-                if (r < 16) {
-                    src = s.Wb + (size_t)(s.n0 + r) * K + k0 + c * 8;
-                } else {
-                    const int m = min(s.m0 + (r - 16), s.row_hi - 1);
-                    src = x + (size_t)m * K + k0 + c * 8;
-                }
-                dma16(src, dst + u0);
+                dma16(u0 < 16 * kCh ? rW : rX, voff[j], (uint32_t)k_stage * (BKS * 2), dst + u0);
             }
+            ++k_stage;
         };
         const int pro = total < NR - 1 ? total : NR - 1;
         for (int q = 0; q < pro; ++q)
             issue(q);
         for (int q = 0; q < total; ++q) {
-            if (q + NR - 2 <= total - 1)
+            if (q + NR - 2 < total)
                 wait_vmcnt<C::kInstr * (NR - 2)>();
             else
                 wait_vmcnt<0>();
-            barrier_only();  // stage q is in LDS; slot (q-1) % NR is free
+            barrier_after_lds_reads();  // stage q is in LDS; slot (q-1) % NR is free
             if (q + NR - 1 < total)
                 issue(q + NR - 1);
         }
     } else {
-        // ---- consumer: the MFMA chain of m-tile `wave` ----
+        // ---- consumer: the MFMA chain of m-tile `wave`, one stage behind its
+        // LDS reads so that they overlap the chain ----
         const int ci = wave;
         const int rw = lane & 15;
         const int rx = 16 + 16 * ci + rw;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int q = 0; q < total; ++q) {
-            // stage q is in LDS; this wave's reads of stage q-1 have returned
-            barrier_after_lds_reads();
+        uint4 a0[C::kSteps], b0[C::kSteps], a1[C::kSteps], b1[C::kSteps];
+        auto read = [&](int q, uint4* a, uint4* b) {
             const uint4* st = ring + (q % NR) * C::kStageUnits;
-            uint4 a[C::kSteps], b[C::kSteps];
 #pragma unroll
             for (int t = 0; t < C::kSteps; ++t) {
                 const int cl = 4 * t + (lane >> 4);
-                a[t] = st[rw * C::kChunks + (cl ^ (rw & C::kSwz))];
-                b[t] = st[rx * C::kChunks + (cl ^ (rx & C::kSwz))];
+                a[t] = st[rw * kCh + swz<kCh>(rw, cl)];
+                b[t] = st[rx * kCh + swz<kCh>(rx, cl)];
+            }
+        };
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // stage q's fragments are in (a, b); read stage q+1 into (na, nb)
+        // before running q's chain
+        auto stage = [&](int q, const uint4* a, const uint4* b, uint4* na, uint4* nb) {
+            if (q + 1 < total) {
+                barrier_after_lds_reads();
+                read(q + 1, na, nb);
             }
 #pragma unroll
             for (int t = 0; t < C::kSteps; ++t)
@@ -420,6 +469,15 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
                     store4(y + (size_t)m * N + s.n0 + 4 * (lane >> 4), acc);
                 acc = f32x4{0.f, 0.f, 0.f, 0.f};
             }
+        };
+        if (total > 0) {
+            barrier_after_lds_reads();
+            read(0, a0, b0);
+        }
+        for (int q = 0; q < total; q += 2) {
+            stage(q, a0, b0, a1, b1);
+            if (q + 1 < total)
+                stage(q + 1, a1, b1, a0, b0);
         }
     }
 }
@@ -480,17 +538,17 @@ __global__ void __launch_bounds__((MB + 2) * 64)
 // ---------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK, int NS>
 hipError_t run_tiled(const void* W, const void* x, int M, float* y, int N, int K,
                      hipStream_t stream)
 {
-    using C = TiledCfg<BM, BN, WM, WN>;
+    using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int nblocks = tiles_m * tiles_n;
-    hipLaunchKernelGGL((bigemm_tiled<BM, BN, WM, WN>), dim3(nblocks), dim3(C::kThreads), 0, stream,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K,
-                       tiles_m, tiles_n, 4);
+    hipLaunchKernelGGL((bigemm_tiled<BM, BN, WM, WN, BK, NS>), dim3(nblocks), dim3(C::kThreads),
+                       0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
+                       y, M, N, K, tiles_m, tiles_n, 4);
     return hipGetLastError();
 }
 
@@ -528,11 +586,11 @@ hipError_t run_stream_grouped(const void* W, const void* x, const int32_t* off, 
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK, int NS>
 hipError_t run_tiled_grouped(const void* W, const void* x, const int32_t* off, int E, int R,
                              float* y, int N, int K, int cmin, hipStream_t stream)
 {
-    using C = TiledCfg<BM, BN, WM, WN>;
+    using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     const int tiles_n = (N + BN - 1) / BN;
     // m-blocks of experts with more than cmin rows: at most R/BM + (number of
     // such experts), and there are at most min(E, R/(cmin+1)) of those.
@@ -541,19 +599,43 @@ hipError_t run_tiled_grouped(const void* W, const void* x, const int32_t* off, i
     const long long nblocks = slots * tiles_n;
     if (nblocks <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL((bigemm_tiled_grouped<BM, BN, WM, WN>), dim3((unsigned)nblocks),
+    hipLaunchKernelGGL((bigemm_tiled_grouped<BM, BN, WM, WN, BK, NS>), dim3((unsigned)nblocks),
                        dim3(C::kThreads), 0, stream, static_cast<const uint16_t*>(x),
                        static_cast<const uint16_t*>(W), y, off, E, R, N, K, tiles_n, cmin);
     return hipGetLastError();
 }
 
+// The tiled configurations, largest first: {BM, BN, blocks per CU}.
+struct TileShape {
+    DenseKernel kind;
+    int bm, bn, per_cu;
+};
+constexpr TileShape kTileShapes[] = {
+    {DenseKernel::kTiled256, 256, 256, 1},
+    {DenseKernel::kTiled128, 128, 128, 2},
+    {DenseKernel::kTiled128x64, 128, 64, 2},
+    {DenseKernel::kTiled64, 64, 64, 2},
+};
+
 }  // namespace
 
 DenseKernel choose_dense(const Plan& p, int M)
 {
-    if (M <= p.stream_max_m)
-        return M <= 16 ? DenseKernel::kStream16 : DenseKernel::kStream32;
-    return M >= 1024 ? DenseKernel::kTiled256 : DenseKernel::kTiled128;
+    if (M <= p.stream_max_m) {
+        if (M <= 16)
+            return DenseKernel::kStream16;
+        if (M <= 32)
+            return DenseKernel::kStream32;
+        return DenseKernel::kStream64;
+    }
+    // The largest output block that still gives every CU a block; failing
+    // that, the one with the most blocks.
+    for (const TileShape& t : kTileShapes) {
+        const long long blocks = (long long)((M + t.bm - 1) / t.bm) * ((p.n + t.bn - 1) / t.bn);
+        if (blocks >= p.num_cus)
+            return t.kind;
+    }
+    return DenseKernel::kTiled64;
 }
 
 const char* dense_kernel_name(DenseKernel k)
@@ -561,6 +643,9 @@ const char* dense_kernel_name(DenseKernel k)
     switch (k) {
     case DenseKernel::kStream16: return "bigemm_stream<mb=1>";
     case DenseKernel::kStream32: return "bigemm_stream<mb=2>";
+    case DenseKernel::kStream64: return "bigemm_stream<mb=4>";
+    case DenseKernel::kTiled64: return "bigemm_tiled<64x64>";
+    case DenseKernel::kTiled128x64: return "bigemm_tiled<128x64>";
     case DenseKernel::kTiled128: return "bigemm_tiled<128x128>";
     case DenseKernel::kTiled256: return "bigemm_tiled<256x256>";
     }
@@ -575,12 +660,18 @@ hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, floa
         return run_stream_k<1, 8>(W, x, M, y, p.n, p.k, p.num_cus, stream);
     case DenseKernel::kStream32:
         return run_stream_k<2, 5>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+    case DenseKernel::kStream64:
+        return run_stream_k<4, 3>(W, x, M, y, p.n, p.k, p.num_cus, stream);
     case DenseKernel::kTiled256:
-        return run_tiled<256, 256, 2, 4>(W, x, M, y, p.n, p.k, stream);
+        return run_tiled<256, 256, 2, 4, 32, 4>(W, x, M, y, p.n, p.k, stream);
     case DenseKernel::kTiled128:
+        return run_tiled<128, 128, 2, 2, 64, 2>(W, x, M, y, p.n, p.k, stream);
+    case DenseKernel::kTiled128x64:
+        return run_tiled<128, 64, 2, 2, 64, 3>(W, x, M, y, p.n, p.k, stream);
+    case DenseKernel::kTiled64:
         break;
     }
-    return run_tiled<128, 128, 2, 2>(W, x, M, y, p.n, p.k, stream);
+    return run_tiled<64, 64, 2, 2, 64, 4>(W, x, M, y, p.n, p.k, stream);
 }
 
 hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int32_t* offsets,
@@ -601,7 +692,7 @@ hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int
         if (err != hipSuccess)
             return err;
     }
-    return run_tiled_grouped<128, 128, 2, 2>(W, x, offsets, p.experts, R, y, p.n, p.k, smax, stream);
+    return run_tiled_grouped<128, 128, 2, 2, 64, 2>(W, x, offsets, p.experts, R, y, p.n, p.k, smax, stream);
 }
 
 }  // namespace bigemm
