@@ -27,6 +27,8 @@
 // Both have a grouped (MoE) variant whose per-expert row counts stay on the
 // device.
 
+#include <type_traits>
+
 #include "bigemm_internal.h"
 
 namespace bigemm {
@@ -83,15 +85,20 @@ __device__ __forceinline__ void store4(float* p, const f32x4& v)
 }
 
 // XOR swizzle of 16-byte chunk c of row r in an LDS tile whose rows hold kCh
-// chunks: the 16 lanes that read one MFMA fragment (16 rows, one chunk) hit
-// 16 distinct 16-byte bank groups of a 256-byte bank line.
+// chunks.  An MFMA fragment read has 16 lanes reading one chunk of 16
+// consecutive rows.  The XOR terms are the ones measured free of LDS bank
+// conflicts on gfx950 for exactly that read (SQ_LDS_BANK_CONFLICT = 0 for a
+// ds_read_b128 of 16 rows x 4 chunks), per row width: 64-byte rows
+// (r >> 1) & 3, 128-byte rows (r >> 1) & 7, 256- and 512-byte rows r & 15.
 template <int kCh>
 __device__ __forceinline__ int swz(int r, int c)
 {
     if constexpr (kCh >= 16)
         return c ^ (r & 15);
+    else if constexpr (kCh == 8)
+        return c ^ ((r >> 1) & 7);
     else
-        return c ^ ((r / (16 / kCh)) & (kCh - 1));
+        return c ^ ((r >> 1) & 3);
 }
 
 // ---------------------------------------------------------------------------
@@ -332,21 +339,55 @@ __global__ void __launch_bounds__(WM * WN * 64)
 // ---------------------------------------------------------------------------
 // Streaming kernel (small M)
 // ---------------------------------------------------------------------------
-template <int MB, int NR, int BKS>
+// MB consumer waves (one 16-row m-tile each) share one 16-column strip of W.
+// A stage holds BKS values of k for the 16 W rows and the first XR rows of
+// the m-block (XR = 16*MB, or fewer when the call has fewer rows: the
+// consumer of a single m-tile then re-reads row XR-1 for its padding rows).
+// NP producer waves split a stage's loads; NR stages live in an LDS ring.
+constexpr int kStreamLdsBudget = 144 * 1024;
+// Producer waves per streaming workgroup: the WG has at most 8 waves (two
+// per SIMD, so each may use 256 VGPRs); narrower stages have fewer loads and
+// use fewer producers.
+template <int MB, int BKS>
+constexpr int stream_producers()
+{
+    return BKS == 256 ? 8 - MB : (BKS == 128 ? (6 - MB > 2 ? 6 - MB : 2) : 2);
+}
+
+template <int MB, int XR, int BKS, int NP>
+struct StreamShape {
+    static constexpr int kChunks = BKS / 8;  // 16-byte units per row per stage
+    static constexpr int kStageUnits = (16 + XR) * kChunks;
+    static constexpr int kT = kStageUnits / 64;  // load instructions per stage
+    static constexpr int kHi = (kT + NP - 1) / NP;  // share of the first kT % NP producers
+    static constexpr int kLo = kT / NP;             // share of the others
+    static constexpr int kByLds = kStreamLdsBudget / (kStageUnits * 16);
+    static constexpr int kByVmcnt = 63 / kHi + 1;
+    static constexpr int kNR = kByLds < kByVmcnt ? (kByLds < 16 ? kByLds : 16)
+                                                 : (kByVmcnt < 16 ? kByVmcnt : 16);
+};
+
+template <int MB, int XR, int BKS, int NP>
 struct StreamCfg {
-    static constexpr int kConsumers = MB;  // one per 16-row m-tile
-    static constexpr int kProducers = 2;
-    static constexpr int kThreads = (MB + kProducers) * 64;
-    static constexpr int kChunks = BKS / 8;       // 16-byte units per row per stage
-    static constexpr int kRows = 16 * (1 + MB);   // 16 rows of W, then 16*MB rows of x
-    static constexpr int kStageUnits = kRows * kChunks;
-    static constexpr int kInstr = kStageUnits / (64 * kProducers);  // per producer per stage
+    using S = StreamShape<MB, XR, BKS, NP>;
+    static constexpr int kConsumers = MB;
+    static constexpr int kProducers = NP;
+    static constexpr int kThreads = (MB + NP) * 64;
+    static constexpr int kChunks = S::kChunks;
+    static constexpr int kStageUnits = S::kStageUnits;
+    static constexpr int kT = S::kT;
+    static constexpr int kHi = S::kHi;
+    static constexpr int kLo = S::kLo;
+    static constexpr int NR = S::kNR;
     static constexpr int kSteps = BKS / 32;
     static constexpr int kLdsBytes = NR * kStageUnits * 16;
-    static_assert(kStageUnits % (64 * kProducers) == 0, "a stage must split evenly");
-    static_assert(kInstr * (NR - 1) < 64, "loads in flight must fit vmcnt");
+    static_assert(XR == 16 * MB || (MB == 1 && XR < 16), "x rows per stage");
+    static_assert(kStageUnits % 64 == 0, "a stage is whole load instructions");
     static_assert((16 * kChunks) % 64 == 0, "one load must not straddle W and x");
-    static_assert(kLdsBytes <= 160 * 1024, "LDS");
+    static_assert(kLo >= 1, "every producer loads something");
+    static_assert(NR >= 3, "ring too shallow");
+    static_assert(kHi * (NR - 1) < 64, "loads in flight must fit vmcnt");
+    static_assert(kLdsBytes <= kStreamLdsBudget, "LDS");
 };
 
 // Where work item `item` lives: rows m0 .. row_hi-1 of x/y, W rows
@@ -356,7 +397,7 @@ struct StreamItem {
     const uint16_t* Wb;
 };
 
-template <int MB, int NR, int BKS>
+template <int MB, int XR, int BKS, int NP>
 __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ W, float* __restrict__ y,
                                             int N, int K, int tiles_n, int nitems,
@@ -364,8 +405,9 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
                                             // the expert list, both in LDS
                                             int M, const int* sh_off, const int* elist)
 {
-    using C = StreamCfg<MB, NR, BKS>;
+    using C = StreamCfg<MB, XR, BKS, NP>;
     constexpr int kCh = C::kChunks;
+    constexpr int NR = C::NR;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = gridDim.x;
@@ -392,55 +434,63 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
     };
 
     if (wave >= MB) {
-        // ---- producer: keeps NR-1 stages of W and x in flight ----
+        // ---- producers: keep NR-1 stages of W and x in flight ----
         const int pw = wave - MB;
-        const uint32_t rowb = (uint32_t)K * 2;
-        __amdgpu_buffer_rsrc_t rW = make_rsrc(W, 16), rX = make_rsrc(x, 16);
-        uint32_t voff[C::kInstr];
-        int cur_it = -1, k_stage = nst;
-        // stages are issued in order q = 0, 1, 2, ...: nst stages per item
-        auto issue = [&](int q) {
-            if (k_stage == nst) {  // entering the next item: its rows, once
-                ++cur_it;
-                k_stage = 0;
-                const StreamItem s = item_at(cur_it);
-                const int xrows = min(16 * MB, s.row_hi - s.m0);
-                rW = make_rsrc(s.Wb + (size_t)s.n0 * K, 16 * rowb);
-                rX = make_rsrc(x + (size_t)s.m0 * K, (uint32_t)xrows * rowb);
+        auto produce = [&](auto count_tag, int first) {
+            constexpr int kI = decltype(count_tag)::value;
+            const uint32_t rowb = (uint32_t)K * 2;
+            __amdgpu_buffer_rsrc_t rW = make_rsrc(W, 16), rX = make_rsrc(x, 16);
+            uint32_t voff[kI];
+            int cur_it = -1, k_stage = nst;
+            // stages are issued in order q = 0, 1, 2, ...: nst stages per item
+            auto issue = [&](int q) {
+                if (k_stage == nst) {  // entering the next item: its rows, once
+                    ++cur_it;
+                    k_stage = 0;
+                    const StreamItem s = item_at(cur_it);
+                    const int xrows = min(XR, s.row_hi - s.m0);
+                    rW = make_rsrc(s.Wb + (size_t)s.n0 * K, 16 * rowb);
+                    rX = make_rsrc(x + (size_t)s.m0 * K, (uint32_t)xrows * rowb);
 #pragma unroll
-                for (int j = 0; j < C::kInstr; ++j) {
-                    const int u = (pw * C::kInstr + j) * 64 + lane;
-                    const int r = u / kCh;
-                    const int c = swz<kCh>(r, u % kCh);
-                    voff[j] = (r < 16 ? (uint32_t)r : (uint32_t)min(r - 16, xrows - 1)) * rowb + c * 16;
+                    for (int j = 0; j < kI; ++j) {
+                        const int u = (first + j) * 64 + lane;
+                        const int r = u / kCh;
+                        const int c = swz<kCh>(r, u % kCh);
+                        voff[j] = (r < 16 ? (uint32_t)r : (uint32_t)min(r - 16, xrows - 1)) * rowb + c * 16;
+                    }
                 }
-            }
-            uint4* dst = ring + (q % NR) * C::kStageUnits;
+                uint4* dst = ring + (q % NR) * C::kStageUnits;
 #pragma unroll
-            for (int j = 0; j < C::kInstr; ++j) {
-                const int u0 = (pw * C::kInstr + j) * 64;
-                dma16(u0 < 16 * kCh ? rW : rX, voff[j], (uint32_t)k_stage * (BKS * 2), dst + u0);
+                for (int j = 0; j < kI; ++j) {
+                    const int u0 = (first + j) * 64;
+                    dma16(u0 < 16 * kCh ? rW : rX, voff[j], (uint32_t)k_stage * (BKS * 2), dst + u0);
+                }
+                ++k_stage;
+            };
+            const int pro = total < NR - 1 ? total : NR - 1;
+            for (int q = 0; q < pro; ++q)
+                issue(q);
+            for (int q = 0; q < total; ++q) {
+                if (q + NR - 2 < total)
+                    wait_vmcnt<kI * (NR - 2)>();
+                else
+                    wait_vmcnt<0>();
+                barrier_after_lds_reads();  // stage q is in LDS; slot (q-1) % NR is free
+                if (q + NR - 1 < total)
+                    issue(q + NR - 1);
             }
-            ++k_stage;
         };
-        const int pro = total < NR - 1 ? total : NR - 1;
-        for (int q = 0; q < pro; ++q)
-            issue(q);
-        for (int q = 0; q < total; ++q) {
-            if (q + NR - 2 < total)
-                wait_vmcnt<C::kInstr * (NR - 2)>();
-            else
-                wait_vmcnt<0>();
-            barrier_after_lds_reads();  // stage q is in LDS; slot (q-1) % NR is free
-            if (q + NR - 1 < total)
-                issue(q + NR - 1);
-        }
+        constexpr int kExtra = C::kT % NP;  // producers that take kHi loads
+        if (pw < kExtra)
+            produce(std::integral_constant<int, C::kHi>{}, pw * C::kHi);
+        else
+            produce(std::integral_constant<int, C::kLo>{}, kExtra * C::kHi + (pw - kExtra) * C::kLo);
     } else {
         // ---- consumer: the MFMA chain of m-tile `wave`, one stage behind its
         // LDS reads so that they overlap the chain ----
         const int ci = wave;
         const int rw = lane & 15;
-        const int rx = 16 + 16 * ci + rw;
+        const int rx = 16 + (MB == 1 ? min(rw, XR - 1) : 16 * ci + rw);
         uint4 a0[C::kSteps], b0[C::kSteps], a1[C::kSteps], b1[C::kSteps];
         auto read = [&](int q, uint4* a, uint4* b) {
             const uint4* st = ring + (q % NR) * C::kStageUnits;
@@ -482,28 +532,28 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
     }
 }
 
-template <int MB, int NR, int BKS>
-__global__ void __launch_bounds__((MB + 2) * 64)
+template <int MB, int XR, int BKS, int NP>
+__global__ void __launch_bounds__((MB + NP) * 64)
     bigemm_stream(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                   float* __restrict__ y, int M, int N, int K)
 {
-    using C = StreamCfg<MB, NR, BKS>;
-    __shared__ uint4 ring[NR * C::kStageUnits];
+    using C = StreamCfg<MB, XR, BKS, NP>;
+    __shared__ uint4 ring[C::NR * C::kStageUnits];
     const int tiles_n = N / 16;
     const int mblocks = (M + 16 * MB - 1) / (16 * MB);
-    stream_body<MB, NR, BKS>(ring, x, W, y, N, K, tiles_n, mblocks * tiles_n, M, nullptr, nullptr);
+    stream_body<MB, XR, BKS, NP>(ring, x, W, y, N, K, tiles_n, mblocks * tiles_n, M, nullptr, nullptr);
 }
 
 // Grouped: one m-block per expert whose row count c satisfies 0 < c <= cmax
-// (cmax <= 16 * MB).
-template <int MB, int NR, int BKS>
-__global__ void __launch_bounds__((MB + 2) * 64)
+// (cmax <= XR).
+template <int MB, int XR, int BKS, int NP>
+__global__ void __launch_bounds__((MB + NP) * 64)
     bigemm_stream_grouped(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                           float* __restrict__ y, const int32_t* __restrict__ off, int E, int R,
                           int N, int K, int cmax)
 {
-    using C = StreamCfg<MB, NR, BKS>;
-    __shared__ uint4 ring[NR * C::kStageUnits];
+    using C = StreamCfg<MB, XR, BKS, NP>;
+    __shared__ uint4 ring[C::NR * C::kStageUnits];
     __shared__ int sh_off[kMaxExperts + 1];
     __shared__ int elist[kMaxExperts + 1];
     // compact, ascending list of the experts this kernel serves
@@ -532,7 +582,7 @@ __global__ void __launch_bounds__((MB + 2) * 64)
     __syncthreads();
     const int tiles_n = N / 16;
     const int count = elist[kMaxExperts];
-    stream_body<MB, NR, BKS>(ring, x, W, y, N, K, tiles_n, count * tiles_n, 0, sh_off, elist);
+    stream_body<MB, XR, BKS, NP>(ring, x, W, y, N, K, tiles_n, count * tiles_n, 0, sh_off, elist);
 }
 
 // ---------------------------------------------------------------------------
@@ -552,35 +602,37 @@ hipError_t run_tiled(const void* W, const void* x, int M, float* y, int N, int K
     return hipGetLastError();
 }
 
-template <int MB, int NR, int BKS>
+template <int MB, int XR, int BKS, int NP>
 hipError_t run_stream(const void* W, const void* x, int M, float* y, int N, int K, int num_cus,
                       hipStream_t stream)
 {
-    using C = StreamCfg<MB, NR, BKS>;
+    using C = StreamCfg<MB, XR, BKS, NP>;
     const int items = ((M + 16 * MB - 1) / (16 * MB)) * (N / 16);
     const int grid = items < num_cus ? items : num_cus;
-    hipLaunchKernelGGL((bigemm_stream<MB, NR, BKS>), dim3(grid), dim3(C::kThreads), 0, stream,
+    hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP>), dim3(grid), dim3(C::kThreads), 0, stream,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K);
     return hipGetLastError();
 }
 
-template <int MB, int NR>
+// The stage depth: 256 values of k when K allows it.  x rows per stage: at
+// least what a 64-row load group of that stage width needs.
+template <int MB, int XR>
 hipError_t run_stream_k(const void* W, const void* x, int M, float* y, int N, int K, int num_cus,
                         hipStream_t stream)
 {
     if (K % 256 == 0)
-        return run_stream<MB, NR, 256>(W, x, M, y, N, K, num_cus, stream);
+        return run_stream<MB, XR, 256, stream_producers<MB, 256>()>(W, x, M, y, N, K, num_cus, stream);
     if (K % 128 == 0)
-        return run_stream<MB, NR, 128>(W, x, M, y, N, K, num_cus, stream);
-    return run_stream<MB, NR, 64>(W, x, M, y, N, K, num_cus, stream);
+        return run_stream<MB, (XR < 4 ? 4 : XR), 128, stream_producers<MB, 128>()>(W, x, M, y, N, K, num_cus, stream);
+    return run_stream<MB, (XR < 8 ? 8 : XR), 64, stream_producers<MB, 64>()>(W, x, M, y, N, K, num_cus, stream);
 }
 
-template <int MB, int NR, int BKS>
+template <int MB, int XR, int BKS, int NP>
 hipError_t run_stream_grouped(const void* W, const void* x, const int32_t* off, int E, int R,
                               float* y, int N, int K, int cmax, int num_cus, hipStream_t stream)
 {
-    using C = StreamCfg<MB, NR, BKS>;
-    hipLaunchKernelGGL((bigemm_stream_grouped<MB, NR, BKS>), dim3(num_cus), dim3(C::kThreads), 0,
+    using C = StreamCfg<MB, XR, BKS, NP>;
+    hipLaunchKernelGGL((bigemm_stream_grouped<MB, XR, BKS, NP>), dim3(num_cus), dim3(C::kThreads), 0,
                        stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y,
                        off, E, R, N, K, cmax);
     return hipGetLastError();
@@ -657,11 +709,17 @@ hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, floa
 {
     switch (choose_dense(p, M)) {
     case DenseKernel::kStream16:
-        return run_stream_k<1, 8>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+        if (M <= 2)
+            return run_stream_k<1, 2>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+        if (M <= 4)
+            return run_stream_k<1, 4>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+        if (M <= 8)
+            return run_stream_k<1, 8>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+        return run_stream_k<1, 16>(W, x, M, y, p.n, p.k, p.num_cus, stream);
     case DenseKernel::kStream32:
-        return run_stream_k<2, 5>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+        return run_stream_k<2, 32>(W, x, M, y, p.n, p.k, p.num_cus, stream);
     case DenseKernel::kStream64:
-        return run_stream_k<4, 3>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+        return run_stream_k<4, 64>(W, x, M, y, p.n, p.k, p.num_cus, stream);
     case DenseKernel::kTiled256:
         return run_tiled<256, 256, 2, 4, 32, 4>(W, x, M, y, p.n, p.k, stream);
     case DenseKernel::kTiled128:
@@ -684,11 +742,11 @@ hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int
     hipError_t err = hipSuccess;
     if (smax > 0) {
         if (p.k % 256 == 0)
-            err = run_stream_grouped<1, 8, 256>(W, x, offsets, p.experts, R, y, p.n, p.k, smax, p.num_cus, stream);
+            err = run_stream_grouped<1, 16, 256, stream_producers<1, 256>()>(W, x, offsets, p.experts, R, y, p.n, p.k, smax, p.num_cus, stream);
         else if (p.k % 128 == 0)
-            err = run_stream_grouped<1, 8, 128>(W, x, offsets, p.experts, R, y, p.n, p.k, smax, p.num_cus, stream);
+            err = run_stream_grouped<1, 16, 128, stream_producers<1, 128>()>(W, x, offsets, p.experts, R, y, p.n, p.k, smax, p.num_cus, stream);
         else
-            err = run_stream_grouped<1, 8, 64>(W, x, offsets, p.experts, R, y, p.n, p.k, smax, p.num_cus, stream);
+            err = run_stream_grouped<1, 16, 64, stream_producers<1, 64>()>(W, x, offsets, p.experts, R, y, p.n, p.k, smax, p.num_cus, stream);
         if (err != hipSuccess)
             return err;
     }
