@@ -109,8 +109,8 @@ bi_status_t bi_gemm_create(int N, int K, const void *W, bi_gemm_t *out);
  * constants (Detent, §6 "Search": a repin regenerates the selector without
  * solving again), and for tests that force a kernel path.  Only pin->splits
  * and pin->stream_max_m are read; the pin must be legal for (N, K)
- * (splits == 1, K % (64 * splits) == 0, 0 <= stream_max_m <= 4096), else
- * BI_ERR_INVALID_ARGUMENT.  Otherwise as bi_gemm_create.
+ * (1 <= splits <= 16, K % (64 * splits) == 0, 0 <= stream_max_m <= 4096),
+ * else BI_ERR_INVALID_ARGUMENT.  Otherwise as bi_gemm_create.
  */
 bi_status_t bi_gemm_create_pinned(int N, int K, const void *W, const bi_pin_info *pin,
                                   bi_gemm_t *out);
@@ -124,7 +124,9 @@ bi_status_t bi_gemm_create_pinned(int N, int K, const void *W, const bi_pin_info
  *           default stream.
  * Asynchronous: no allocation, no synchronisation, no compilation, so the
  * call may be captured into a HIP graph.  x and y are borrowed for the
- * duration of the enqueued work; y must not overlap x or W.
+ * duration of the enqueued work; y must not overlap x or W.  A tree with
+ * S > 1 splits enqueues S kernels on `stream`: the first writes each split-0
+ * partial into y, each later one adds its split's partial to y in order.
  */
 bi_status_t bi_gemm_run(bi_gemm_t h, const void *x, int M, float *y, void *stream);
 

@@ -58,13 +58,12 @@ int g_strict = -1;  // -1: read BI_GEMM_STRICT on first use
 constexpr int kDefaultStreamMaxM = 16;
 
 // A pin is legal for (N, K) when its splits divide K into equal parts that
-// are whole 64-wide stages, and the streaming threshold is sane.  Only the
-// S = 1 tree has kernels.
+// are whole 64-wide stages, and the streaming threshold is sane.
 bool pin_legal(int N, int K, int splits, int stream_max_m, std::string* why)
 {
     (void)N;
-    if (splits != 1) {
-        *why = "only the single-split tree (S = 1) is built";
+    if (splits < 1 || splits > bigemm::kMaxSplits) {
+        *why = "splits must be within 1..16";
         return false;
     }
     if (K % (splits * bigemm::kKGranule) != 0) {

@@ -20,12 +20,15 @@ constexpr int kKGranule = 64;
 // of them in LDS).
 constexpr int kMaxExperts = 1024;
 
+// Most K splits a tree may have.
+constexpr int kMaxSplits = 16;
+
 // What `run` needs from a handle.  The tree (splits) is frozen at create;
 // the tiling fields only choose among kernels that realise that tree.
 struct Plan {
     int n, k;              // layer shape
     int experts;           // 0 dense, E grouped
-    int splits;            // S (only 1 is built)
+    int splits;            // S: contiguous equal K splits, folded in order
     int stream_max_m;      // rows per expert/call at or below which the
                            // weight-streaming kernel runs
     int num_cus;           // compute units of the bound device

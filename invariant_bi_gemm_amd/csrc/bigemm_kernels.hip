@@ -8,7 +8,8 @@
 //   * step t covers k = 32t .. 32t+31; lane group g = lane/16 supplies
 //     k = 32t + 8g .. 32t + 8g + 7 of its row (8 consecutive bf16);
 //   * steps run in ascending t from a +0 accumulator, one chain per split
-//     (only S = 1 is built).
+//     of S contiguous equal K ranges; the split results are added in order,
+//     ((p0 + p1) + p2) + ..., in fp32 round-to-nearest-even.
 // The result of an MFMA element depends only on its own A row, B column and
 // accumulator (checked on the device by the library's invariance tests), so
 // where a row sits in a tile, which tile or kernel handles it and what the
@@ -82,6 +83,25 @@ __device__ __forceinline__ void barrier_after_lds_reads()
 __device__ __forceinline__ void store4(float* p, const f32x4& v)
 {
     *reinterpret_cast<f32x4*>(p) = v;
+}
+
+// One split of the reduction: values k0 .. k0+klen-1 of every row.  Split 0
+// stores its chain's result; split s > 0 adds its chain's result to what
+// splits 0..s-1 left in y, in fp32 round-to-nearest-even, so that y ends as
+// ((p0 + p1) + p2) + ...  The splits run as consecutive launches on one
+// stream, which orders them.
+struct Split {
+    int k0, klen, fold;
+};
+
+__device__ __forceinline__ void emit4(float* p, const f32x4& v, int fold)
+{
+    if (fold) {
+        const f32x4 prev = *reinterpret_cast<const f32x4*>(p);
+        store4(p, prev + v);
+    } else {
+        store4(p, v);
+    }
 }
 
 // XOR swizzle of 16-byte chunk c of row r in an LDS tile whose rows hold kCh
@@ -183,7 +203,7 @@ template <int BM, int BN, int WM, int WN, int BK, int NS>
 __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ Wb,
                                             float* __restrict__ y, int m0, int row_hi, int n0,
-                                            int N, int K)
+                                            int N, int K, Split sp)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     constexpr int kCh = C::kCh;
@@ -218,7 +238,7 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
 #pragma unroll
         for (int j = 0; j < C::kInstr; ++j) {
             const int u0 = (wave * C::kInstr + j) * 64;
-            dma16(u0 < BN * kCh ? rW : rX, voff[j], (uint32_t)s * (BK * 2),
+            dma16(u0 < BN * kCh ? rW : rX, voff[j], (uint32_t)(sp.k0 + s * BK) * 2,
                   lds + buf * C::kStageUnits + u0);
         }
     };
@@ -230,43 +250,78 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
         for (int j = 0; j < C::FM; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / BK;
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (s < nk)
-            issue(s, s);
-    for (int s = 0; s < nk; ++s) {
-        // this wave's loads of stage s have landed ...
-        if (s + NS - 2 < nk)
-            wait_vmcnt<C::kInstr * (NS - 2)>();
-        else
-            wait_vmcnt<0>();
-        // ... and every wave's; every wave is done reading stage s-1
-        barrier_after_lds_reads();
-        if (s + NS - 1 < nk)
-            issue(s + NS - 1, (s + NS - 1) % NS);  // into the buffer of stage s-1
+    // Fragments of one stage, double buffered in registers: the reads of
+    // stage s+1 are issued between the two halves of stage s's MFMAs.
+    using FragA = uint4[C::kSteps][C::FN];
+    using FragB = uint4[C::kSteps][C::FM];
+    FragA fa0, fa1;
+    FragB fb0, fb1;
+    auto read_frags = [&](int s, FragA& fa, FragB& fb) {
         const uint4* sW = lds + (s % NS) * C::kStageUnits;
         const uint4* sX = sW + BN * kCh;
 #pragma unroll
         for (int ks = 0; ks < C::kSteps; ++ks) {
             const int cl = ks * 4 + (lane >> 4);
-            uint4 a[C::FN], b[C::FM];
 #pragma unroll
             for (int t = 0; t < C::FN; ++t) {
                 const int r = wn * C::TN + t * 16 + (lane & 15);
-                a[t] = sW[r * kCh + swz<kCh>(r, cl)];
+                fa[ks][t] = sW[r * kCh + swz<kCh>(r, cl)];
             }
 #pragma unroll
             for (int t = 0; t < C::FM; ++t) {
                 const int r = wm * C::TM + t * 16 + (lane & 15);
-                b[t] = sX[r * kCh + swz<kCh>(r, cl)];
+                fb[ks][t] = sX[r * kCh + swz<kCh>(r, cl)];
             }
+        }
+    };
+    // MFMAs of W-fragment rows [i0, i1) of one stage; every accumulator
+    // still takes its k-steps in ascending order.
+    auto mfmas = [&](const FragA& fa, const FragB& fb, int i0, int i1) {
+#pragma unroll
+        for (int ks = 0; ks < C::kSteps; ++ks)
 #pragma unroll
             for (int i = 0; i < C::FN; ++i)
 #pragma unroll
                 for (int j = 0; j < C::FM; ++j)
-                    acc[i][j] = mfma_step(a[i], b[j], acc[i][j]);
+                    if (i >= i0 && i < i1)
+                        acc[i][j] = mfma_step(fa[ks][i], fb[ks][j], acc[i][j]);
+    };
+    constexpr int kHalf = C::FN / 2 > 0 ? C::FN / 2 : 1;
+
+    const int nk = sp.klen / BK;
+    // Stage s lives in buffer s % NS.  All NS buffers are filled up front;
+    // stage s + NS is issued once every wave has read stage s.
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        if (s < nk)
+            issue(s, s);
+    if (nk - 1 >= NS - 1)
+        wait_vmcnt<C::kInstr * (NS - 1)>();
+    else
+        wait_vmcnt<0>();
+    barrier_after_lds_reads();
+    read_frags(0, fa0, fb0);
+
+    auto stage = [&](int s, const FragA& fa, const FragB& fb, FragA& na, FragB& nb) {
+        mfmas(fa, fb, 0, kHalf);
+        if (s + 1 < nk) {
+            // this wave's loads of stage s+1 have landed ...
+            if (nk - 2 - s >= NS - 2)
+                wait_vmcnt<C::kInstr * (NS - 2)>();
+            else
+                wait_vmcnt<0>();
+            // ... and every wave's; every wave has read stage s
+            barrier_after_lds_reads();
+            if (s + NS < nk)
+                issue(s + NS, s % NS);
+            read_frags(s + 1, na, nb);
         }
+        mfmas(fa, fb, kHalf, C::FN);
+    };
+    for (int s = 0; s < nk; s += 2) {
+        stage(s, fa0, fb0, fa1, fb1);
+        if (s + 1 < nk)
+            stage(s + 1, fa1, fb1, fa0, fb0);
     }
 
 #pragma unroll
@@ -278,7 +333,7 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
         for (int i = 0; i < C::FN; ++i) {
             const int n = n0 + wn * C::TN + i * 16 + 4 * (lane >> 4);
             if (n < N)
-                store4(y + (size_t)m * N + n, acc[i][j]);
+                emit4(y + (size_t)m * N + n, acc[i][j], sp.fold);
         }
     }
 }
@@ -305,13 +360,14 @@ __device__ __forceinline__ void tile_of_block(int b, int nblocks, int tiles_m, i
 template <int BM, int BN, int WM, int WN, int BK, int NS>
 __global__ void __launch_bounds__(WM * WN * 64)
     bigemm_tiled(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
-                 float* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n, int group_m)
+                 float* __restrict__ y, int M, int N, int K, Split sp, int tiles_m, int tiles_n,
+                 int group_m)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     __shared__ uint4 lds[NS * C::kStageUnits];
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
-    tiled_block<BM, BN, WM, WN, BK, NS>(lds, x, W, y, tm * BM, M, tn * BN, N, K);
+    tiled_block<BM, BN, WM, WN, BK, NS>(lds, x, W, y, tm * BM, M, tn * BN, N, K, sp);
 }
 
 // Grouped: block (slot, tn) where slot enumerates the m-blocks of experts
@@ -320,7 +376,7 @@ template <int BM, int BN, int WM, int WN, int BK, int NS>
 __global__ void __launch_bounds__(WM * WN * 64)
     bigemm_tiled_grouped(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                          float* __restrict__ y, const int32_t* __restrict__ off, int E, int R,
-                         int N, int K, int tiles_n, int cmin)
+                         int N, int K, Split sp, int tiles_n, int cmin)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     __shared__ uint4 lds[NS * C::kStageUnits];
@@ -333,7 +389,7 @@ __global__ void __launch_bounds__(WM * WN * 64)
     if (e < 0)
         return;
     tiled_block<BM, BN, WM, WN, BK, NS>(lds, x, W + (size_t)e * N * K, y, lo + lb * BM, hi,
-                                        tn * BN, N, K);
+                                        tn * BN, N, K, sp);
 }
 
 // ---------------------------------------------------------------------------
@@ -400,7 +456,7 @@ struct StreamItem {
 template <int MB, int XR, int BKS, int NP>
 __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ W, float* __restrict__ y,
-                                            int N, int K, int tiles_n, int nitems,
+                                            int N, int K, Split sp, int tiles_n, int nitems,
                                             // dense: M rows; grouped: clamped offsets and
                                             // the expert list, both in LDS
                                             int M, const int* sh_off, const int* elist)
@@ -412,7 +468,7 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = gridDim.x;
     const int mine = nitems > (int)blockIdx.x ? (nitems - 1 - (int)blockIdx.x) / G + 1 : 0;
-    const int nst = K / BKS;
+    const int nst = sp.klen / BKS;
     const int total = mine * nst;
 
     auto item_at = [&](int it) {
@@ -463,7 +519,7 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
 #pragma unroll
                 for (int j = 0; j < kI; ++j) {
                     const int u0 = (first + j) * 64;
-                    dma16(u0 < 16 * kCh ? rW : rX, voff[j], (uint32_t)k_stage * (BKS * 2), dst + u0);
+                    dma16(u0 < 16 * kCh ? rW : rX, voff[j], (uint32_t)(sp.k0 + k_stage * BKS) * 2, dst + u0);
                 }
                 ++k_stage;
             };
@@ -516,7 +572,7 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
                 const StreamItem s = item_at(q / nst);
                 const int m = s.m0 + 16 * ci + rw;
                 if (m < s.row_hi)
-                    store4(y + (size_t)m * N + s.n0 + 4 * (lane >> 4), acc);
+                    emit4(y + (size_t)m * N + s.n0 + 4 * (lane >> 4), acc, sp.fold);
                 acc = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         };
@@ -535,13 +591,13 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
 template <int MB, int XR, int BKS, int NP>
 __global__ void __launch_bounds__((MB + NP) * 64)
     bigemm_stream(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
-                  float* __restrict__ y, int M, int N, int K)
+                  float* __restrict__ y, int M, int N, int K, Split sp)
 {
     using C = StreamCfg<MB, XR, BKS, NP>;
     __shared__ uint4 ring[C::NR * C::kStageUnits];
     const int tiles_n = N / 16;
     const int mblocks = (M + 16 * MB - 1) / (16 * MB);
-    stream_body<MB, XR, BKS, NP>(ring, x, W, y, N, K, tiles_n, mblocks * tiles_n, M, nullptr, nullptr);
+    stream_body<MB, XR, BKS, NP>(ring, x, W, y, N, K, sp, tiles_n, mblocks * tiles_n, M, nullptr, nullptr);
 }
 
 // Grouped: one m-block per expert whose row count c satisfies 0 < c <= cmax
@@ -550,7 +606,7 @@ template <int MB, int XR, int BKS, int NP>
 __global__ void __launch_bounds__((MB + NP) * 64)
     bigemm_stream_grouped(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                           float* __restrict__ y, const int32_t* __restrict__ off, int E, int R,
-                          int N, int K, int cmax)
+                          int N, int K, Split sp, int cmax)
 {
     using C = StreamCfg<MB, XR, BKS, NP>;
     __shared__ uint4 ring[C::NR * C::kStageUnits];
@@ -582,14 +638,14 @@ __global__ void __launch_bounds__((MB + NP) * 64)
     __syncthreads();
     const int tiles_n = N / 16;
     const int count = elist[kMaxExperts];
-    stream_body<MB, XR, BKS, NP>(ring, x, W, y, N, K, tiles_n, count * tiles_n, 0, sh_off, elist);
+    stream_body<MB, XR, BKS, NP>(ring, x, W, y, N, K, sp, tiles_n, count * tiles_n, 0, sh_off, elist);
 }
 
 // ---------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int BK, int NS>
-hipError_t run_tiled(const void* W, const void* x, int M, float* y, int N, int K,
+hipError_t run_tiled(const void* W, const void* x, int M, float* y, int N, int K, Split sp,
                      hipStream_t stream)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
@@ -598,49 +654,49 @@ hipError_t run_tiled(const void* W, const void* x, int M, float* y, int N, int K
     const int nblocks = tiles_m * tiles_n;
     hipLaunchKernelGGL((bigemm_tiled<BM, BN, WM, WN, BK, NS>), dim3(nblocks), dim3(C::kThreads),
                        0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
-                       y, M, N, K, tiles_m, tiles_n, 4);
+                       y, M, N, K, sp, tiles_m, tiles_n, 4);
     return hipGetLastError();
 }
 
 template <int MB, int XR, int BKS, int NP>
-hipError_t run_stream(const void* W, const void* x, int M, float* y, int N, int K, int num_cus,
-                      hipStream_t stream)
+hipError_t run_stream(const void* W, const void* x, int M, float* y, int N, int K, Split sp,
+                      int num_cus, hipStream_t stream)
 {
     using C = StreamCfg<MB, XR, BKS, NP>;
     const int items = ((M + 16 * MB - 1) / (16 * MB)) * (N / 16);
     const int grid = items < num_cus ? items : num_cus;
     hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP>), dim3(grid), dim3(C::kThreads), 0, stream,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K);
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K, sp);
     return hipGetLastError();
 }
 
 // The stage depth: 256 values of k when K allows it.  x rows per stage: at
 // least what a 64-row load group of that stage width needs.
 template <int MB, int XR>
-hipError_t run_stream_k(const void* W, const void* x, int M, float* y, int N, int K, int num_cus,
-                        hipStream_t stream)
+hipError_t run_stream_k(const void* W, const void* x, int M, float* y, int N, int K, Split sp,
+                        int num_cus, hipStream_t stream)
 {
-    if (K % 256 == 0)
-        return run_stream<MB, XR, 256, stream_producers<MB, 256>()>(W, x, M, y, N, K, num_cus, stream);
-    if (K % 128 == 0)
-        return run_stream<MB, (XR < 4 ? 4 : XR), 128, stream_producers<MB, 128>()>(W, x, M, y, N, K, num_cus, stream);
-    return run_stream<MB, (XR < 8 ? 8 : XR), 64, stream_producers<MB, 64>()>(W, x, M, y, N, K, num_cus, stream);
+    if (sp.klen % 256 == 0)
+        return run_stream<MB, XR, 256, stream_producers<MB, 256>()>(W, x, M, y, N, K, sp, num_cus, stream);
+    if (sp.klen % 128 == 0)
+        return run_stream<MB, (XR < 4 ? 4 : XR), 128, stream_producers<MB, 128>()>(W, x, M, y, N, K, sp, num_cus, stream);
+    return run_stream<MB, (XR < 8 ? 8 : XR), 64, stream_producers<MB, 64>()>(W, x, M, y, N, K, sp, num_cus, stream);
 }
 
 template <int MB, int XR, int BKS, int NP>
 hipError_t run_stream_grouped(const void* W, const void* x, const int32_t* off, int E, int R,
-                              float* y, int N, int K, int cmax, int num_cus, hipStream_t stream)
+                              float* y, int N, int K, Split sp, int cmax, int num_cus, hipStream_t stream)
 {
     using C = StreamCfg<MB, XR, BKS, NP>;
     hipLaunchKernelGGL((bigemm_stream_grouped<MB, XR, BKS, NP>), dim3(num_cus), dim3(C::kThreads), 0,
                        stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y,
-                       off, E, R, N, K, cmax);
+                       off, E, R, N, K, sp, cmax);
     return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int NS>
 hipError_t run_tiled_grouped(const void* W, const void* x, const int32_t* off, int E, int R,
-                             float* y, int N, int K, int cmin, hipStream_t stream)
+                             float* y, int N, int K, Split sp, int cmin, hipStream_t stream)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     const int tiles_n = (N + BN - 1) / BN;
@@ -653,7 +709,7 @@ hipError_t run_tiled_grouped(const void* W, const void* x, const int32_t* off, i
         return hipSuccess;
     hipLaunchKernelGGL((bigemm_tiled_grouped<BM, BN, WM, WN, BK, NS>), dim3((unsigned)nblocks),
                        dim3(C::kThreads), 0, stream, static_cast<const uint16_t*>(x),
-                       static_cast<const uint16_t*>(W), y, off, E, R, N, K, tiles_n, cmin);
+                       static_cast<const uint16_t*>(W), y, off, E, R, N, K, sp, tiles_n, cmin);
     return hipGetLastError();
 }
 
@@ -704,32 +760,49 @@ const char* dense_kernel_name(DenseKernel k)
     return "?";
 }
 
-hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, float* y,
-                        hipStream_t stream)
+namespace {
+
+hipError_t launch_dense_split(const Plan& p, DenseKernel kind, const void* W, const void* x, int M,
+                              float* y, Split sp, hipStream_t stream)
 {
-    switch (choose_dense(p, M)) {
+    switch (kind) {
     case DenseKernel::kStream16:
         if (M <= 2)
-            return run_stream_k<1, 2>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+            return run_stream_k<1, 2>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
         if (M <= 4)
-            return run_stream_k<1, 4>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+            return run_stream_k<1, 4>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
         if (M <= 8)
-            return run_stream_k<1, 8>(W, x, M, y, p.n, p.k, p.num_cus, stream);
-        return run_stream_k<1, 16>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+            return run_stream_k<1, 8>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
+        return run_stream_k<1, 16>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
     case DenseKernel::kStream32:
-        return run_stream_k<2, 32>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+        return run_stream_k<2, 32>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
     case DenseKernel::kStream64:
-        return run_stream_k<4, 64>(W, x, M, y, p.n, p.k, p.num_cus, stream);
+        return run_stream_k<4, 64>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
     case DenseKernel::kTiled256:
-        return run_tiled<256, 256, 2, 4, 32, 4>(W, x, M, y, p.n, p.k, stream);
+        return run_tiled<256, 256, 2, 4, 32, 4>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled128:
-        return run_tiled<128, 128, 2, 2, 64, 2>(W, x, M, y, p.n, p.k, stream);
+        return run_tiled<128, 128, 2, 2, 64, 2>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled128x64:
-        return run_tiled<128, 64, 2, 2, 64, 3>(W, x, M, y, p.n, p.k, stream);
+        return run_tiled<128, 64, 2, 2, 64, 3>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled64:
         break;
     }
-    return run_tiled<64, 64, 2, 2, 64, 4>(W, x, M, y, p.n, p.k, stream);
+    return run_tiled<64, 64, 2, 2, 64, 4>(W, x, M, y, p.n, p.k, sp, stream);
+}
+
+}  // namespace
+
+hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, float* y,
+                        hipStream_t stream)
+{
+    const DenseKernel kind = choose_dense(p, M);
+    const int klen = p.k / p.splits;
+    for (int s = 0; s < p.splits; ++s) {
+        const hipError_t e = launch_dense_split(p, kind, W, x, M, y, Split{s * klen, klen, s > 0}, stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int32_t* offsets,
@@ -739,18 +812,25 @@ hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int
     // tiled kernel; both realise the same tree, so the split point only
     // moves work, never bits.
     const int smax = p.stream_max_m < 16 ? p.stream_max_m : 16;
-    hipError_t err = hipSuccess;
-    if (smax > 0) {
-        if (p.k % 256 == 0)
-            err = run_stream_grouped<1, 16, 256, stream_producers<1, 256>()>(W, x, offsets, p.experts, R, y, p.n, p.k, smax, p.num_cus, stream);
-        else if (p.k % 128 == 0)
-            err = run_stream_grouped<1, 16, 128, stream_producers<1, 128>()>(W, x, offsets, p.experts, R, y, p.n, p.k, smax, p.num_cus, stream);
-        else
-            err = run_stream_grouped<1, 16, 64, stream_producers<1, 64>()>(W, x, offsets, p.experts, R, y, p.n, p.k, smax, p.num_cus, stream);
+    const int klen = p.k / p.splits;
+    for (int s = 0; s < p.splits; ++s) {
+        const Split sp{s * klen, klen, s > 0};
+        hipError_t err = hipSuccess;
+        if (smax > 0) {
+            if (klen % 256 == 0)
+                err = run_stream_grouped<1, 16, 256, stream_producers<1, 256>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, stream);
+            else if (klen % 128 == 0)
+                err = run_stream_grouped<1, 16, 128, stream_producers<1, 128>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, stream);
+            else
+                err = run_stream_grouped<1, 16, 64, stream_producers<1, 64>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, stream);
+            if (err != hipSuccess)
+                return err;
+        }
+        err = run_tiled_grouped<128, 128, 2, 2, 64, 2>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, stream);
         if (err != hipSuccess)
             return err;
     }
-    return run_tiled_grouped<128, 128, 2, 2, 64, 2>(W, x, offsets, p.experts, R, y, p.n, p.k, smax, stream);
+    return hipSuccess;
 }
 
 }  // namespace bigemm

@@ -74,7 +74,7 @@ def test_create_null_out(lib):
 
 def test_create_pinned_rejects_illegal_pins(lib):
     h = ctypes.c_void_p()
-    for splits, smax in ((2, 16), (0, 16), (1, -1), (1, 100000)):
+    for splits, smax in ((3, 16), (0, 16), (17, 16), (16, 16), (1, -1), (1, 100000)):
         p = BiPinInfo()
         p.splits, p.stream_max_m = splits, smax
         assert lib.bi_gemm_create_pinned(256, 512, ctypes.c_void_p(4096), ctypes.byref(p), ctypes.byref(h)) == INV
@@ -136,7 +136,7 @@ def test_pin_table_entries_legal():
         rows.append((arch, n, k))
         assert arch == "gfx950"
         assert n % 16 == 0 and k % 64 == 0
-        assert s == 1 and k % (64 * s) == 0  # only the single-split tree is built
+        assert 1 <= s <= 16 and k % (64 * s) == 0
         assert 0 <= smax <= 4096
     assert version and version > 0
     assert len(rows) == len(set(rows))
@@ -147,7 +147,8 @@ def test_pin_table_entries_legal():
 
 @pytest.mark.parametrize("body", [
     "gfx950 256 512 1 16\n",                                # no version
-    "version 1\ngfx950 256 512 2 16\n",                     # S = 2 has no kernels
+    "version 1\ngfx950 256 512 3 16\n",                     # 512 is not 3 equal 64-multiples
+    "version 1\ngfx950 256 512 32 16\n",                    # more than 16 splits
     "version 1\ngfx950 256 500 1 16\n",                     # K not a multiple of 64
     "version 1\ngfx950 256 512 1 16\ngfx950 256 512 1 8\n",  # duplicate shape
     "version 1\ngfx950 256 512 1\n",                        # missing field
