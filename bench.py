@@ -121,6 +121,75 @@ def cpu_baseline(w_bits, x_bits, n, k, target_s=12.0):
             "sample": "fp64 oracle on %d rows (all %d columns) of the same layer, %.1f s" % (rows, n, dt)}
 
 
+def _time_calls(fn, reps):
+    import torch
+
+    for _ in range(2):
+        fn(0)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def invariance_cost(bg, ws, xd, ms, n, k, reps=10):
+    """Cost of invariance: the pinned call at each M against the fastest
+    choice a batch-dependent selector could make at that M among the same
+    kernels (any split count, any streaming threshold), and hipBLASLt
+    (torch.matmul, bf16 output) as context, with whether its rows keep their
+    bits across M."""
+    import numpy as np
+    import torch
+
+    import invariant_bi_gemm_amd.tuner as tuner
+
+    copies = len(ws)
+    splits = [s for s in (1, 2, 4) if s in tuner.legal_splits(k)]
+    cands = [(s_, sm) for s_ in splits for sm in (0, 16, 64)]
+    ys = {m: torch.empty((m, n), dtype=torch.float32, device="cuda:0") for m in ms}
+    # the pinned handles, timed the same way as the alternatives
+    pinned_hs = [bg.Gemm(w) for w in ws]
+    pinned = {m: _time_calls(lambda i: pinned_hs[i % copies](xd[:m], out=ys[m]), reps) for m in ms}
+    best = {m: (pinned[m], tuple(pinned_hs[0].pin[f] for f in ("splits", "stream_max_m"))) for m in ms}
+    for s_, sm in cands:
+        hs = [bg.Gemm(w, pin={"splits": s_, "stream_max_m": sm}) for w in ws]
+        for m in ms:
+            t = _time_calls(lambda i: hs[i % copies](xd[:m], out=ys[m]), reps)
+            if t < best[m][0]:
+                best[m] = (t, (s_, sm))
+        for h in hs:
+            h.close()
+    pinned_ms = pinned
+    rows = []
+    tot_pin = tot_best = tot_blas = 0.0
+    wts = [w.t() for w in ws]
+    probe = xd[:1]
+    ref_row = torch.matmul(probe, wts[0]).view(torch.int16)
+    for m in ms:
+        tb = _time_calls(lambda i: torch.matmul(xd[:m], wts[i % copies]), reps)
+        same = bool(torch.equal(torch.matmul(xd[:m], wts[0])[:1].view(torch.int16), ref_row))
+        tot_pin += pinned_ms[m]
+        tot_best += best[m][0]
+        tot_blas += tb
+        rows.append({"M": m, "pinned_us": round(pinned_ms[m] * 1e3, 2),
+                     "best_per_M_us": round(best[m][0] * 1e3, 2),
+                     "best_choice": list(best[m][1]) if best[m][1] else None,
+                     "hipblaslt_bf16out_us": round(tb * 1e3, 2),
+                     "hipblaslt_row0_same_bits_as_M1": same})
+    return {"what": "pinned tree vs the fastest per-M choice of split count and kernel "
+                    "(a batch-dependent selector) over the same kernels, both timed back to back "
+                    "with rotated weights; hipBLASLt (torch.matmul, bf16 output) as context",
+            "ratio_pinned_over_best_per_M": round(tot_pin / tot_best, 4),
+            "pinned_sweep_ms": round(tot_pin, 4),
+            "hipblaslt_sweep_ms": round(tot_blas, 4),
+            "per_m": rows}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +203,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the cost-of-invariance and hipBLASLt context measurements")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -237,6 +308,10 @@ def main(argv=None):
                       "tflops": round(flops[m] / t / 1e12, 1),
                       "hbm_gbs": round(hbm_bytes[m] / t / 1e9, 0)})
 
+    compare = None
+    if not args.no_compare:
+        compare = invariance_cost(bg, ws, xd, ms, n, k)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w_bits, x_bits, n, k)
@@ -259,6 +334,7 @@ def main(argv=None):
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_m": per_m,
+        "invariance_cost": compare,
         "peak_tflops_in_sweep": max(p["tflops"] for p in per_m),
         "context": "pages' numbers (H100, other hardware): vendor GEMM 527 TFLOPS vs Triton "
                    "batch-invariant 194 TFLOPS peak on this layer",
