@@ -713,16 +713,19 @@ hipError_t run_tiled_grouped(const void* W, const void* x, const int32_t* off, i
     return hipGetLastError();
 }
 
-// The tiled configurations, largest first: {BM, BN, blocks per CU}.
+// The tiled block shapes, largest first.  A shape comes in two depths: a
+// shallow pipeline that leaves LDS for two blocks per CU, and a deep one
+// (more stages in flight, more waves) for grids with at most one block per
+// CU, where nothing else on the CU hides the load latency.
 struct TileShape {
-    DenseKernel kind;
-    int bm, bn, per_cu;
+    DenseKernel kind, deep;
+    int bm, bn;
 };
 constexpr TileShape kTileShapes[] = {
-    {DenseKernel::kTiled256, 256, 256, 1},
-    {DenseKernel::kTiled128, 128, 128, 2},
-    {DenseKernel::kTiled128x64, 128, 64, 2},
-    {DenseKernel::kTiled64, 64, 64, 2},
+    {DenseKernel::kTiled256, DenseKernel::kTiled256, 256, 256},
+    {DenseKernel::kTiled128, DenseKernel::kTiled128Deep, 128, 128},
+    {DenseKernel::kTiled128x64, DenseKernel::kTiled128x64Deep, 128, 64},
+    {DenseKernel::kTiled64, DenseKernel::kTiled64, 64, 64},
 };
 
 }  // namespace
@@ -741,7 +744,7 @@ DenseKernel choose_dense(const Plan& p, int M)
     for (const TileShape& t : kTileShapes) {
         const long long blocks = (long long)((M + t.bm - 1) / t.bm) * ((p.n + t.bn - 1) / t.bn);
         if (blocks >= p.num_cus)
-            return t.kind;
+            return blocks <= p.num_cus ? t.deep : t.kind;
     }
     return DenseKernel::kTiled64;
 }
@@ -754,7 +757,9 @@ const char* dense_kernel_name(DenseKernel k)
     case DenseKernel::kStream64: return "bigemm_stream<mb=4>";
     case DenseKernel::kTiled64: return "bigemm_tiled<64x64>";
     case DenseKernel::kTiled128x64: return "bigemm_tiled<128x64>";
+    case DenseKernel::kTiled128x64Deep: return "bigemm_tiled<128x64,deep>";
     case DenseKernel::kTiled128: return "bigemm_tiled<128x128>";
+    case DenseKernel::kTiled128Deep: return "bigemm_tiled<128x128,deep>";
     case DenseKernel::kTiled256: return "bigemm_tiled<256x256>";
     }
     return "?";
@@ -784,6 +789,10 @@ hipError_t launch_dense_split(const Plan& p, DenseKernel kind, const void* W, co
         return run_tiled<128, 128, 2, 2, 64, 2>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled128x64:
         return run_tiled<128, 64, 2, 2, 64, 3>(W, x, M, y, p.n, p.k, sp, stream);
+    case DenseKernel::kTiled128x64Deep:
+        return run_tiled<128, 64, 2, 2, 64, 6>(W, x, M, y, p.n, p.k, sp, stream);
+    case DenseKernel::kTiled128Deep:
+        return run_tiled<128, 128, 2, 4, 64, 4>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled64:
         break;
     }

@@ -175,20 +175,22 @@ def test_offset_view_of_x(gpu):
 
 def test_every_kernel_configuration(gpu):
     """One layer through every kernel the dispatcher can pick (streaming with
-    1, 2 and 4 m-tiles; tiled 64x64, 128x64, 128x128, 256x256): probe rows of
-    each call equal the rows alone, and the values pass the oracle bound."""
+    1, 2 and 4 m-tiles; tiled 64x64, 128x64 and 128x128 in both depths,
+    256x256): probe rows of each call equal the rows alone, and the values
+    pass the oracle bound."""
     import oracle
     from gpu_util import assert_parity
 
     n, k = 4096, 1024
     w = synth.normal_bf16(150, (n, k), 0.02)
-    ms = [1, 17, 33, 100, 300, 600, 1100, 2100, 4100]
+    ms = [1, 17, 33, 100, 300, 512, 600, 1024, 1100, 2100, 4100]
     x = synth.normal_bf16(151, (max(ms), k))
     g = gpu.Gemm(to_dev(w), pin={"splits": 1, "stream_max_m": 64})
     xd = to_dev(x)
     names = {g.kernel_name(m) for m in ms}
     assert names == {"bigemm_stream<mb=1>", "bigemm_stream<mb=2>", "bigemm_stream<mb=4>",
-                     "bigemm_tiled<64x64>", "bigemm_tiled<128x64>", "bigemm_tiled<128x128>",
+                     "bigemm_tiled<64x64>", "bigemm_tiled<128x64>", "bigemm_tiled<128x64,deep>",
+                     "bigemm_tiled<128x128>", "bigemm_tiled<128x128,deep>",
                      "bigemm_tiled<256x256>"}, names
     probes = {m: synth.probe_rows(152 + m, m, 16) for m in ms}
     allrows = np.unique(np.concatenate(list(probes.values())))
