@@ -244,15 +244,27 @@ def main(argv=None):
         torch.cuda.synchronize()
         del a, b
 
+    # the timed calls go straight to the C ABI with precomputed arguments, so
+    # the host keeps ahead of the GPU even for the decode-size calls
+    import ctypes
+
+    lib = bg.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    xp = ctypes.c_void_p(xd.data_ptr())
+    yps = {m: ctypes.c_void_p(ys[m].data_ptr()) for m in ms}
+    hps = [h._h for h in handles]
+    run = lib.bi_gemm_run
     call_no = [0]
 
     def step(events=None):
         for j, m in enumerate(ms):
-            h = handles[call_no[0] % copies]
+            h = hps[call_no[0] % copies]
             call_no[0] += 1
             if events is not None:
                 events[j][0].record()
-            h(xd[:m], out=ys[m])
+            st = run(h, xp, m, yps[m], stream)
+            if st != 0:
+                bg.check(st)
             if events is not None:
                 events[j][1].record()
 

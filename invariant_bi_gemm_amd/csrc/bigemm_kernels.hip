@@ -192,7 +192,7 @@ struct TiledCfg {
     static_assert(kStageUnits % (64 * kWaves) == 0, "a stage must split evenly over the waves");
     static_assert((BN * kCh) % 64 == 0, "one load instruction must not straddle W and x");
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tiles are whole MFMA tiles");
-    static_assert(kInstr * (NS - 1) < 64, "loads in flight must fit vmcnt");
+    static_assert(kInstr * NS < 64, "loads in flight must fit vmcnt");
     static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
@@ -292,37 +292,53 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
     // Stage s lives in buffer s % NS.  All NS buffers are filled up front;
     // stage s + NS is issued once every wave has read stage s.
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-        if (s < nk)
-            issue(s, s);
-    if (nk - 1 >= NS - 1)
-        wait_vmcnt<C::kInstr * (NS - 1)>();
-    else
-        wait_vmcnt<0>();
+    for (int q = 0; q < NS; ++q)
+        issue(min(q, nk - 1), q);
+    wait_vmcnt<C::kInstr * (NS - 1)>();  // stage 0 has landed
     barrier_after_lds_reads();
     read_frags(0, fa0, fb0);
 
+    // One stage with a successor, branch free so the scheduler can interleave
+    // its loads, fragment reads and MFMAs.  Stage s + NS goes into the buffer
+    // of stage s; past the last stage the last one is loaded again into a
+    // buffer that is never read, which keeps the count of loads in flight the
+    // same in every iteration: after stage s+1, NS-2 stages are outstanding.
     auto stage = [&](int s, const FragA& fa, const FragB& fb, FragA& na, FragB& nb) {
         mfmas(fa, fb, 0, kHalf);
-        if (s + 1 < nk) {
-            // this wave's loads of stage s+1 have landed ...
-            if (nk - 2 - s >= NS - 2)
-                wait_vmcnt<C::kInstr * (NS - 2)>();
-            else
-                wait_vmcnt<0>();
-            // ... and every wave's; every wave has read stage s
-            barrier_after_lds_reads();
-            if (s + NS < nk)
-                issue(s + NS, s % NS);
-            read_frags(s + 1, na, nb);
-        }
+        wait_vmcnt<C::kInstr * (NS - 2)>();  // this wave's loads of stage s+1 have landed
+        barrier_after_lds_reads();           // every wave's have; all have read stage s
+        issue(min(s + NS, nk - 1), s % NS);
+        read_frags(s + 1, na, nb);
         mfmas(fa, fb, kHalf, C::FN);
+#ifdef BIGEMM_INTERLEAVE
+        // spread the loads and fragment reads over the second-half MFMAs
+        constexpr int kReads = (C::FN + C::FM) * C::kSteps;
+        constexpr int kMf = (C::FN - kHalf) * C::FM * C::kSteps;
+#pragma unroll
+        for (int q = 0; q < C::kInstr; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, kMf / (2 * C::kInstr), 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, kReads / C::kInstr, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, kMf / (2 * C::kInstr), 0);
+        }
+#endif
     };
-    for (int s = 0; s < nk; s += 2) {
+    // The last stage: no successor.
+    auto last = [&](const FragA& fa, const FragB& fb) {
+        mfmas(fa, fb, 0, C::FN);
+    };
+    int s = 0;
+    for (; s + 2 < nk; s += 2) {
         stage(s, fa0, fb0, fa1, fb1);
-        if (s + 1 < nk)
-            stage(s + 1, fa1, fb1, fa0, fb0);
+        stage(s + 1, fa1, fb1, fa0, fb0);
     }
+    if (s + 1 < nk) {
+        stage(s, fa0, fb0, fa1, fb1);
+        last(fa1, fb1);
+    } else {
+        last(fa0, fb0);
+    }
+    wait_vmcnt<0>();  // no load into LDS may outlive the block
 
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) {
