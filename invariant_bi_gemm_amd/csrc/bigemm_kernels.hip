@@ -250,41 +250,36 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
         for (int j = 0; j < C::FM; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Fragments of one stage, double buffered in registers: the reads of
-    // stage s+1 are issued between the two halves of stage s's MFMAs.
-    using FragA = uint4[C::kSteps][C::FN];
-    using FragB = uint4[C::kSteps][C::FM];
+    // Fragments of one MFMA k-step, double buffered in registers: the reads
+    // for step g+1 are issued between the two halves of step g's MFMAs.
+    using FragA = uint4[C::FN];
+    using FragB = uint4[C::FM];
     FragA fa0, fa1;
     FragB fb0, fb1;
-    auto read_frags = [&](int s, FragA& fa, FragB& fb) {
+    auto read_frags = [&](int s, int ks, FragA& fa, FragB& fb) {
         const uint4* sW = lds + (s % NS) * C::kStageUnits;
         const uint4* sX = sW + BN * kCh;
+        const int cl = ks * 4 + (lane >> 4);
 #pragma unroll
-        for (int ks = 0; ks < C::kSteps; ++ks) {
-            const int cl = ks * 4 + (lane >> 4);
+        for (int t = 0; t < C::FN; ++t) {
+            const int r = wn * C::TN + t * 16 + (lane & 15);
+            fa[t] = sW[r * kCh + swz<kCh>(r, cl)];
+        }
 #pragma unroll
-            for (int t = 0; t < C::FN; ++t) {
-                const int r = wn * C::TN + t * 16 + (lane & 15);
-                fa[ks][t] = sW[r * kCh + swz<kCh>(r, cl)];
-            }
-#pragma unroll
-            for (int t = 0; t < C::FM; ++t) {
-                const int r = wm * C::TM + t * 16 + (lane & 15);
-                fb[ks][t] = sX[r * kCh + swz<kCh>(r, cl)];
-            }
+        for (int t = 0; t < C::FM; ++t) {
+            const int r = wm * C::TM + t * 16 + (lane & 15);
+            fb[t] = sX[r * kCh + swz<kCh>(r, cl)];
         }
     };
-    // MFMAs of W-fragment rows [i0, i1) of one stage; every accumulator
-    // still takes its k-steps in ascending order.
+    // MFMAs of W-fragment rows [i0, i1) of one k-step; every accumulator
+    // takes its k-steps in ascending order.
     auto mfmas = [&](const FragA& fa, const FragB& fb, int i0, int i1) {
 #pragma unroll
-        for (int ks = 0; ks < C::kSteps; ++ks)
+        for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-            for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-                for (int j = 0; j < C::FM; ++j)
-                    if (i >= i0 && i < i1)
-                        acc[i][j] = mfma_step(fa[ks][i], fb[ks][j], acc[i][j]);
+            for (int j = 0; j < C::FM; ++j)
+                if (i >= i0 && i < i1)
+                    acc[i][j] = mfma_step(fa[i], fb[j], acc[i][j]);
     };
     constexpr int kHalf = C::FN / 2 > 0 ? C::FN / 2 : 1;
 
@@ -296,47 +291,51 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
         issue(min(q, nk - 1), q);
     wait_vmcnt<C::kInstr * (NS - 1)>();  // stage 0 has landed
     barrier_after_lds_reads();
-    read_frags(0, fa0, fb0);
+    read_frags(0, 0, fa0, fb0);
 
-    // One stage with a successor, branch free so the scheduler can interleave
-    // its loads, fragment reads and MFMAs.  Stage s + NS goes into the buffer
-    // of stage s; past the last stage the last one is loaded again into a
-    // buffer that is never read, which keeps the count of loads in flight the
-    // same in every iteration: after stage s+1, NS-2 stages are outstanding.
-    auto stage = [&](int s, const FragA& fa, const FragB& fb, FragA& na, FragB& nb) {
+    // k-step ks of stage s, which has a successor step; branch free so the
+    // scheduler can interleave its loads, fragment reads and MFMAs.  After a
+    // stage's last step the next step is in stage s+1: wait until it has
+    // landed and every wave has read stage s, then refill stage s's buffer
+    // with stage s+NS.  Past the last stage the last one is loaded again
+    // into a buffer that is never read, which keeps the count of loads in
+    // flight the same at every stage: after stage s+1, NS-2 are outstanding.
+    auto step = [&](int s, auto ksc, const FragA& fa, const FragB& fb, FragA& na, FragB& nb) {
+        constexpr int ks = decltype(ksc)::value;
         mfmas(fa, fb, 0, kHalf);
-        wait_vmcnt<C::kInstr * (NS - 2)>();  // this wave's loads of stage s+1 have landed
-        barrier_after_lds_reads();           // every wave's have; all have read stage s
-        issue(min(s + NS, nk - 1), s % NS);
-        read_frags(s + 1, na, nb);
-        mfmas(fa, fb, kHalf, C::FN);
-#ifdef BIGEMM_INTERLEAVE
-        // spread the loads and fragment reads over the second-half MFMAs
-        constexpr int kReads = (C::FN + C::FM) * C::kSteps;
-        constexpr int kMf = (C::FN - kHalf) * C::FM * C::kSteps;
-#pragma unroll
-        for (int q = 0; q < C::kInstr; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, kMf / (2 * C::kInstr), 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, kReads / C::kInstr, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, kMf / (2 * C::kInstr), 0);
+        if constexpr (ks + 1 == C::kSteps) {
+            wait_vmcnt<C::kInstr * (NS - 2)>();  // this wave's loads of stage s+1 have landed
+            barrier_after_lds_reads();           // every wave's have; all have read stage s
+            issue(min(s + NS, nk - 1), s % NS);
+            read_frags(s + 1, 0, na, nb);
+        } else {
+            read_frags(s, ks + 1, na, nb);
         }
-#endif
+        mfmas(fa, fb, kHalf, C::FN);
     };
-    // The last stage: no successor.
-    auto last = [&](const FragA& fa, const FragB& fb) {
-        mfmas(fa, fb, 0, C::FN);
-    };
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
     int s = 0;
-    for (; s + 2 < nk; s += 2) {
-        stage(s, fa0, fb0, fa1, fb1);
-        stage(s + 1, fa1, fb1, fa0, fb0);
-    }
-    if (s + 1 < nk) {
-        stage(s, fa0, fb0, fa1, fb1);
-        last(fa1, fb1);
+    if constexpr (C::kSteps == 2) {
+        // one stage per iteration: step 0 from fa0 into fa1, step 1 back
+        for (; s + 1 < nk; ++s) {
+            step(s, K0{}, fa0, fb0, fa1, fb1);
+            step(s, K1{}, fa1, fb1, fa0, fb0);
+        }
+        step(s, K0{}, fa0, fb0, fa1, fb1);
+        mfmas(fa1, fb1, 0, C::FN);
     } else {
-        last(fa0, fb0);
+        // two stages per iteration, alternating fragment sets
+        for (; s + 2 < nk; s += 2) {
+            step(s, K0{}, fa0, fb0, fa1, fb1);
+            step(s + 1, K0{}, fa1, fb1, fa0, fb0);
+        }
+        if (s + 1 < nk) {
+            step(s, K0{}, fa0, fb0, fa1, fb1);
+            mfmas(fa1, fb1, 0, C::FN);
+        } else {
+            mfmas(fa0, fb0, 0, C::FN);
+        }
     }
     wait_vmcnt<0>();  // no load into LDS may outlive the block
 
@@ -800,7 +799,7 @@ hipError_t launch_dense_split(const Plan& p, DenseKernel kind, const void* W, co
     case DenseKernel::kStream64:
         return run_stream_k<4, 64>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
     case DenseKernel::kTiled256:
-        return run_tiled<256, 256, 2, 4, 32, 4>(W, x, M, y, p.n, p.k, sp, stream);
+        return run_tiled<256, 256, 2, 4, 64, 2>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled128:
         return run_tiled<128, 128, 2, 2, 64, 2>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled128x64:
