@@ -20,7 +20,7 @@
 // Kernel families:
 //   bigemm_tiled   mid and large M: an NS-stage LDS pipeline fed by direct
 //                  buffer->LDS loads, one barrier per stage, output blocks
-//                  from 64x64 to 256x256 chosen by M.  MFMA bound at large M.
+//                  from 64x64 to 256x256 (x rows by W rows) chosen by M.  MFMA bound at large M.
 //   bigemm_stream  small M: a persistent, warp-specialised weight streamer.
 //                  Two producer waves keep a deep LDS ring of W (and x) full
 //                  with direct buffer->LDS loads; consumer waves run the MFMA
@@ -738,6 +738,7 @@ struct TileShape {
 };
 constexpr TileShape kTileShapes[] = {
     {DenseKernel::kTiled256, DenseKernel::kTiled256, 256, 256},
+    {DenseKernel::kTiled128x256, DenseKernel::kTiled128x256, 128, 256},
     {DenseKernel::kTiled128, DenseKernel::kTiled128Deep, 128, 128},
     {DenseKernel::kTiled128x64, DenseKernel::kTiled128x64Deep, 128, 64},
     {DenseKernel::kTiled64, DenseKernel::kTiled64, 64, 64},
@@ -775,6 +776,7 @@ const char* dense_kernel_name(DenseKernel k)
     case DenseKernel::kTiled128x64Deep: return "bigemm_tiled<128x64,deep>";
     case DenseKernel::kTiled128: return "bigemm_tiled<128x128>";
     case DenseKernel::kTiled128Deep: return "bigemm_tiled<128x128,deep>";
+    case DenseKernel::kTiled128x256: return "bigemm_tiled<128x256>";
     case DenseKernel::kTiled256: return "bigemm_tiled<256x256>";
     }
     return "?";
@@ -800,6 +802,8 @@ hipError_t launch_dense_split(const Plan& p, DenseKernel kind, const void* W, co
         return run_stream_k<4, 64>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
     case DenseKernel::kTiled256:
         return run_tiled<256, 256, 2, 4, 64, 2>(W, x, M, y, p.n, p.k, sp, stream);
+    case DenseKernel::kTiled128x256:
+        return run_tiled<128, 256, 2, 4, 64, 3>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled128:
         return run_tiled<128, 128, 2, 2, 64, 2>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled128x64:
