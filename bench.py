@@ -49,6 +49,11 @@ WORKLOADS = {
                                    "M in {1,8,64,512,4096,16384}"),
 }
 
+# Qwen3-30B-A3B-style MoE expert GEMMs: 128 experts, top-8 routing.
+MOE = dict(experts=128, topk=8, up=(1536, 2048), down=(2048, 768), tokens=[1, 16, 256, 4096], std=0.02,
+           desc="MoE expert GEMMs (Qwen3-30B-A3B-style): 128 experts, top-8 of softmax(N(0,1) logits), "
+                "up W bf16 [128,1536,2048] and down W bf16 [128,2048,768], T in {1,16,256,4096} tokens")
+
 
 def kernel_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
@@ -97,7 +102,7 @@ def to_dev(bits):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda:0")
 
 
-def cpu_baseline(w_bits, x_bits, n, k, target_s=12.0):
+def cpu_baseline(w_bits, x_bits, n, k, target_s=15.0):
     """The oracle, as it stands, on the host cores: rows of the same layer.
 
     Times a small probe first, then enough rows for about `target_s` seconds.
@@ -190,12 +195,143 @@ def invariance_cost(bg, ws, xd, ms, n, k, reps=10):
             "per_m": rows}
 
 
+def run_moe(args, bg):
+    """One step = the up and the down expert GEMM at every token count T of
+    the sweep (rows = 8T, grouped by expert).  Weights rotate over copies so
+    the Infinity Cache does not hold the touched experts between calls."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    E, topk = MOE["experts"], MOE["topk"]
+    shapes = {"up": MOE["up"], "down": MOE["down"]}
+    copies = 2
+    handles, wbits = {}, {}
+    for i, (name, (n, k)) in enumerate(shapes.items()):
+        wbits[name] = synth.normal_bf16(42 + i, (E, n, k), MOE["std"])
+        w0 = to_dev(wbits[name])
+        handles[name] = [bg.GroupedGemm(w0)] + [bg.GroupedGemm(w0.clone()) for _ in range(copies - 1)]
+    calls = []  # (T, name, x, offsets, y, flops, bytes)
+    for t in MOE["tokens"]:
+        tok, off, _ = synth.moe_routing(42 + t, t, E, topk)
+        touched = int(np.count_nonzero(np.diff(off)))
+        r = len(tok)
+        for name, (n, k) in shapes.items():
+            x_tok = synth.normal_bf16(43 + t + k, (t, k))
+            x = to_dev(np.ascontiguousarray(x_tok[tok]))
+            y = torch.empty((r, n), dtype=torch.float32, device="cuda:0")
+            calls.append((t, name, x, torch.as_tensor(off, device="cuda:0"), y, 2.0 * r * n * k,
+                          2.0 * touched * n * k + 2.0 * r * k + 4.0 * r * n, touched))
+    # straight to the C ABI with precomputed arguments, as in the dense sweep
+    import ctypes
+
+    lib = bg.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cargs = [(tuple(h._h for h in handles[name]), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(off.data_ptr()),
+              int(x.shape[0]), ctypes.c_void_p(y.data_ptr())) for (_, name, x, off, y, _, _, _) in calls]
+    run = lib.bi_grouped_gemm_run
+    call_no = [0]
+
+    def step(events=None):
+        for j, (hs, xp, offp, r, yp) in enumerate(cargs):
+            h = hs[call_no[0] % copies]
+            call_no[0] += 1
+            if events is not None:
+                events[j][0].record()
+            st = run(h, xp, offp, r, yp, stream)
+            if st != 0:
+                bg.check(st)
+            if events is not None:
+                events[j][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in calls]
+          for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s_ in range(args.steps):
+        step(ev[s_])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    per = [float(np.mean([ev[s_][j][0].elapsed_time(ev[s_][j][1]) for s_ in range(args.steps)]))
+           for j in range(len(calls))]
+    step_flops = sum(c[5] for c in calls)
+    rows = []
+    for (t, name, _, _, _, fl, by, touched), ms in zip(calls, per):
+        rows.append({"T": t, "gemm": name, "rows": 8 * t, "experts_touched": touched, "us": round(ms * 1e3, 2),
+                     "tflops": round(fl / (ms * 1e-3) / 1e12, 1), "hbm_gbs": round(by / (ms * 1e-3) / 1e9, 0)})
+    dom = max(range(len(calls)), key=lambda j: per[j])
+    t, name, _, _, _, fl, by, _ = calls[dom]
+    if t * topk >= 16 * E:   # tens of rows per expert: the tiled MFMA kernel carries the call
+        ach = fl / (per[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        ach = by / (per[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": None,
+                 "kernel": "grouped %s GEMM at T=%d (streaming + tiled grouped kernels)" % (name, t),
+                 "launches_per_step": 1, "avg_launch_us": per[dom] * 1e3})
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = moe_cpu_baseline(wbits, calls)
+    out = {
+        "metric": "batch-invariant bf16 GEMM TFLOPS (M sweep) + % MFMA/HBM roofline, 1 GPU",
+        "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; W ~ N(0,%g), x ~ N(0,1), routing from N(0,1) logits)" % MOE["std"],
+        "config": {"workload": MOE["desc"], "tokens": MOE["tokens"], "weight_copies_rotated": copies,
+                   "kernel_source_sha256_16": kernel_hash()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_call": rows,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def moe_cpu_baseline(wbits, calls, target_s=15.0):
+    """The oracle's grouped GEMM on the host cores, on a bounded sample: the
+    T=256 up-projection rows, as many as fit in about `target_s` seconds."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    t, name, x, off, _, _, _, _ = next(c for c in calls if c[0] == 256 and c[1] == "up")
+    xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    offs = off.cpu().numpy()
+    w = wbits[name]
+    n, k = w.shape[1], w.shape[2]
+    t0 = time.perf_counter()
+    oracle.grouped_f64(xb, w, offs, rows=np.arange(4))
+    probe = max(time.perf_counter() - t0, 1e-3) / 4
+    nrows = int(max(4, min(xb.shape[0], target_s / probe)))
+    t0 = time.perf_counter()
+    oracle.grouped_f64(xb, w, offs, rows=np.arange(nrows))
+    dt = time.perf_counter() - t0
+    return {"value": 2.0 * nrows * n * k / dt / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(),
+            "kind": "oracle", "sample": "fp64 oracle, grouped up-projection (N=%d, K=%d), first %d of the %d "
+            "rows at T=%d, %.1f s" % (n, k, nrows, xb.shape[0], t, dt)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama8b_down", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="llama8b_down", choices=sorted(WORKLOADS) + ["moe"])
     ap.add_argument("--rotate-gib", type=float, default=1.0,
                     help="weight copies to rotate over, in GiB (defeats the Infinity Cache)")
     ap.add_argument("--m", type=str, default=None,
@@ -222,6 +358,8 @@ def main(argv=None):
         print("no GPU visible", file=sys.stderr)
         return 1
     bg.load()
+    if args.workload == "moe":
+        return run_moe(args, bg)
     wl = dict(WORKLOADS[args.workload])
     if args.m:
         wl["ms"] = [int(v) for v in args.m.split(",")]
