@@ -266,7 +266,9 @@ def run_moe(args, bg):
                      "tflops": round(fl / (ms * 1e-3) / 1e12, 1), "hbm_gbs": round(by / (ms * 1e-3) / 1e9, 0)})
     dom = max(range(len(calls)), key=lambda j: per[j])
     t, name, _, _, _, fl, by, _ = calls[dom]
-    if t * topk >= 16 * E:   # tens of rows per expert: the tiled MFMA kernel carries the call
+    # the binding roofline: the larger of the MFMA time and the HBM time of
+    # the call's algorithmic work
+    if fl / (PEAK_BF16_TFLOPS * 1e12) >= by / (PEAK_HBM_GBS * 1e9):
         ach = fl / (per[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     else:

@@ -128,45 +128,57 @@ __device__ __forceinline__ int swz(int r, int c)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int clamp_off(int v, int R) { return v < 0 ? 0 : (v > R ? R : v); }
 
-// Which expert owns m-block `slot`.  Experts whose row count c satisfies
-// cmin < c <= cmax each contribute ceil(c / bm) m-blocks, in ascending expert
-// order.  Every thread of the block calls this; `sh` is E + 3 ints of LDS.
-// Returns the expert (or -1 when slot is past the last m-block), its block
-// index and its row range.
-__device__ int grouped_find(const int32_t* __restrict__ off, int E, int R, int bm, int cmin,
-                            int cmax, int slot, int* lb_out, int* lo_out, int* hi_out, int* sh)
+// Plan of a grouped call, built by every block in its own LDS: s_off[e] =
+// offsets[e] clamped to 0..R, and s_first[e] = the m-blocks of the experts
+// before e that the kernel serves (row count c with cmin < c <= cmax, each
+// taking ceil(c / bm) m-blocks, or one when bm is 0); s_first[E] is their
+// total.  Wave 0 scans 64 experts at a time.
+__device__ void grouped_plan(const int32_t* __restrict__ off, int E, int R, int bm, int cmin,
+                             int cmax, int* s_off, int* s_first)
 {
     for (int e = threadIdx.x; e <= E; e += blockDim.x)
-        sh[e] = clamp_off(off[e], R);
-    if (threadIdx.x == 0) {
-        sh[E + 1] = -1;
-        sh[E + 2] = 0;
+        s_off[e] = clamp_off(off[e], R);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        int carry = 0;
+        for (int base = 0; base < E; base += 64) {
+            const int e = base + lane;
+            const int c = e < E ? max(s_off[e + 1] - s_off[e], 0) : 0;
+            const int mine = (c > cmin && c <= cmax) ? (bm > 0 ? (c - 1) / bm + 1 : 1) : 0;
+            int v = mine;
+            for (int d = 1; d < 64; d <<= 1) {
+                const int u = __shfl_up(v, d, 64);
+                if (lane >= d)
+                    v += u;
+            }
+            if (e < E)
+                s_first[e] = carry + v - mine;
+            carry += __shfl(v, 63, 64);
+        }
+        if (lane == 0)
+            s_first[E] = carry;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        const int c = max(sh[e + 1] - sh[e], 0);
-        const int mine = (c > cmin && c <= cmax) ? (c + bm - 1) / bm : 0;
-        if (mine == 0)
-            continue;
-        int before = 0;
-        for (int j = 0; j < e; ++j) {
-            const int cj = max(sh[j + 1] - sh[j], 0);
-            before += (cj > cmin && cj <= cmax) ? (cj + bm - 1) / bm : 0;
-        }
-        if (slot >= before && slot < before + mine) {
-            sh[E + 1] = e;
-            sh[E + 2] = slot - before;
-        }
+}
+
+// The expert owning m-block `slot` (0 <= slot < s_first[E]): the last e with
+// s_first[e] <= slot, which serves at least one m-block.  Sets its block
+// index and row range.
+__device__ __forceinline__ int grouped_slot(const int* s_off, const int* s_first, int E, int bm,
+                                            int slot, int* m0, int* hi)
+{
+    int lo = 0, up = E;
+    while (up - lo > 1) {
+        const int mid = (lo + up) >> 1;
+        if (s_first[mid] <= slot)
+            lo = mid;
+        else
+            up = mid;
     }
-    __syncthreads();
-    const int e = sh[E + 1];
-    *lb_out = sh[E + 2];
-    if (e >= 0) {
-        *lo_out = sh[e];
-        *hi_out = sh[e] + max(sh[e + 1] - sh[e], 0);
-    }
-    __syncthreads();  // sh is reused by the caller
-    return e;
+    *m0 = s_off[lo] + (slot - s_first[lo]) * bm;
+    *hi = s_off[lo] + max(s_off[lo + 1] - s_off[lo], 0);
+    return lo;
 }
 
 // ---------------------------------------------------------------------------
@@ -385,8 +397,11 @@ __global__ void __launch_bounds__(WM * WN * 64)
     tiled_block<BM, BN, WM, WN, BK, NS>(lds, x, W, y, tm * BM, M, tn * BN, N, K, sp);
 }
 
-// Grouped: block (slot, tn) where slot enumerates the m-blocks of experts
-// with more than cmin rows.
+// Grouped, persistent: the output tiles (slot, tn) -- slot enumerating the
+// m-blocks of the experts with more than cmin rows -- are counted on the
+// device and cut into 8 contiguous ranges, one per XCD (hardware hands block b
+// to XCD b % 8; the grid is a multiple of 8), so each XCD's L2 holds few
+// experts at a time and every XCD gets the same share whatever the routing.
 template <int BM, int BN, int WM, int WN, int BK, int NS>
 __global__ void __launch_bounds__(WM * WN * 64)
     bigemm_tiled_grouped(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
@@ -395,16 +410,20 @@ __global__ void __launch_bounds__(WM * WN * 64)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     __shared__ uint4 lds[NS * C::kStageUnits];
-    static_assert(C::kLdsBytes >= (kMaxExperts + 4) * 4, "offsets must fit the stage buffers");
-    const int slot = blockIdx.x / tiles_n;
-    const int tn = blockIdx.x % tiles_n;
-    int lb, lo = 0, hi = 0;
-    const int e = grouped_find(off, E, R, BM, cmin, 0x7fffffff, slot, &lb, &lo, &hi,
-                               reinterpret_cast<int*>(lds));
-    if (e < 0)
-        return;
-    tiled_block<BM, BN, WM, WN, BK, NS>(lds, x, W + (size_t)e * N * K, y, lo + lb * BM, hi,
-                                        tn * BN, N, K, sp);
+    __shared__ int s_off[kMaxExperts + 1];
+    __shared__ int s_first[kMaxExperts + 1];
+    grouped_plan(off, E, R, BM, cmin, 0x7fffffff, s_off, s_first);
+    const int total = s_first[E] * tiles_n;
+    const int xcd = blockIdx.x % 8;
+    const int per_xcd = gridDim.x / 8;
+    const int t_end = (int)((long long)total * (xcd + 1) / 8);
+    for (int t = (int)((long long)total * xcd / 8) + (int)(blockIdx.x / 8); t < t_end; t += per_xcd) {
+        int m0, hi;
+        const int e = grouped_slot(s_off, s_first, E, BM, t / tiles_n, &m0, &hi);
+        barrier_after_lds_reads();  // every wave is done with the previous tile's stages
+        tiled_block<BM, BN, WM, WN, BK, NS>(lds, x, W + (size_t)e * N * K, y, m0, hi,
+                                            (t % tiles_n) * BN, N, K, sp);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -626,33 +645,18 @@ __global__ void __launch_bounds__((MB + NP) * 64)
     using C = StreamCfg<MB, XR, BKS, NP>;
     __shared__ uint4 ring[C::NR * C::kStageUnits];
     __shared__ int sh_off[kMaxExperts + 1];
-    __shared__ int elist[kMaxExperts + 1];
+    __shared__ int first[kMaxExperts + 1];
+    __shared__ int elist[kMaxExperts];
     // compact, ascending list of the experts this kernel serves
-    for (int e = threadIdx.x; e <= E; e += blockDim.x)
-        sh_off[e] = clamp_off(off[e], R);
-    __syncthreads();
+    grouped_plan(off, E, R, 0, 0, cmax, sh_off, first);
+    const int count = first[E];
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         const int c = sh_off[e + 1] - sh_off[e];
-        if (c > 0 && c <= cmax) {
-            int before = 0;
-            for (int j = 0; j < e; ++j) {
-                const int cj = sh_off[j + 1] - sh_off[j];
-                before += (cj > 0 && cj <= cmax) ? 1 : 0;
-            }
-            elist[before] = e;
-        }
-    }
-    if (threadIdx.x == 0) {
-        int n = 0;
-        for (int j = 0; j < E; ++j) {
-            const int cj = sh_off[j + 1] - sh_off[j];
-            n += (cj > 0 && cj <= cmax) ? 1 : 0;
-        }
-        elist[kMaxExperts] = n;
+        if (c > 0 && c <= cmax)
+            elist[first[e]] = e;
     }
     __syncthreads();
     const int tiles_n = N / 16;
-    const int count = elist[kMaxExperts];
     stream_body<MB, XR, BKS, NP>(ring, x, W, y, N, K, sp, tiles_n, count * tiles_n, 0, sh_off, elist);
 }
 
@@ -711,20 +715,20 @@ hipError_t run_stream_grouped(const void* W, const void* x, const int32_t* off, 
 
 template <int BM, int BN, int WM, int WN, int BK, int NS>
 hipError_t run_tiled_grouped(const void* W, const void* x, const int32_t* off, int E, int R,
-                             float* y, int N, int K, Split sp, int cmin, hipStream_t stream)
+                             float* y, int N, int K, Split sp, int cmin, int num_cus,
+                             hipStream_t stream)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
+    if (R <= cmin)
+        return hipSuccess;  // no expert can have more than cmin rows
     const int tiles_n = (N + BN - 1) / BN;
-    // m-blocks of experts with more than cmin rows: at most R/BM + (number of
-    // such experts), and there are at most min(E, R/(cmin+1)) of those.
-    const long long big = R / (cmin + 1);
-    const long long slots = (R + BM - 1) / BM + (big < E ? big : E);
-    const long long nblocks = slots * tiles_n;
-    if (nblocks <= 0)
-        return hipSuccess;
-    hipLaunchKernelGGL((bigemm_tiled_grouped<BM, BN, WM, WN, BK, NS>), dim3((unsigned)nblocks),
-                       dim3(C::kThreads), 0, stream, static_cast<const uint16_t*>(x),
-                       static_cast<const uint16_t*>(W), y, off, E, R, N, K, sp, tiles_n, cmin);
+    // resident blocks: as many per CU as LDS allows (at most two), rounded
+    // to whole sets of 8 (one per XCD)
+    const int per_cu = 2 * (C::kLdsBytes + 4 * (2 * kMaxExperts + 2)) <= 160 * 1024 ? 2 : 1;
+    const int grid = (num_cus * per_cu + 7) / 8 * 8;
+    hipLaunchKernelGGL((bigemm_tiled_grouped<BM, BN, WM, WN, BK, NS>), dim3(grid), dim3(C::kThreads),
+                       0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y,
+                       off, E, R, N, K, sp, tiles_n, cmin);
     return hipGetLastError();
 }
 
@@ -854,7 +858,7 @@ hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int
             if (err != hipSuccess)
                 return err;
         }
-        err = run_tiled_grouped<128, 128, 2, 2, 64, 2>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, stream);
+        err = run_tiled_grouped<128, 128, 2, 2, 64, 2>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, stream);
         if (err != hipSuccess)
             return err;
     }
