@@ -22,9 +22,9 @@
 //                  buffer->LDS loads, one barrier per stage, output blocks
 //                  from 64x64 to 256x256 (x rows by W rows) chosen by M.  MFMA bound at large M.
 //   bigemm_stream  small M: a persistent, warp-specialised weight streamer.
-//                  Two producer waves keep a deep LDS ring of W (and x) full
-//                  with direct buffer->LDS loads; consumer waves run the MFMA
-//                  chain of one 16-column tile.  HBM bound.
+//                  Up to seven producer waves keep a deep LDS ring of W (and
+//                  x) full with direct buffer->LDS loads; consumer waves run
+//                  the MFMA chain of one 16-column tile.  HBM bound.
 // Both have a grouped (MoE) variant whose per-expert row counts stay on the
 // device.
 
@@ -441,7 +441,7 @@ constexpr int kStreamLdsBudget = 144 * 1024;
 template <int MB, int BKS>
 constexpr int stream_producers()
 {
-    return BKS == 256 ? 8 - MB : (BKS == 128 ? (6 - MB > 2 ? 6 - MB : 2) : 2);
+    return BKS >= 256 ? 8 - MB : (BKS == 128 ? (6 - MB > 2 ? 6 - MB : 2) : 2);
 }
 
 template <int MB, int XR, int BKS, int NP>
@@ -576,32 +576,42 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
         else
             produce(std::integral_constant<int, C::kLo>{}, kExtra * C::kHi + (pw - kExtra) * C::kLo);
     } else {
-        // ---- consumer: the MFMA chain of m-tile `wave`, one stage behind its
-        // LDS reads so that they overlap the chain ----
+        // ---- consumer: the MFMA chain of m-tile `wave`.  Fragments are
+        // double-buffered by half stage: the reads of the next half overlap
+        // the chain of the current one, and the next stage's first half is
+        // read once the barrier says it has landed.
         const int ci = wave;
         const int rw = lane & 15;
         const int rx = 16 + (MB == 1 ? min(rw, XR - 1) : 16 * ci + rw);
-        uint4 a0[C::kSteps], b0[C::kSteps], a1[C::kSteps], b1[C::kSteps];
-        auto read = [&](int q, uint4* a, uint4* b) {
+        constexpr int kH = C::kSteps / 2;  // k-steps per half stage
+        uint4 a0[kH], b0[kH], a1[kH], b1[kH];
+        auto read = [&](int q, int h, uint4* a, uint4* b) {
             const uint4* st = ring + (q % NR) * C::kStageUnits;
 #pragma unroll
-            for (int t = 0; t < C::kSteps; ++t) {
-                const int cl = 4 * t + (lane >> 4);
+            for (int t = 0; t < kH; ++t) {
+                const int cl = 4 * (h * kH + t) + (lane >> 4);
                 a[t] = st[rw * kCh + swz<kCh>(rw, cl)];
                 b[t] = st[rx * kCh + swz<kCh>(rx, cl)];
             }
         };
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        // stage q's fragments are in (a, b); read stage q+1 into (na, nb)
-        // before running q's chain
-        auto stage = [&](int q, const uint4* a, const uint4* b, uint4* na, uint4* nb) {
-            if (q + 1 < total) {
-                barrier_after_lds_reads();
-                read(q + 1, na, nb);
-            }
+        auto chain = [&](f32x4& acc, const uint4* a, const uint4* b) {
 #pragma unroll
-            for (int t = 0; t < C::kSteps; ++t)
+            for (int t = 0; t < kH; ++t)
                 acc = mfma_step(a[t], b[t], acc);
+        };
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (total > 0) {
+            barrier_after_lds_reads();
+            read(0, 0, a0, b0);
+        }
+        for (int q = 0; q < total; ++q) {
+            read(q, 1, a1, b1);
+            chain(acc, a0, b0);
+            if (q + 1 < total) {
+                barrier_after_lds_reads();  // stage q+1 has landed; stage q is read
+                read(q + 1, 0, a0, b0);
+            }
+            chain(acc, a1, b1);
             if ((q + 1) % nst == 0) {
                 const StreamItem s = item_at(q / nst);
                 const int m = s.m0 + 16 * ci + rw;
@@ -609,15 +619,6 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
                     emit4(y + (size_t)m * N + s.n0 + 4 * (lane >> 4), acc, sp.fold);
                 acc = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-        };
-        if (total > 0) {
-            barrier_after_lds_reads();
-            read(0, a0, b0);
-        }
-        for (int q = 0; q < total; q += 2) {
-            stage(q, a0, b0, a1, b1);
-            if (q + 1 < total)
-                stage(q + 1, a1, b1, a0, b0);
         }
     }
 }
@@ -689,12 +690,17 @@ hipError_t run_stream(const void* W, const void* x, int M, float* y, int N, int 
     return hipGetLastError();
 }
 
-// The stage depth: 256 values of k when K allows it.  x rows per stage: at
-// least what a 64-row load group of that stage width needs.
+// The stage depth: 512 values of k for a single m-tile (1 KB of every row per
+// stage), else 256, when K allows it.  x rows per stage: at least what a
+// 64-row load group of that stage width needs.
 template <int MB, int XR>
 hipError_t run_stream_k(const void* W, const void* x, int M, float* y, int N, int K, Split sp,
                         int num_cus, hipStream_t stream)
 {
+    if constexpr (MB == 1) {
+        if (sp.klen % 512 == 0)
+            return run_stream<MB, XR, 512, stream_producers<MB, 512>()>(W, x, M, y, N, K, sp, num_cus, stream);
+    }
     if (sp.klen % 256 == 0)
         return run_stream<MB, XR, 256, stream_producers<MB, 256>()>(W, x, M, y, N, K, sp, num_cus, stream);
     if (sp.klen % 128 == 0)
@@ -849,7 +855,9 @@ hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int
         const Split sp{s * klen, klen, s > 0};
         hipError_t err = hipSuccess;
         if (smax > 0) {
-            if (klen % 256 == 0)
+            if (klen % 512 == 0)
+                err = run_stream_grouped<1, 16, 512, stream_producers<1, 512>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, stream);
+            else if (klen % 256 == 0)
                 err = run_stream_grouped<1, 16, 256, stream_producers<1, 256>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, stream);
             else if (klen % 128 == 0)
                 err = run_stream_grouped<1, 16, 128, stream_producers<1, 128>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, stream);
