@@ -37,7 +37,8 @@ struct Plan {
 // The dense kernels `run` may launch; M picks one, the tree is the same.
 enum class DenseKernel {
     kStream16, kStream32, kStream64,
-    kTiled64, kTiled128x64, kTiled128x64Deep, kTiled128, kTiled128Deep, kTiled128x256, kTiled256
+    kTiled64x32, kTiled64, kTiled128x64, kTiled128x64Deep, kTiled128, kTiled128Deep, kTiled128x256,
+    kTiled256
 };
 DenseKernel choose_dense(const Plan& p, int M);
 const char* dense_kernel_name(DenseKernel k);

@@ -20,7 +20,7 @@
 // Kernel families:
 //   bigemm_tiled   mid and large M: an NS-stage LDS pipeline fed by direct
 //                  buffer->LDS loads, one barrier per stage, output blocks
-//                  from 64x64 to 256x256 (x rows by W rows) chosen by M.  MFMA bound at large M.
+//                  from 64x32 to 256x256 (x rows by W rows) chosen by M.  MFMA bound at large M.
 //   bigemm_stream  small M: a persistent, warp-specialised weight streamer.
 //                  Up to seven producer waves keep a deep LDS ring of W (and
 //                  x) full with direct buffer->LDS loads; consumer waves run
@@ -752,6 +752,7 @@ constexpr TileShape kTileShapes[] = {
     {DenseKernel::kTiled128, DenseKernel::kTiled128Deep, 128, 128},
     {DenseKernel::kTiled128x64, DenseKernel::kTiled128x64Deep, 128, 64},
     {DenseKernel::kTiled64, DenseKernel::kTiled64, 64, 64},
+    {DenseKernel::kTiled64x32, DenseKernel::kTiled64x32, 64, 32},
 };
 
 }  // namespace
@@ -766,13 +767,13 @@ DenseKernel choose_dense(const Plan& p, int M)
         return DenseKernel::kStream64;
     }
     // The largest output block that still gives every CU a block; failing
-    // that, the one with the most blocks.
+    // that, the smallest (the one with the most blocks).
     for (const TileShape& t : kTileShapes) {
         const long long blocks = (long long)((M + t.bm - 1) / t.bm) * ((p.n + t.bn - 1) / t.bn);
         if (blocks >= p.num_cus)
             return blocks <= p.num_cus ? t.deep : t.kind;
     }
-    return DenseKernel::kTiled64;
+    return DenseKernel::kTiled64x32;
 }
 
 const char* dense_kernel_name(DenseKernel k)
@@ -781,6 +782,7 @@ const char* dense_kernel_name(DenseKernel k)
     case DenseKernel::kStream16: return "bigemm_stream<mb=1>";
     case DenseKernel::kStream32: return "bigemm_stream<mb=2>";
     case DenseKernel::kStream64: return "bigemm_stream<mb=4>";
+    case DenseKernel::kTiled64x32: return "bigemm_tiled<64x32>";
     case DenseKernel::kTiled64: return "bigemm_tiled<64x64>";
     case DenseKernel::kTiled128x64: return "bigemm_tiled<128x64>";
     case DenseKernel::kTiled128x64Deep: return "bigemm_tiled<128x64,deep>";
@@ -822,6 +824,8 @@ hipError_t launch_dense_split(const Plan& p, DenseKernel kind, const void* W, co
         return run_tiled<128, 64, 2, 2, 64, 6>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled128Deep:
         return run_tiled<128, 128, 2, 4, 64, 4>(W, x, M, y, p.n, p.k, sp, stream);
+    case DenseKernel::kTiled64x32:
+        return run_tiled<64, 32, 2, 2, 64, 8>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled64:
         break;
     }

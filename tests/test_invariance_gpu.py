@@ -175,8 +175,8 @@ def test_offset_view_of_x(gpu):
 
 def test_every_kernel_configuration(gpu):
     """One layer through every kernel the dispatcher can pick (streaming with
-    1, 2 and 4 m-tiles; tiled 64x64, 128x64 and 128x128 in both depths,
-    128x256 and 256x256): probe rows of each call equal the rows alone, and the values
+    1, 2 and 4 m-tiles; tiled 64x32, 64x64, 128x64 and 128x128 in both
+    depths, 128x256 and 256x256): probe rows of each call equal the rows alone, and the values
     pass the oracle bound."""
     import oracle
     from gpu_util import assert_parity
@@ -189,7 +189,8 @@ def test_every_kernel_configuration(gpu):
     xd = to_dev(x)
     names = {g.kernel_name(m) for m in ms}
     assert names == {"bigemm_stream<mb=1>", "bigemm_stream<mb=2>", "bigemm_stream<mb=4>",
-                     "bigemm_tiled<64x64>", "bigemm_tiled<128x64>", "bigemm_tiled<128x64,deep>",
+                     "bigemm_tiled<64x32>", "bigemm_tiled<64x64>", "bigemm_tiled<128x64>",
+                     "bigemm_tiled<128x64,deep>",
                      "bigemm_tiled<128x128>", "bigemm_tiled<128x128,deep>",
                      "bigemm_tiled<128x256>", "bigemm_tiled<256x256>"}, names
     probes = {m: synth.probe_rows(152 + m, m, 16) for m in ms}
