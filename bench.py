@@ -305,13 +305,13 @@ def run_moe(args, bg):
 
 def moe_cpu_baseline(wbits, calls, target_s=15.0):
     """The oracle's grouped GEMM on the host cores, on a bounded sample: the
-    T=256 up-projection rows, as many as fit in about `target_s` seconds."""
+    T=4096 up-projection rows, as many as fit in about `target_s` seconds."""
     import numpy as np
     import torch
 
     import oracle
 
-    t, name, x, off, _, _, _, _ = next(c for c in calls if c[0] == 256 and c[1] == "up")
+    t, name, x, off, _, _, _, _ = next(c for c in calls if c[0] == 4096 and c[1] == "up")
     xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
     offs = off.cpu().numpy()
     w = wbits[name]
