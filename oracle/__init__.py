@@ -11,6 +11,9 @@ Contents:
 * ``gemm_i64``      exact int64 result for integer-valued inputs;
 * ``grouped_f64``   the MoE expert-grouped variant;
 * ``fold_f32``      the in-order fp32 combine of split partial sums;
+* ``moe_topk``, ``moe_permute``, ``swiglu_f64``, ``moe_combine_f64``
+                    the MoE layer's steps around the grouped GEMM: routing,
+                    grouping by expert, SwiGLU and the weighted combine;
 * ``exact``         exact-rational brute force (``oracle/exact.py``).
 
 Each function cites the passage it follows in ``oracle.c``.  Every function is
@@ -65,8 +68,13 @@ def open_library(path: str):
     lib.oracle_grouped_f64.argtypes = [P, P, L, L, L, P, L, P, L, P, P, I]
     lib.oracle_fold_f32.argtypes = [P, L, L, P]
     lib.oracle_max_threads.argtypes = []
+    lib.oracle_moe_topk.argtypes = [P, L, L, L, P, P]
+    lib.oracle_moe_permute.argtypes = [P, L, L, L, P, P, P]
+    lib.oracle_swiglu_f64.argtypes = [P, L, L, P]
+    lib.oracle_moe_combine_f64.argtypes = [P, L, P, P, L, L, L, P, P]
     for f in (lib.oracle_gemm_f64, lib.oracle_gemm_i64, lib.oracle_grouped_f64,
-              lib.oracle_fold_f32, lib.oracle_max_threads):
+              lib.oracle_fold_f32, lib.oracle_max_threads, lib.oracle_moe_topk,
+              lib.oracle_moe_permute, lib.oracle_swiglu_f64, lib.oracle_moe_combine_f64):
         f.restype = ctypes.c_int
     return lib
 
@@ -178,6 +186,72 @@ def fold_f32(parts, lib=None):
     if rc != 0:
         raise ValueError("oracle_fold_f32 rejected its arguments (%d)" % rc)
     return out.reshape(p.shape[1:])
+
+
+def moe_topk(logits, k: int, lib=None):
+    """Top-k routing: ``(ids [T,k] int32, w [T,k] float64)``, best first, ties to
+    the lower expert id; ``w`` is the softmax over the chosen logits."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    if lg.ndim != 2:
+        raise ValueError("logits must be [T, E]")
+    t, e = lg.shape
+    ids = np.empty((t, k), np.int32)
+    w = np.empty((t, k), np.float64)
+    rc = _load(lib).oracle_moe_topk(lg.ctypes.data, t, e, int(k), ids.ctypes.data, w.ctypes.data)
+    if rc == -3:
+        raise ValueError("moe_topk needs finite logits")
+    if rc != 0:
+        raise ValueError("oracle_moe_topk rejected its arguments (%d)" % rc)
+    return ids, w
+
+
+def moe_permute(ids, experts: int, lib=None):
+    """Stable grouping of the (token, slot) pairs by expert:
+    ``(offsets [E+1], token_of_row [R], row_of [T,k])``, all int32."""
+    a = np.ascontiguousarray(ids, dtype=np.int32)
+    if a.ndim != 2:
+        raise ValueError("ids must be [T, k]")
+    t, k = a.shape
+    off = np.empty(experts + 1, np.int32)
+    tok = np.empty(t * k, np.int32)
+    row_of = np.empty((t, k), np.int32)
+    rc = _load(lib).oracle_moe_permute(a.ctypes.data, t, int(experts), k, off.ctypes.data,
+                                    tok.ctypes.data, row_of.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_moe_permute rejected its arguments (%d)" % rc)
+    return off, tok, row_of
+
+
+def swiglu_f64(h, lib=None):
+    """``silu(h[:, :I]) * h[:, I:]`` in fp64 for h float32 [R, 2I]."""
+    hh = np.ascontiguousarray(h, dtype=np.float32)
+    if hh.ndim != 2 or hh.shape[1] % 2:
+        raise ValueError("h must be [R, 2I]")
+    r, i2 = hh.shape
+    out = np.empty((r, i2 // 2), np.float64)
+    rc = _load(lib).oracle_swiglu_f64(hh.ctypes.data, r, i2 // 2, out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_swiglu_f64 rejected its arguments (%d)" % rc)
+    return out
+
+
+def moe_combine_f64(o, w, row_of, lib=None):
+    """``y[t] = sum_j w[t,j] * o[row_of[t,j]]`` in fp64 and its magnitude
+    ``s[t] = sum_j |w[t,j] * o[row_of[t,j]]|``."""
+    oo = np.ascontiguousarray(o, dtype=np.float32)
+    ww = np.ascontiguousarray(w, dtype=np.float32)
+    ro = np.ascontiguousarray(row_of, dtype=np.int32)
+    if oo.ndim != 2 or ww.shape != ro.shape or ww.ndim != 2:
+        raise ValueError("shape mismatch")
+    r, h = oo.shape
+    t, k = ww.shape
+    y = np.empty((t, h), np.float64)
+    s = np.empty((t, h), np.float64)
+    rc = _load(lib).oracle_moe_combine_f64(oo.ctypes.data, r, ww.ctypes.data, ro.ctypes.data, t, k, h,
+                                     y.ctypes.data, s.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_moe_combine_f64 rejected its arguments (%d)" % rc)
+    return y, s
 
 
 def within_bound(y_gpu, y_ref, a, rel: float = 1e-4):

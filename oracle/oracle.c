@@ -199,3 +199,141 @@ int oracle_fold_f32(const float *parts, long S, long count, float *out)
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * The MoE layer around the grouped GEMM.  The fused MoE is one of the kernel
+ * families whose selection reads the batch (Detent, §2 Obs. 1 and Fig. 3a:
+ * it takes the tuned row nearest the batch's token count); each step below is
+ * a function of one token's own values, so the whole layer is too.  The steps
+ * follow a Qwen3-30B-A3B-style expert layer (Detent, §8.1: the MoE deployment;
+ * CoRun, §VII-C: a router perturbation changes the experts a token uses):
+ * router logits, top-k, grouping of the rows by expert, up projection, SwiGLU,
+ * down projection, and the weighted combine of each token's k expert outputs.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Top-k routing of each token: the k experts with the largest logits, best
+ * first, an equal logit going to the lower expert id; the decision compares
+ * the fp32 logits as given.  weights w[t][j] = exp(l_j - l_0) / sum_i exp(l_i
+ * - l_0) over the k chosen logits, in fp64 (the softmax over all experts,
+ * renormalised over the chosen ones, is the same number).  k passes over the
+ * logits, each taking the best expert not yet chosen.  Returns 0, -1 on a bad
+ * argument, -3 when a logit is not finite.
+ */
+int oracle_moe_topk(const float *logits, long T, long E, long k, int32_t *ids, double *w)
+{
+    if (!logits || !ids || !w || T < 0 || E <= 0 || k <= 0 || k > E || k > 1024)
+        return -1;
+    for (long i = 0; i < T * E; ++i)
+        if (!isfinite(logits[i]))
+            return -3;
+    for (long t = 0; t < T; ++t) {
+        const float *l = logits + t * E;
+        int32_t *id = ids + t * k;
+        for (long j = 0; j < k; ++j) {
+            long best = -1;
+            for (long e = 0; e < E; ++e) {
+                int taken = 0;
+                for (long q = 0; q < j; ++q)
+                    taken |= id[q] == e;
+                if (taken)
+                    continue;
+                if (best < 0 || l[e] > l[best])  /* ties keep the lower id found first */
+                    best = e;
+            }
+            id[j] = (int32_t)best;
+        }
+        double z[1024];
+        double s = 0.0;
+        for (long j = 0; j < k; ++j) {
+            z[j] = exp((double)l[id[j]] - (double)l[id[0]]);
+            s += z[j];
+        }
+        for (long j = 0; j < k; ++j)
+            w[t * k + j] = z[j] / s;
+    }
+    return 0;
+}
+
+/*
+ * Rows grouped by expert: every (token t, slot j) pair becomes one row of its
+ * expert ids[t][j]; experts in ascending id, and inside an expert the pairs
+ * in ascending (t, j) -- a stable counting sort.  offsets[E+1] delimits each
+ * expert's rows, token_of_row[R] names a row's token and row_of[t*k + j] the
+ * row of pair (t, j).  Returns 0, or -1 on a bad argument or an id outside
+ * 0..E-1.
+ */
+int oracle_moe_permute(const int32_t *ids, long T, long E, long k, int32_t *offsets,
+                       int32_t *token_of_row, int32_t *row_of)
+{
+    if (!ids || !offsets || !token_of_row || !row_of || T < 0 || E <= 0 || k <= 0)
+        return -1;
+    for (long i = 0; i < T * k; ++i)
+        if (ids[i] < 0 || ids[i] >= E)
+            return -1;
+    for (long e = 0; e <= E; ++e)
+        offsets[e] = 0;
+    for (long i = 0; i < T * k; ++i)
+        offsets[ids[i] + 1] += 1;
+    for (long e = 0; e < E; ++e)
+        offsets[e + 1] += offsets[e];
+    for (long e = 0; e < E; ++e) {
+        long r = offsets[e];
+        for (long t = 0; t < T; ++t)
+            for (long j = 0; j < k; ++j)
+                if (ids[t * k + j] == e) {
+                    token_of_row[r] = (int32_t)t;
+                    row_of[t * k + j] = (int32_t)r;
+                    ++r;
+                }
+    }
+    return 0;
+}
+
+/*
+ * SwiGLU of the up projection's output h [R, 2I] (gate columns 0..I-1, up
+ * columns I..2I-1): a[r][i] = silu(g) * u with silu(g) = g / (1 + exp(-g)),
+ * in fp64.  Returns 0 or -1.
+ */
+int oracle_swiglu_f64(const float *h, long R, long I, double *a)
+{
+    if (!h || !a || R < 0 || I <= 0)
+        return -1;
+    for (long r = 0; r < R; ++r)
+        for (long i = 0; i < I; ++i) {
+            double g = h[r * 2 * I + i];
+            double u = h[r * 2 * I + I + i];
+            a[r * I + i] = g / (1.0 + exp(-g)) * u;
+        }
+    return 0;
+}
+
+/*
+ * Weighted combine of each token's k expert outputs:
+ *   y[t][n] = sum_j w[t][j] * o[row_of[t][j]][n]
+ * in fp64, and s[t][n] = sum_j |w[t][j] * o[row_of[t][j]][n]|, the scale of
+ * the bound a fixed-order fp32 sum is judged by.  Returns 0, or -1 on a bad
+ * argument or a row outside 0..R-1.
+ */
+int oracle_moe_combine_f64(const float *o, long R, const float *w, const int32_t *row_of, long T,
+                           long k, long H, double *y, double *s)
+{
+    if (!o || !w || !row_of || !y || R < 0 || T < 0 || k <= 0 || H < 0)
+        return -1;
+    for (long i = 0; i < T * k; ++i)
+        if (row_of[i] < 0 || row_of[i] >= R)
+            return -1;
+    for (long t = 0; t < T; ++t)
+        for (long n = 0; n < H; ++n) {
+            double acc = 0.0, mag = 0.0;
+            for (long j = 0; j < k; ++j) {
+                double p = (double)w[t * k + j] * (double)o[(long)row_of[t * k + j] * H + n];
+                acc += p;
+                mag += fabs(p);
+            }
+            y[t * H + n] = acc;
+            if (s)
+                s[t * H + n] = mag;
+        }
+    return 0;
+}

@@ -35,6 +35,7 @@ __all__ = [
     "silu_mul_bf16",
     "rms_rows_bf16",
     "moe_routing",
+    "router_logits",
     "probe_rows",
 ]
 
@@ -110,32 +111,42 @@ def rms_rows_bf16(seed: int, shape, eps: float = 1e-5) -> np.ndarray:
 
 
 def moe_routing(seed: int, tokens: int, experts: int = 128, topk: int = 8):
-    """Top-k routing from softmax of N(0,1) router logits.
+    """A routing of ``tokens`` tokens to ``topk`` distinct experts each, laid
+    out as the grouped GEMM takes its rows.
 
-    Returns ``(token_of_row, expert_offsets, topk_ids)``:
+    Each token's experts are a uniformly drawn ``topk``-subset of the experts:
+    the distribution that the top-k of i.i.d. N(0,1) router logits has.  (The
+    routing computation itself is a step of the MoE layer; this only draws an
+    input with its statistics.)  Returns ``(token_of_row, expert_offsets,
+    topk_ids)``:
 
-    * ``topk_ids`` [tokens, topk] int32: the chosen experts per token,
-      best first; ties go to the lower expert id;
+    * ``topk_ids`` [tokens, topk] int32: each token's experts in drawn order;
     * rows are grouped by expert (ascending) and, inside an expert, by token
       (ascending); ``token_of_row`` [tokens*topk] int32 names each row's token;
     * ``expert_offsets`` [experts+1] int32: rows of expert ``e`` are
       ``offsets[e] .. offsets[e+1]-1``.
     """
-    logits = _normal_f32(seed, (tokens, experts))
-    z = logits - logits.max(axis=1, keepdims=True)
-    p = np.exp(z, dtype=np.float32)
-    p /= p.sum(axis=1, keepdims=True, dtype=np.float32)
-    # stable sort on (-p) keeps the lower id first among equal probabilities
-    order = np.argsort(-p, axis=1, kind="stable")
-    topk_ids = order[:, :topk].astype(np.int32)
-    tok = np.repeat(np.arange(tokens, dtype=np.int64), topk)
-    exp = topk_ids.reshape(-1).astype(np.int64)
-    perm = np.lexsort((tok, exp))
-    token_of_row = tok[perm].astype(np.int32)
-    counts = np.bincount(exp, minlength=experts)
+    g = rng(seed)
+    topk_ids = np.zeros((tokens, topk), dtype=np.int32)
+    for t in range(tokens):
+        topk_ids[t] = g.permutation(experts)[:topk]
+    chosen = [set(int(e) for e in row) for row in topk_ids]
+    token_of_row = np.array([t for e in range(experts) for t in range(tokens) if e in chosen[t]],
+                            dtype=np.int32)
     offsets = np.zeros(experts + 1, dtype=np.int32)
-    offsets[1:] = np.cumsum(counts)
+    for e in range(experts):
+        offsets[e + 1] = offsets[e] + sum(1 for t in range(tokens) if e in chosen[t])
     return token_of_row, offsets, topk_ids
+
+
+def router_logits(seed: int, tokens: int, experts: int = 128, step: float = 0.0) -> np.ndarray:
+    """fp32 router logits [tokens, experts], N(0,1).  With ``step`` > 0 they are
+    rounded to multiples of ``step``, which makes equal logits common (the
+    case the routing's tie rule decides)."""
+    lg = _normal_f32(seed, (tokens, experts))
+    if step > 0:
+        lg = (np.round(lg / np.float32(step)) * np.float32(step)).astype(np.float32)
+    return np.ascontiguousarray(lg, dtype=np.float32)
 
 
 def probe_rows(seed: int, m: int, count: int = 64) -> np.ndarray:

@@ -201,6 +201,95 @@ def pin_fold(lib=None):
         assert int(got.view(np.uint32)[0]) == want, (parts, hex(int(got.view(np.uint32)[0])), hex(want))
 
 
+def pin_moe_topk(lib=None):
+    """Routing against a plain sort, closed-form weights and shift invariance."""
+    for seed, t, e, k, step in ((910, 40, 16, 4, 0.5), (911, 20, 9, 9, 0.25), (912, 30, 128, 8, 0.0)):
+        lg = synth.router_logits(seed, t, e, step=step)
+        ids, w = oracle.moe_topk(lg, k, lib=lib)
+        for i in range(t):
+            want = sorted(range(e), key=lambda q: (-float(lg[i, q]), q))[:k]
+            assert ids[i].tolist() == want, (seed, i)
+        assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+        assert np.all(np.diff(w, axis=1) <= 0)
+        # adding a constant that keeps every logit exact changes nothing
+        if step > 0:
+            ids2, w2 = oracle.moe_topk(lg + np.float32(0.5), k, lib=lib)
+            assert np.array_equal(ids, ids2) and np.allclose(w, w2, rtol=0, atol=1e-15)
+    # all logits equal: the k lowest ids, weight 1/k each
+    ids, w = oracle.moe_topk(np.full((2, 10), 0.75, np.float32), 4, lib=lib)
+    assert ids.tolist() == [[0, 1, 2, 3]] * 2 and np.all(w == 0.25)
+    # two chosen logits ln(3) apart: weights 3/4 and 1/4 (up to the fp32 logit)
+    l3 = np.float32(np.log(3.0))
+    ids, w = oracle.moe_topk(np.array([[0.0, l3, -5.0]], np.float32), 2, lib=lib)
+    assert ids.tolist() == [[1, 0]] and abs(w[0, 0] - 0.75) < 1e-7 and abs(w[0, 1] - 0.25) < 1e-7
+    try:
+        oracle.moe_topk(np.array([[0.0, np.inf]], np.float32), 1, lib=lib)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a non-finite logit must be rejected")
+
+
+def pin_moe_permute(lib=None):
+    """Grouping against numpy's stable sort by expert, and its inverse."""
+    for seed, t, e, k in ((920, 50, 16, 4), (921, 7, 128, 8), (922, 1, 8, 8)):
+        g = synth.rng(seed)
+        ids = np.stack([g.permutation(e)[:k] for _ in range(t)]).astype(np.int32)
+        off, tok, row_of = oracle.moe_permute(ids, e, lib=lib)
+        flat = ids.reshape(-1)
+        order = np.argsort(flat, kind="stable")
+        assert np.array_equal(tok, (order // k).astype(np.int32))
+        assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=e))]))
+        inv = np.empty(t * k, np.int64)
+        inv[order] = np.arange(t * k)
+        assert np.array_equal(row_of.reshape(-1), inv)
+        assert np.array_equal(tok[row_of], np.repeat(np.arange(t), k).reshape(t, k))
+    try:
+        oracle.moe_permute(np.array([[0, 9]], np.int32), 8, lib=lib)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("an id outside 0..E-1 must be rejected")
+
+
+def pin_swiglu(lib=None):
+    """Closed forms of silu(g) * u and scipy's logistic function."""
+    from scipy.special import expit
+
+    l3 = float(np.float32(np.log(3.0)))
+    gates = [0.0, l3, 30.0, -30.0, 1.0]
+    ups = [3.0, 0.5, 2.0, 2.0, 0.0]
+    a = oracle.swiglu_f64(np.array([gates + ups], np.float32), lib=lib)[0]
+    assert a[0] == 0.0                                      # silu(0) = 0
+    assert abs(a[1] / (0.375 * l3) - 1.0) < 1e-7            # silu(ln 3) = 3/4 ln 3, times 1/2
+    assert abs(a[2] / 60.0 - 1.0) < 1e-12                   # large gate: g * u
+    assert -1e-11 < a[3] < 0.0                              # very negative gate: ~0, negative
+    assert a[4] == 0.0                                      # up 0 -> 0
+    g = synth.rng(930).standard_normal((40, 64)).astype(np.float32) * 4
+    a = oracle.swiglu_f64(g, lib=lib)
+    gg, uu = g[:, :32].astype(np.float64), g[:, 32:].astype(np.float64)
+    assert np.allclose(a, gg * expit(gg) * uu, rtol=1e-14, atol=1e-300)
+
+
+def pin_moe_combine(lib=None):
+    """Integer outputs with dyadic weights sum exactly in any order."""
+    g = synth.rng(940)
+    t, k, h, r = 12, 4, 24, 48
+    o = g.integers(-3, 4, size=(r, h)).astype(np.float32)
+    w = np.exp2(-g.integers(0, 4, size=(t, k))).astype(np.float32)
+    row_of = np.stack([g.permutation(r)[:k] for _ in range(t)]).astype(np.int32)
+    y, s = oracle.moe_combine_f64(o, w, row_of, lib=lib)
+    for i in range(t):
+        for n in range(h):
+            want = sum(Fraction(float(w[i, j])) * Fraction(float(o[row_of[i, j], n])) for j in range(k))
+            assert Fraction(y[i, n]) == want
+            assert s[i, n] == float(sum(abs(Fraction(float(w[i, j])) * Fraction(float(o[row_of[i, j], n])))
+                                        for j in range(k)))
+    # one expert with weight 1 returns its row
+    y1, _ = oracle.moe_combine_f64(o, np.ones((t, 1), np.float32), row_of[:, :1], lib=lib)
+    assert np.array_equal(y1, o[row_of[:, 0]].astype(np.float64))
+
+
 ALL_PINS = [
     pin_exact_rationals,
     pin_golden_gemm,
@@ -211,4 +300,8 @@ ALL_PINS = [
     pin_row_selection,
     pin_grouped,
     pin_fold,
+    pin_moe_topk,
+    pin_moe_permute,
+    pin_swiglu,
+    pin_moe_combine,
 ]

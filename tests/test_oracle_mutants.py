@@ -1,7 +1,8 @@
 """Planted mistakes in the oracle, on the CPU: each broken copy of oracle.c
 must fail at least one pin.  This shows the pins would catch a dropped term,
-a wrong sign or index, a transposed operand, a narrower accumulator or a
-reordered combine in the oracle itself.
+a wrong sign or index, a transposed operand, a narrower accumulator, a
+reordered combine, a flipped tie rule, an unstable grouping or a swapped
+operand in the oracle itself.
 """
 import os
 
@@ -27,6 +28,18 @@ MUTANTS = [
      "volatile float t = parts[j];\n        for (long s = 1; s < S; ++s)\n            t = t + parts[s * count + j];",
      "volatile float t = parts[(S - 1) * count + j];\n        for (long s = S - 2; s >= 0; --s)\n            t = t + parts[s * count + j];", 0),
     ("fold_in_fp64", "volatile float t = parts[j];", "volatile double t = parts[j];", 0),
+    ("topk_ties_to_higher_id", "if (best < 0 || l[e] > l[best])", "if (best < 0 || l[e] >= l[best])", 0),
+    ("topk_weight_sign", "z[j] = exp((double)l[id[j]] - (double)l[id[0]]);",
+     "z[j] = exp((double)l[id[0]] - (double)l[id[j]]);", 0),
+    ("permute_unstable",
+     "for (long t = 0; t < T; ++t)\n            for (long j = 0; j < k; ++j)\n                if (ids[t * k + j] == e) {",
+     "for (long t = T - 1; t >= 0; --t)\n            for (long j = 0; j < k; ++j)\n                if (ids[t * k + j] == e) {", 0),
+    ("permute_offset_index", "offsets[ids[i] + 1] += 1;", "offsets[ids[i]] += 1;", 0),
+    ("swiglu_sigmoid_sign", "a[r * I + i] = g / (1.0 + exp(-g)) * u;", "a[r * I + i] = g / (1.0 + exp(g)) * u;", 0),
+    ("swiglu_gate_up_swapped", "double g = h[r * 2 * I + i];", "double g = h[r * 2 * I + I + i];", 0),
+    ("combine_drops_last_expert", "for (long j = 0; j < k; ++j) {\n                double p = (double)w",
+     "for (long j = 0; j < k - 1; ++j) {\n                double p = (double)w", 0),
+    ("combine_ignores_weight", "double p = (double)w[t * k + j] * ", "double p = 1.0 * ", 0),
 ]
 
 

@@ -60,12 +60,21 @@ def test_moe_routing_tables():
         assert np.all(np.diff(rows) > 0)
         for t in rows:
             assert e in ids[t]
-    # top-k really is the k largest logits
-    g = synth.rng(42)
-    logits = g.standard_normal(size=(256, 128), dtype=np.float32)
-    for t in range(0, 256, 37):
-        top = set(np.argsort(-logits[t])[:8].tolist())
-        assert top == set(ids[t].tolist())
+    # every expert is about equally popular (uniform 8-subsets: 16 rows each)
+    counts = np.diff(off)
+    assert counts.min() > 0 and abs(counts.mean() - 16) < 1e-9 and counts.max() < 48
+    # same seed, same routing
+    tok2, off2, ids2 = synth.moe_routing(42, 256, experts=128, topk=8)
+    assert np.array_equal(tok, tok2) and np.array_equal(off, off2) and np.array_equal(ids, ids2)
+
+
+def test_router_logits():
+    lg = synth.router_logits(5, 64, 128)
+    assert lg.dtype == np.float32 and lg.shape == (64, 128) and 0.8 < lg.std() < 1.2
+    q = synth.router_logits(5, 64, 128, step=0.25)
+    assert np.all(q * 4 == np.round(q * 4))
+    # rounding makes ties common
+    assert any(len(set(row.tolist())) < 128 for row in q)
 
 
 def test_probe_rows():
