@@ -48,13 +48,23 @@ def rng(seed: int) -> np.random.Generator:
 def f32_to_bf16_bits(a) -> np.ndarray:
     """Round fp32 values to bf16 (round to nearest, ties to even).
 
-    Returns the 16-bit patterns.  Inputs must be finite.
+    Returns the 16-bit patterns.  Inputs must be finite: then the 32-bit sum
+    below cannot wrap (only NaN patterns exceed 0xFFFF8000).  Works in chunks
+    of 2^24 values to bound the temporaries.
     """
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = (u + 0x7FFF + lsb) >> 16
-    return r.astype(np.uint16)
+    u = a.reshape(-1).view(np.uint32)
+    out = np.empty(u.shape, np.uint16)
+    step = 1 << 24
+    for lo in range(0, u.size, step):
+        c = u[lo:lo + step]
+        r = c >> 16
+        r &= 1
+        r += 0x7FFF
+        r += c
+        r >>= 16
+        out[lo:lo + step] = r
+    return out.reshape(a.shape)
 
 
 def bf16_bits_to_f32(b) -> np.ndarray:

@@ -5,11 +5,12 @@ reordered combine, a flipped tie rule, an unstable grouping or a swapped
 operand in the oracle itself.
 """
 import os
+import subprocess
+import sys
 
 import pytest
 
 import oracle
-from oracle_pins import ALL_PINS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -50,17 +51,37 @@ def _mutate(text, old, new, occurrence):
     return text[:pos] + new + text[pos + len(old):]
 
 
+# Runs every pin against one compiled mutant in a child process: a planted
+# mistake may write out of bounds (a shifted offset table does), and that
+# must not corrupt the test runner's heap.  Prints the pins that failed.
+CHILD = r"""
+import sys
+sys.path[:0] = sys.argv[3:]
+import oracle
+from oracle_pins import ALL_PINS
+lib = oracle.open_library(sys.argv[1])
+failed = []
+for pin in ALL_PINS:
+    try:
+        pin(lib=lib)
+    except (AssertionError, ValueError):
+        failed.append(pin.__name__)
+print("FAILED_PINS", len(failed), " ".join(failed))
+"""
+
+
 @pytest.mark.parametrize("name,old,new,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(tmp_path, name, old, new, occ):
     text = open(SRC).read()
     assert old in text, "mutation site vanished: " + name
     src = tmp_path / ("oracle_%s.c" % name)
     src.write_text(_mutate(text, old, new, occ))
-    lib = oracle.open_library(oracle.compile_source(str(src), str(tmp_path / ("lib%s.so" % name))))
-    failures = []
-    for pin in ALL_PINS:
-        try:
-            pin(lib=lib)
-        except (AssertionError, ValueError) as exc:  # noqa: PERF203
-            failures.append((pin.__name__, repr(exc)[:80]))
-    assert failures, "no pin caught the planted mistake " + name
+    so = oracle.compile_source(str(src), str(tmp_path / ("lib%s.so" % name)))
+    here = os.path.dirname(os.path.abspath(__file__))
+    res = subprocess.run([sys.executable, "-c", CHILD, so, name, here, os.path.dirname(here)],
+                         capture_output=True, text=True, timeout=300)
+    lines = [l for l in res.stdout.splitlines() if l.startswith("FAILED_PINS")]
+    if lines:  # the pins ran to the end (the process may still crash on exit)
+        assert int(lines[-1].split()[1]) > 0, "no pin caught the planted mistake " + name
+    else:
+        assert res.returncode < 0, res.stderr[-2000:]  # a pin run crashed: caught
