@@ -3,7 +3,8 @@
 ``y = x @ W.T`` in fp32 with bits of every row independent of the batch:
 row count, row position and the other rows never change a row's result.
 The compute runs in the hand-written HIP library ``libbigemm.so`` (C ABI in
-``include/bi_gemm.h``); this package is its thin Python binding.
+``include/bi_gemm.h``, and ``include/bi_moe.h`` for the MoE expert layer built
+around the grouped GEMM); this package is its thin Python binding.
 """
 from ._lib import (  # noqa: F401
     LIB_PATH,
@@ -14,8 +15,14 @@ from ._lib import (  # noqa: F401
     BiPinInfo,
     Gemm,
     GroupedGemm,
+    MoeLayer,
     check,
+    gather_rows,
     last_error,
     load,
+    moe_combine,
+    moe_permute,
+    moe_topk,
     status_string,
+    swiglu,
 )

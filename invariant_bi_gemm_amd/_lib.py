@@ -1,4 +1,4 @@
-"""ctypes binding of the C ABI declared in include/bi_gemm.h.
+"""ctypes binding of the C ABI declared in include/bi_gemm.h and include/bi_moe.h.
 
 Argument marshalling only: every step of the GEMM runs in the HIP library
 ``libbigemm.so``.  Tensors are PyTorch device tensors (PyTorch provides device
@@ -66,6 +66,14 @@ def _declare(lib):
         "bi_status_string": ([S], ctypes.c_char_p),
         "bi_gemm_kernel_name": ([P, I], ctypes.c_char_p),
         "bi_last_error": ([], ctypes.c_char_p),
+        "bi_moe_topk": ([P, I, I, I, P, P, P], S),
+        "bi_moe_permute": ([P, I, I, I, P, P, P, P], S),
+        "bi_gather_rows": ([P, I, P, I, I, P, P], S),
+        "bi_swiglu": ([P, I, I, P, P], S),
+        "bi_moe_combine": ([P, I, P, P, P, I, I, I, P, P], S),
+        "bi_moe_create": ([I, I, I, I, P, P, P, I, ctypes.POINTER(P)], S),
+        "bi_moe_run": ([P, P, I, P, P], S),
+        "bi_moe_destroy": ([P], None),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -241,6 +249,140 @@ class GroupedGemm:
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:
             self._lib.bi_gemm_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001
+            pass
+
+
+# ---- the MoE layer around the grouped GEMM (include/bi_moe.h) ----------------
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def moe_topk(logits, k: int, stream=None):
+    """Top-k routing of fp32 logits [T, E]: ``(ids int32 [T,k], weights fp32 [T,k])``."""
+    import torch
+
+    lib = load()
+    _need(logits, torch.float32, 2, "logits")
+    t, e = (int(v) for v in logits.shape)
+    ids = torch.empty((t, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((t, k), dtype=torch.float32, device=logits.device)
+    check(lib.bi_moe_topk(_p(logits), t, e, int(k), _p(ids), _p(w), _stream_ptr(stream)))
+    return ids, w
+
+
+def moe_permute(ids, experts: int, stream=None):
+    """Stable grouping of the (token, slot) pairs by expert:
+    ``(offsets [E+1], token_of_row [T*k], row_of [T,k])``, int32."""
+    import torch
+
+    lib = load()
+    _need(ids, torch.int32, 2, "ids")
+    t, k = (int(v) for v in ids.shape)
+    dev = ids.device
+    off = torch.empty(experts + 1, dtype=torch.int32, device=dev)
+    tok = torch.empty(t * k, dtype=torch.int32, device=dev)
+    row_of = torch.empty((t, k), dtype=torch.int32, device=dev)
+    check(lib.bi_moe_permute(_p(ids), t, int(experts), k, _p(off), _p(tok), _p(row_of), _stream_ptr(stream)))
+    return off, tok, row_of
+
+
+def gather_rows(src, idx, stream=None):
+    """``src[idx]`` for bf16 rows (an index outside the rows gives zeros)."""
+    import torch
+
+    lib = load()
+    _need(src, torch.bfloat16, 2, "src")
+    _need(idx, torch.int32, 1, "idx")
+    r, kk = int(idx.shape[0]), int(src.shape[1])
+    out = torch.empty((r, kk), dtype=torch.bfloat16, device=src.device)
+    check(lib.bi_gather_rows(_p(src), int(src.shape[0]), _p(idx), r, kk, _p(out), _stream_ptr(stream)))
+    return out
+
+
+def swiglu(h, stream=None):
+    """bf16 ``silu(h[:, :I]) * h[:, I:]`` of an fp32 up projection h [R, 2I]."""
+    import torch
+
+    lib = load()
+    _need(h, torch.float32, 2, "h")
+    r, i2 = (int(v) for v in h.shape)
+    if i2 % 2:
+        raise ValueError("h must have an even number of columns")
+    out = torch.empty((r, i2 // 2), dtype=torch.bfloat16, device=h.device)
+    check(lib.bi_swiglu(_p(h), r, i2 // 2, _p(out), _stream_ptr(stream)))
+    return out
+
+
+def moe_combine(o, ids, weights, row_of, stream=None):
+    """``y[t] = sum_j weights[t,j] * o[row_of[t,j]]`` in ascending expert id."""
+    import torch
+
+    lib = load()
+    _need(o, torch.float32, 2, "o")
+    _need(ids, torch.int32, 2, "ids")
+    _need(weights, torch.float32, 2, "weights")
+    _need(row_of, torch.int32, 2, "row_of")
+    t, k = (int(v) for v in ids.shape)
+    if tuple(weights.shape) != (t, k) or tuple(row_of.shape) != (t, k):
+        raise ValueError("ids, weights and row_of must all be [T, k]")
+    r, hdim = (int(v) for v in o.shape)
+    y = torch.empty((t, hdim), dtype=torch.float32, device=o.device)
+    check(lib.bi_moe_combine(_p(o), r, _p(ids), _p(weights), _p(row_of), t, k, hdim, _p(y),
+                             _stream_ptr(stream)))
+    return y
+
+
+class MoeLayer:
+    """The expert layer: router, top-k, grouping, up projection, SwiGLU, down
+    projection and the weighted combine, every token's output independent of
+    the batch.  ``W_router`` bf16 [E, H], ``W_up`` bf16 [E, 2I, H] (gate rows
+    then up rows), ``W_down`` bf16 [E, H, I]; the handle keeps references."""
+
+    def __init__(self, W_router, W_up, W_down, k: int, max_tokens: int):
+        import torch
+
+        lib = load()
+        _need(W_router, torch.bfloat16, 2, "W_router")
+        _need(W_up, torch.bfloat16, 3, "W_up")
+        _need(W_down, torch.bfloat16, 3, "W_down")
+        self.e, self.h = (int(v) for v in W_router.shape)
+        self.i = int(W_down.shape[2])
+        self.k, self.max_tokens = int(k), int(max_tokens)
+        if tuple(W_up.shape) != (self.e, 2 * self.i, self.h) or tuple(W_down.shape) != (self.e, self.h, self.i):
+            raise ValueError("W_up must be [E, 2I, H] and W_down [E, H, I]")
+        self._w = (W_router, W_up, W_down)
+        self._lib = lib
+        h = ctypes.c_void_p()
+        with torch.cuda.device(W_router.device):
+            st = lib.bi_moe_create(self.e, self.k, self.h, self.i, _p(W_router), _p(W_up), _p(W_down),
+                                   self.max_tokens, ctypes.byref(h))
+        check(st)
+        self._h = h
+
+    def __call__(self, x, out=None, stream=None):
+        import torch
+
+        _need(x, torch.bfloat16, 2, "x")
+        t = int(x.shape[0])
+        if int(x.shape[1]) != self.h:
+            raise ValueError("x must be [T, %d]" % self.h)
+        if out is None:
+            out = torch.empty((t, self.h), dtype=torch.float32, device=x.device)
+        else:
+            _need(out, torch.float32, 2, "out")
+        check(self._lib.bi_moe_run(self._h, _p(x), t, _p(out), _stream_ptr(stream)))
+        return out
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.bi_moe_destroy(self._h)
             self._h = ctypes.c_void_p()
 
     def __del__(self):

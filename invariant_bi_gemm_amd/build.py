@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbigemm.so")
-SOURCES = ["bigemm_api.cpp", "bigemm_kernels.hip"]
+SOURCES = ["bigemm_api.cpp", "bigemm_kernels.hip", "moe_api.cpp", "moe_kernels.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

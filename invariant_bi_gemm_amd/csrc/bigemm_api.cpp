@@ -324,6 +324,25 @@ bi_status_t check_run_device(const bi_gemm* h)
 
 }  // namespace
 
+namespace bigemm {
+
+bi_status_t api_fail(bi_status_t st, const char* msg) { return fail(st, msg); }
+
+bi_status_t api_device(int* dev, int* num_cus)
+{
+    DeviceInfo info;
+    const bi_status_t st = current_device(dev, &info);
+    if (st != BI_OK)
+        return st;
+    if (!info.gfx950)
+        return fail(BI_ERR_UNSUPPORTED_DEVICE, "device " + std::to_string(*dev) + " is " + info.arch +
+                                                   ", the kernels are built for gfx950");
+    *num_cus = info.num_cus;
+    return BI_OK;
+}
+
+}  // namespace bigemm
+
 extern "C" {
 
 bi_status_t bi_gemm_load_pins(const char* path)

@@ -43,6 +43,12 @@ enum class DenseKernel {
 DenseKernel choose_dense(const Plan& p, int M);
 const char* dense_kernel_name(DenseKernel k);
 
+// Host helpers the MoE layer's API shares with the GEMM API
+// (bigemm_api.cpp): record the calling thread's bi_last_error() and return
+// st; and the current device, failing unless it is a gfx950.
+bi_status_t api_fail(bi_status_t st, const char* msg);
+bi_status_t api_device(int* dev, int* num_cus);
+
 // Launchers (bigemm_kernels.hip).  They assume validated arguments.
 hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, float* y,
                         hipStream_t stream);

@@ -141,7 +141,7 @@ def test_pin_table_entries_legal():
     assert version and version > 0
     assert len(rows) == len(set(rows))
     # every shape the workloads use has a pin
-    for shape in ((256, 512), (4096, 14336), (28672, 4096), (8192, 3584), (1536, 2048), (2048, 768)):
+    for shape in ((128, 2048), (256, 512), (4096, 14336), (28672, 4096), (8192, 3584), (1536, 2048), (2048, 768)):
         assert ("gfx950",) + shape in rows
 
 
