@@ -328,12 +328,241 @@ def moe_cpu_baseline(wbits, calls, target_s=15.0):
             "rows at T=%d, %.1f s" % (n, k, nrows, xb.shape[0], t, dt)}
 
 
+def _moe_layer_weights(seed=42):
+    import synth
+
+    E, H, I = MOE["experts"], MOE["up"][1], MOE["down"][1]
+    return (synth.normal_bf16(seed + 10, (E, H), MOE["std"]),
+            synth.normal_bf16(seed + 11, (E, 2 * I, H), MOE["std"]),
+            synth.normal_bf16(seed + 12, (E, H, I), MOE["std"]))
+
+
+def moe_layer_work(t, touched_up, touched_down):
+    """Algorithmic flops and HBM bytes of each step of the layer at T tokens
+    (R = kT rows); a GEMM's weight bytes count only the touched experts."""
+    E, k, H, I = MOE["experts"], MOE["topk"], MOE["up"][1], MOE["down"][1]
+    r = k * t
+    return [
+        ("router GEMM", 2.0 * t * E * H, 2.0 * E * H + 2.0 * t * H + 4.0 * t * E),
+        ("top-k", 0.0, 4.0 * t * E + 8.0 * t * k),
+        ("grouping", 0.0, 4.0 * t * k + 4.0 * (E + 1) + 8.0 * r),
+        ("gather", 0.0, 2.0 * t * H + 2.0 * r * H + 4.0 * r),
+        ("up GEMM", 2.0 * r * 2 * I * H, 2.0 * touched_up * 2 * I * H + 2.0 * r * H + 4.0 * r * 2 * I),
+        ("SwiGLU", 0.0, 4.0 * r * 2 * I + 2.0 * r * I),
+        ("down GEMM", 2.0 * r * H * I, 2.0 * touched_down * H * I + 2.0 * r * I + 4.0 * r * H),
+        ("combine", 0.0, 4.0 * r * H + 12.0 * t * k + 4.0 * t * H),
+    ]
+
+
+def _roof(flops, nbytes, us):
+    """The binding roofline of one kernel's algorithmic work and its achieved rate."""
+    if flops / (PEAK_BF16_TFLOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9):
+        a = flops / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": a / PEAK_BF16_TFLOPS}
+    a = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": a / PEAK_HBM_GBS}
+
+
+def run_moe_layer(args, bg):
+    """One step = the whole expert layer (router, top-k, grouping, gather, up
+    projection, SwiGLU, down projection, combine; one bi_moe_run call) at
+    every token count T of the sweep.  Two layer handles over two copies of
+    the weights alternate, so the Infinity Cache does not keep a call's
+    experts for the next call of the same T.  A second pass runs the steps
+    one by one through their own entry points (the same kernels, bit for bit)
+    with events around each, for the per-kernel breakdown and roofline."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import synth
+
+    E, k, H, I = MOE["experts"], MOE["topk"], MOE["up"][1], MOE["down"][1]
+    tokens = MOE["tokens"]
+    tmax = max(tokens)
+    wr, wu, wd = _moe_layer_weights()
+    dev = [tuple(to_dev(w) for w in (wr, wu, wd))]
+    dev.append(tuple(w.clone() for w in dev[0]))
+    layers = [bg.MoeLayer(*d, k=k, max_tokens=tmax) for d in dev]
+    xs = {t: to_dev(synth.normal_bf16(500 + t, (t, H))) for t in tokens}
+    ys = {t: torch.empty((t, H), dtype=torch.float32, device="cuda:0") for t in tokens}
+    lib = bg.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cargs = [(t, ctypes.c_void_p(xs[t].data_ptr()), ctypes.c_void_p(ys[t].data_ptr())) for t in tokens]
+    hs = [l._h for l in layers]
+    call_no = [0]
+
+    def step(events=None):
+        for j, (t, xp, yp) in enumerate(cargs):
+            h = hs[call_no[0] % 2]
+            call_no[0] += 1
+            if events is not None:
+                events[j][0].record()
+            st = lib.bi_moe_run(h, xp, t, yp, stream)
+            if st != 0:
+                bg.check(st)
+            if events is not None:
+                events[j][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in tokens]
+          for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s_ in range(args.steps):
+        step(ev[s_])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    per_t = {t: float(np.mean([ev[s_][j][0].elapsed_time(ev[s_][j][1]) for s_ in range(args.steps)]))
+             for j, t in enumerate(tokens)}
+
+    # per-step breakdown: the steps called one by one on the same inputs
+    breakdown, layer_flops = [], {}
+    for t in tokens:
+        steps_t, touched = _moe_steps_timed(bg, lib, dev, xs[t], t, args.steps)
+        work = moe_layer_work(t, touched, touched)
+        layer_flops[t] = sum(w[1] for w in work)
+        for (name, fl, by), us in zip(work, steps_t):
+            r = _roof(fl, by, us)
+            breakdown.append({"T": t, "step": name, "us": round(us, 2), "bound": r["bound"],
+                              "achieved": round(r["achieved"], 1), "unit": r["unit"], "frac": round(r["frac"], 3),
+                              "_work": (fl, by), "_us": us})
+    step_flops = sum(layer_flops.values())
+    dom = max(breakdown, key=lambda b: b["_us"])
+    roof = _roof(dom["_work"][0], dom["_work"][1], dom["_us"])
+    t = dom["T"]
+    for b in breakdown:
+        del b["_work"], b["_us"]
+    roof.update({"traffic": None, "kernel": "%s at T=%d" % (dom["step"], t), "launches_per_step": 1,
+                 "avg_launch_us": dom["us"]})
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = moe_layer_cpu_baseline(wr, wu, wd)
+    per = [{"T": t, "us": round(per_t[t] * 1e3, 2), "tflops": round(layer_flops[t] / (per_t[t] * 1e-3) / 1e12, 1),
+            "tokens_per_s": round(t / (per_t[t] * 1e-3), 0)} for t in tokens]
+    out = {
+        "metric": "batch-invariant bf16 GEMM TFLOPS (M sweep) + % MFMA/HBM roofline, 1 GPU",
+        "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; W ~ N(0,%g), x ~ N(0,1); routing computed by the layer)" % MOE["std"],
+        "config": {"workload": "MoE expert layer (Qwen3-30B-A3B-style): router [128,2048], top-8, "
+                               "up [128,1536,2048], SwiGLU, down [128,2048,768], combine; T in {1,16,256,4096}",
+                   "tokens": tokens, "weight_copies_rotated": 2, "kernel_source_sha256_16": kernel_hash()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_T": per,
+        "steps_breakdown": breakdown,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _moe_steps_timed(bg, lib, dev, x, t, reps):
+    """The layer's steps through their own entry points, events around each;
+    mean microseconds per step over `reps` runs alternating the two weight
+    copies, and the number of experts the routing touches."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    E, k, H, I = MOE["experts"], MOE["topk"], MOE["up"][1], MOE["down"][1]
+    r = t * k
+    d = "cuda:0"
+    logits = torch.empty((t, E), dtype=torch.float32, device=d)
+    ids = torch.empty((t, k), dtype=torch.int32, device=d)
+    w = torch.empty((t, k), dtype=torch.float32, device=d)
+    off = torch.empty(E + 1, dtype=torch.int32, device=d)
+    tok = torch.empty(r, dtype=torch.int32, device=d)
+    row_of = torch.empty((t, k), dtype=torch.int32, device=d)
+    xg = torch.empty((r, H), dtype=torch.bfloat16, device=d)
+    h = torch.empty((r, 2 * I), dtype=torch.float32, device=d)
+    a = torch.empty((r, I), dtype=torch.bfloat16, device=d)
+    o = torch.empty((r, H), dtype=torch.float32, device=d)
+    y = torch.empty((t, H), dtype=torch.float32, device=d)
+    P = lambda v: ctypes.c_void_p(v.data_ptr())  # noqa: E731
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    handles = [(bg.Gemm(wr), bg.GroupedGemm(wu), bg.GroupedGemm(wd)) for wr, wu, wd in dev]
+    calls = [
+        lambda g: g[0].run_ptr(x.data_ptr(), t, logits.data_ptr()),
+        lambda g: lib.bi_moe_topk(P(logits), t, E, k, P(ids), P(w), st),
+        lambda g: lib.bi_moe_permute(P(ids), t, E, k, P(off), P(tok), P(row_of), st),
+        lambda g: lib.bi_gather_rows(P(x), t, P(tok), r, H, P(xg), st),
+        lambda g: lib.bi_grouped_gemm_run(g[1]._h, P(xg), P(off), r, P(h), st),
+        lambda g: lib.bi_swiglu(P(h), r, I, P(a), st),
+        lambda g: lib.bi_grouped_gemm_run(g[2]._h, P(a), P(off), r, P(o), st),
+        lambda g: lib.bi_moe_combine(P(o), r, P(ids), P(w), P(row_of), t, k, H, P(y), st),
+    ]
+    for c in calls:
+        bg.check(c(handles[0]) or 0)
+    torch.cuda.synchronize()
+    touched = int(np.count_nonzero(np.diff(off.cpu().numpy())))
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(reps)]
+    for i in range(reps):
+        g = handles[i % len(handles)]
+        for j, c in enumerate(calls):
+            ev[i][j][0].record()
+            bg.check(c(g) or 0)
+            ev[i][j][1].record()
+    torch.cuda.synchronize()
+    us = [float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(reps)])) * 1e3
+          for j in range(len(calls))]
+    return us, touched
+
+
+def moe_layer_cpu_baseline(wr, wu, wd, target_s=15.0):
+    """The oracle's steps of the layer chained on the host cores, on a bounded
+    sample: as many tokens of the T=4096 input as fit in about `target_s`."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    E, k, H, I = MOE["experts"], MOE["topk"], MOE["up"][1], MOE["down"][1]
+    x = synth.normal_bf16(500 + 4096, (4096, H))
+
+    def chain(xb):
+        lg, _ = oracle.gemm_f64(xb, wr)
+        ids, w = oracle.moe_topk(lg.astype(np.float32), k)
+        off, tok, row_of = oracle.moe_permute(ids, E)
+        h, _ = oracle.grouped_f64(xb[tok], wu, off)
+        a = synth.f32_to_bf16_bits(oracle.swiglu_f64(h.astype(np.float32)).astype(np.float32))
+        o, _ = oracle.grouped_f64(a, wd, off)
+        return oracle.moe_combine_f64(o.astype(np.float32), w.astype(np.float32), row_of)[0]
+
+    chain(x[:1])
+    t0 = time.perf_counter()
+    chain(x[:4])
+    probe = max(time.perf_counter() - t0, 1e-3) / 4
+    n = int(max(4, min(4096, target_s / probe)))
+    t0 = time.perf_counter()
+    chain(x[:n])
+    dt = time.perf_counter() - t0
+    fl = n * (2.0 * E * H + 2.0 * k * 2 * I * H + 2.0 * k * H * I)
+    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "fp64 oracle steps of the layer chained on the first %d of the 4096 tokens, %.1f s" % (n, dt)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama8b_down", choices=sorted(WORKLOADS) + ["moe"])
+    ap.add_argument("--workload", default="llama8b_down", choices=sorted(WORKLOADS) + ["moe", "moe_layer"])
     ap.add_argument("--rotate-gib", type=float, default=1.0,
                     help="weight copies to rotate over, in GiB (defeats the Infinity Cache)")
     ap.add_argument("--m", type=str, default=None,
@@ -362,6 +591,8 @@ def main(argv=None):
     bg.load()
     if args.workload == "moe":
         return run_moe(args, bg)
+    if args.workload == "moe_layer":
+        return run_moe_layer(args, bg)
     wl = dict(WORKLOADS[args.workload])
     if args.m:
         wl["ms"] = [int(v) for v in args.m.split(",")]

@@ -19,13 +19,25 @@ namespace bimoe {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Top-k routing: one wave per token.  Lane l holds logits l, l+64, ...; k
-// rounds each take the best logit not yet taken across the wave (a larger
-// logit wins, an equal one goes to the lower expert id).  A NaN logit counts
-// as -inf, so every round takes an expert in 0..E-1.  Lane j keeps round j's
-// choice; the weights are the softmax over the k chosen logits, summed in
-// round order.
+// Top-k routing: one wave per token, lane l holding logits l, l+64, ....
+// Logits (a NaN taken as -inf) become order-preserving 32-bit keys (-0 as
+// +0, so equal floats give equal keys).  A radix select over the key bits,
+// from the top, finds tau, the k-th largest key, with one ballot per logit
+// slot per bit.  The chosen experts are those with a key above tau and,
+// among those with key tau, the ones with the lowest ids (an equal logit
+// goes to the lower expert id).  Each chosen expert's rank (larger logit
+// first, then lower id) is counted against the other chosen ones, and lane
+// j collects the expert of rank j.  The weights are the softmax over the k
+// chosen logits, exp(l_j - l_0) summed in rank order, divided.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    if ((u << 1) == 0)
+        u = 0;  // -0 equals +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 template <int PL>  // logits per lane: E <= 64 * PL
 __global__ void __launch_bounds__(256)
     moe_topk(const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
@@ -36,49 +48,82 @@ __global__ void __launch_bounds__(256)
     if (t >= T)
         return;  // whole waves only: t is the same for all 64 lanes
     float v[PL];
-    unsigned taken = 0;  // bit q: logit lane + 64q has been chosen
+    uint32_t key[PL];  // 0 for slots past E: below every real key
 #pragma unroll
     for (int q = 0; q < PL; ++q) {
         const int e = lane + 64 * q;
-        float x = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+        const float x = e < E ? logits[(size_t)t * E + e] : 0.f;
         v[q] = x == x ? x : -INFINITY;
+        key[q] = e < E ? order_key(v[q]) : 0u;
     }
+    // tau: the largest x with #(key >= x) >= k, built bit by bit
+    uint32_t tau = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = tau | (1u << b);
+        int c = 0;
+#pragma unroll
+        for (int q = 0; q < PL; ++q)
+            c += __popcll(__ballot(key[q] >= cand));
+        if (c >= k)
+            tau = cand;
+    }
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    int greater = 0;
+#pragma unroll
+    for (int q = 0; q < PL; ++q)
+        greater += __popcll(__ballot(key[q] > tau));
+    // among keys equal to tau, the lowest ids: rank by id (q, then lane)
+    bool chosen[PL];
+    int eq_before = 0;
+#pragma unroll
+    for (int q = 0; q < PL; ++q) {
+        const unsigned long long eq = __ballot(key[q] == tau);
+        const int r = eq_before + __popcll(eq & lt);
+        chosen[q] = key[q] > tau || (key[q] == tau && r < k - greater);
+        eq_before += __popcll(eq);
+    }
+    // rank of each chosen expert among the chosen: larger key first, then lower id
+    int rank[PL];
+#pragma unroll
+    for (int q = 0; q < PL; ++q)
+        rank[q] = 0;
+#pragma unroll
+    for (int qc = 0; qc < PL; ++qc) {
+        unsigned long long m = __ballot(chosen[qc]);
+        while (m) {
+            const int lc = __builtin_ctzll(m);
+            m &= m - 1;
+            const uint32_t kc = (uint32_t)__builtin_amdgcn_readlane((int)key[qc], lc);
+            const int ec = lc + 64 * qc;
+#pragma unroll
+            for (int q = 0; q < PL; ++q) {
+                const int e = lane + 64 * q;
+                rank[q] += (kc > key[q] || (kc == key[q] && ec < e)) ? 1 : 0;
+            }
+        }
+    }
+    // lane j takes the expert of rank j
     int my_e = 0;
     float my_v = 0.f;
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
 #pragma unroll
-        for (int q = 0; q < PL; ++q) {
-            const int e = lane + 64 * q;
-            const bool free = e < E && !((taken >> q) & 1u);
-            if (free && (v[q] > bv || (v[q] == bv && e < be))) {
-                bv = v[q];
-                be = e;
+    for (int qc = 0; qc < PL; ++qc) {
+        unsigned long long m = __ballot(chosen[qc]);
+        while (m) {
+            const int lc = __builtin_ctzll(m);
+            m &= m - 1;
+            const int rc = __builtin_amdgcn_readlane(rank[qc], lc);
+            const float vc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[qc]), lc));
+            if (lane == rc) {
+                my_e = lc + 64 * qc;
+                my_v = vc;
             }
-        }
-        // the best (value, id) across the wave
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float ov = __shfl_xor(bv, d, 64);
-            const int oe = __shfl_xor(be, d, 64);
-            if (ov > bv || (ov == bv && oe < be)) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if ((be & 63) == lane)
-            taken |= 1u << (be >> 6);
-        if (lane == j) {
-            my_e = be;
-            my_v = bv;
         }
     }
-    const float top = __shfl(my_v, 0, 64);
+    const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
     const float z = lane < k ? expf(my_v - top) : 0.f;
     float s = 0.f;
     for (int j = 0; j < k; ++j)
-        s = s + __shfl(z, j, 64);
+        s = s + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), j));
     if (lane < k) {
         ids[(size_t)t * k + lane] = my_e;
         w[(size_t)t * k + lane] = z / s;
@@ -86,81 +131,108 @@ __global__ void __launch_bounds__(256)
 }
 
 // ---------------------------------------------------------------------------
-// Grouping by expert: block e places the rows of expert e.  Every block
-// counts all (token, slot) pairs per expert in LDS (integer adds: the count is
-// exact whatever their order), takes its base as the count of the lower
-// experts, and then walks the tokens in ascending order, 256 at a time, with
-// a block-wide exclusive scan giving each pair its row.  Pairs whose id is
-// outside 0..E-1 get row -1 and no row.
+// Grouping by expert.  The flat pair index i = t*k + j is already the stable
+// order, so expert e's rows are its pairs in ascending i.  Block (e, c) owns
+// the pairs of chunk c (lo <= i < hi): one counting pass over all pairs gives
+// the number with an id below e (the expert's first row) and the number
+// equal to e before lo (the chunk's first row within the expert); a second
+// pass walks the chunk 1024 pairs at a time, four consecutive pairs per
+// thread, and ranks the matches with wave ballots and one barrier.  Integer
+// counts only: the rows do not depend on the order the hardware runs in.
+// Pairs whose id is outside 0..E-1 get row -1 (written by the e = 0 blocks
+// of their chunk) and no row.
 // ---------------------------------------------------------------------------
 constexpr int kPermThreads = 256;
+constexpr int kPermWaves = kPermThreads / 64;
+
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1)
+        v += __shfl_xor(v, d, 64);
+    return v;
+}
 
 __global__ void __launch_bounds__(kPermThreads)
-    moe_permute(const int32_t* __restrict__ ids, int T, int E, int k, int32_t* __restrict__ offsets,
-                int32_t* __restrict__ tok, int32_t* __restrict__ row_of)
+    moe_permute(const int32_t* __restrict__ ids, int T, int E, int k, int chunk,
+                int32_t* __restrict__ offsets, int32_t* __restrict__ tok, int32_t* __restrict__ row_of)
 {
-    __shared__ int cnt[kMaxExperts];
-    __shared__ int scan[kPermThreads];
-    const int tid = threadIdx.x;
+    __shared__ int s_red[3][kPermWaves];
+    __shared__ int s_tot[2][kPermWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = blockIdx.x;
     const int n = T * k;
-    for (int i = tid; i < E; i += kPermThreads)
-        cnt[i] = 0;
-    __syncthreads();
+    const int lo = min(n, blockIdx.y * chunk), hi = min(n, lo + chunk);
+
+    // pass 1: counts (every pair for "below e" and "equal to e", the pairs
+    // before lo for "equal to e before the chunk")
+    int below = 0, equal = 0, before = 0;
+#pragma unroll 8
     for (int i = tid; i < n; i += kPermThreads) {
         const int x = ids[i];
-        if (x >= 0 && x < E)
-            atomicAdd(&cnt[x], 1);
+        below += (x >= 0 && x < e);
+        equal += (x == e);
+        before += (x == e && i < lo);
+    }
+    below = wave_sum(below);
+    equal = wave_sum(equal);
+    before = wave_sum(before);
+    if (lane == 0) {
+        s_red[0][wave] = below;
+        s_red[1][wave] = equal;
+        s_red[2][wave] = before;
     }
     __syncthreads();
-    int part = 0;
-    for (int i = tid; i < e; i += kPermThreads)
-        part += cnt[i];
-    scan[tid] = part;
-    __syncthreads();
-    for (int d = kPermThreads / 2; d > 0; d >>= 1) {
-        if (tid < d)
-            scan[tid] += scan[tid + d];
-        __syncthreads();
+    below = equal = before = 0;
+#pragma unroll
+    for (int w = 0; w < kPermWaves; ++w) {
+        below += s_red[0][w];
+        equal += s_red[1][w];
+        before += s_red[2][w];
     }
-    int run = scan[0];
-    if (tid == 0) {
-        offsets[e + 1] = run + cnt[e];
+    if (blockIdx.y == 0 && tid == 0) {
+        offsets[e + 1] = below + equal;
         if (e == 0)
             offsets[0] = 0;
     }
-    if (e == 0)
-        for (int i = tid; i < n; i += kPermThreads) {
-            const int x = ids[i];
-            if (x < 0 || x >= E)
-                row_of[i] = -1;
+
+    // pass 2: place the chunk's pairs of expert e in ascending i
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    int run = below + before;
+    int it = 0;
+    for (int base = lo; base < hi; base += 4 * kPermThreads, ++it) {
+        const int i0 = base + 4 * tid;
+        int v[4];
+        int cnt = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v[q] = (i0 + q < hi) ? ids[i0 + q] : -1;
+            cnt += v[q] == e;
+            if (e == 0 && i0 + q < hi && (v[q] < 0 || v[q] >= E))
+                row_of[i0 + q] = -1;
         }
-    __syncthreads();
-    for (int base = 0; base < T; base += kPermThreads) {
-        const int t = base + tid;
-        int mine = 0;
-        if (t < T)
-            for (int j = 0; j < k; ++j)
-                mine += ids[(size_t)t * k + j] == e;
-        // inclusive scan (Hillis-Steele) of the per-token counts
-        scan[tid] = mine;
+        // exclusive prefix of cnt (0..4) over the wave, from its three bits
+        const unsigned long long b0 = __ballot(cnt & 1), b1 = __ballot(cnt & 2), b2 = __ballot(cnt & 4);
+        const int pre = __popcll(b0 & lt) + 2 * __popcll(b1 & lt) + 4 * __popcll(b2 & lt);
+        if (lane == 0)
+            s_tot[it & 1][wave] = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
         __syncthreads();
-        for (int d = 1; d < kPermThreads; d <<= 1) {
-            const int add = tid >= d ? scan[tid - d] : 0;
-            __syncthreads();
-            scan[tid] += add;
-            __syncthreads();
+        int wbase = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kPermWaves; ++w) {
+            const int c = s_tot[it & 1][w];
+            wbase += w < wave ? c : 0;
+            total += c;
         }
-        int r = run + scan[tid] - mine;
-        if (t < T)
-            for (int j = 0; j < k; ++j)
-                if (ids[(size_t)t * k + j] == e) {
-                    tok[r] = t;
-                    row_of[(size_t)t * k + j] = r;
-                    ++r;
-                }
-        run += scan[kPermThreads - 1];
-        __syncthreads();
+        int r = run + wbase + pre;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (v[q] == e) {
+                tok[r] = (i0 + q) / k;
+                row_of[i0 + q] = r;
+                ++r;
+            }
+        run += total;
     }
 }
 
@@ -223,47 +295,60 @@ __global__ void __launch_bounds__(256)
 // Weighted combine: block t computes y[t] = sum_j w[t][j] * o[row_of[t][j]]
 // over the token's k slots taken in ascending expert id (a slot's position
 // breaks a tie), one fp32 multiply and one fp32 add per slot, in that order.
-// A row outside 0..R-1 contributes nothing.  Four columns per thread.
+// Lanes j < k of the first wave load slot j together and rank it by (id,
+// slot) against the others; the sorted slots go to LDS.  A row outside
+// 0..R-1 contributes nothing.  Four columns per thread.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
     moe_combine(const float* __restrict__ o, int R, const int32_t* __restrict__ ids,
                 const float* __restrict__ w, const int32_t* __restrict__ row_of, int k, int H,
                 float* __restrict__ y)
 {
-    __shared__ int s_e[kMaxTopK];
     __shared__ int s_row[kMaxTopK];
     __shared__ float s_w[kMaxTopK];
     const int t = blockIdx.x;
-    if (threadIdx.x == 0) {
-        for (int j = 0; j < k; ++j) {
-            const int e = ids[(size_t)t * k + j];
-            const int r = row_of[(size_t)t * k + j];
-            const float ww = w[(size_t)t * k + j];
-            int p = j;  // insertion sort by expert id, stable
-            while (p > 0 && s_e[p - 1] > e) {
-                s_e[p] = s_e[p - 1];
-                s_row[p] = s_row[p - 1];
-                s_w[p] = s_w[p - 1];
-                --p;
-            }
-            s_e[p] = e;
-            s_row[p] = r;
-            s_w[p] = ww;
+    if (threadIdx.x < 64) {
+        const int j = threadIdx.x;
+        int e = 0x7fffffff, r = -1;
+        float ww = 0.f;
+        if (j < k) {
+            e = ids[(size_t)t * k + j];
+            r = row_of[(size_t)t * k + j];
+            ww = w[(size_t)t * k + j];
+        }
+        int rank = 0;
+        for (int i = 0; i < k; ++i) {
+            const int ei = __builtin_amdgcn_readlane(e, i);
+            rank += (ei < e || (ei == e && i < j)) ? 1 : 0;
+        }
+        if (j < k) {
+            s_row[rank] = r;
+            s_w[rank] = ww;
         }
     }
     __syncthreads();
     for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
         float4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < k; ++j) {
-            const int r = s_row[j];
-            if (r < 0 || r >= R)
-                continue;
-            const float4 v = *reinterpret_cast<const float4*>(o + (size_t)r * H + c);
-            const float ww = s_w[j];
-            acc.x = acc.x + ww * v.x;
-            acc.y = acc.y + ww * v.y;
-            acc.z = acc.z + ww * v.z;
-            acc.w = acc.w + ww * v.w;
+        // eight slots' rows are loaded before any of them is added
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            float4 v[8];
+            bool ok[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = j0 + u < k ? s_row[j0 + u] : -1;
+                ok[u] = r >= 0 && r < R;
+                v[u] = ok[u] ? *reinterpret_cast<const float4*>(o + (size_t)r * H + c)
+                             : float4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (ok[u]) {
+                    const float ww = s_w[j0 + u];
+                    acc.x = acc.x + ww * v[u].x;
+                    acc.y = acc.y + ww * v[u].y;
+                    acc.z = acc.z + ww * v[u].z;
+                    acc.w = acc.w + ww * v[u].w;
+                }
         }
         *reinterpret_cast<float4*>(y + (size_t)t * H + c) = acc;
     }
@@ -298,8 +383,17 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* tok,
                           int32_t* row_of, hipStream_t stream)
 {
-    hipLaunchKernelGGL(moe_permute, dim3(E), dim3(kPermThreads), 0, stream, ids, T, E, k, offsets,
-                       tok, row_of);
+    // chunks of 8192 pairs, at most 8 per expert: every block reads all the
+    // ids once (E * chunks * T*k reads, served from L2), and places its chunk
+    const long long n = (long long)T * k;
+    const int per = 4 * kPermThreads;
+    long long chunk = 8192;
+    if (n > 8 * chunk)
+        chunk = (n + 7) / 8;
+    chunk = (chunk + per - 1) / per * per;
+    const int chunks = n == 0 ? 1 : (int)((n + chunk - 1) / chunk);
+    hipLaunchKernelGGL(moe_permute, dim3(E, chunks), dim3(kPermThreads), 0, stream, ids, T, E, k,
+                       (int)chunk, offsets, tok, row_of);
     return hipGetLastError();
 }
 
