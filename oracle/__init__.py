@@ -14,6 +14,8 @@ Contents:
 * ``moe_topk``, ``moe_permute``, ``swiglu_f64``, ``moe_combine_f64``
                     the MoE layer's steps around the grouped GEMM: routing,
                     grouping by expert, SwiGLU and the weighted combine;
+* ``rmsnorm_f64``   RMSNorm over the hidden dimension (the step before the
+                    gate+up projection);
 * ``exact``         exact-rational brute force (``oracle/exact.py``).
 
 Each function cites the passage it follows in ``oracle.c``.  Every function is
@@ -72,9 +74,11 @@ def open_library(path: str):
     lib.oracle_moe_permute.argtypes = [P, L, L, L, P, P, P]
     lib.oracle_swiglu_f64.argtypes = [P, L, L, P]
     lib.oracle_moe_combine_f64.argtypes = [P, L, P, P, L, L, L, P, P]
+    lib.oracle_rmsnorm_f64.argtypes = [P, P, L, L, ctypes.c_double, P, P]
     for f in (lib.oracle_gemm_f64, lib.oracle_gemm_i64, lib.oracle_grouped_f64,
               lib.oracle_fold_f32, lib.oracle_max_threads, lib.oracle_moe_topk,
-              lib.oracle_moe_permute, lib.oracle_swiglu_f64, lib.oracle_moe_combine_f64):
+              lib.oracle_moe_permute, lib.oracle_swiglu_f64, lib.oracle_moe_combine_f64,
+              lib.oracle_rmsnorm_f64):
         f.restype = ctypes.c_int
     return lib
 
@@ -252,6 +256,23 @@ def moe_combine_f64(o, w, row_of, lib=None):
     if rc != 0:
         raise ValueError("oracle_moe_combine_f64 rejected its arguments (%d)" % rc)
     return y, s
+
+
+def rmsnorm_f64(x_bits, g_bits, eps: float, lib=None):
+    """``x * g / sqrt(mean(x^2) + eps)`` per row in fp64, and the rows' mean
+    squares: ``(y [T,H] float64, ms [T] float64)``."""
+    x = _u16(x_bits, 2)
+    g = _u16(g_bits, 1)
+    t, h = x.shape
+    if g.shape != (h,):
+        raise ValueError("gain must be [H]")
+    y = np.empty((t, h), np.float64)
+    ms = np.empty(t, np.float64)
+    rc = _load(lib).oracle_rmsnorm_f64(x.ctypes.data, g.ctypes.data, t, h, float(eps), y.ctypes.data,
+                                    ms.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_rmsnorm_f64 rejected its arguments (%d)" % rc)
+    return y, ms
 
 
 def within_bound(y_gpu, y_ref, a, rel: float = 1e-4):

@@ -337,3 +337,36 @@ int oracle_moe_combine_f64(const float *o, long R, const float *w, const int32_t
         }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * RMSNorm, the step before the gate+up projection.  A token-wise reduction
+ * over the hidden dimension whose stock kernels split a row across blocks
+ * when the batch is small, so the tree (and the bits) follow the batch
+ * (CoRun, §III-A Fig. 3; the pages measure batch-invariant RMSNorm against
+ * stock kernels in CoRun §II Fig. 2a and LLM-42 notes §2.3 Fig. 4b).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * y[t][h] = x[t][h] * g[h] / sqrt(ms[t] + eps), ms[t] = (1/H) sum_h x[t][h]^2,
+ * in fp64 over bf16 inputs (each square is exact in fp64; the H-term sum of
+ * non-negative terms is within (H-1) * 2^-53 of its value, relatively).  ms
+ * is returned too.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_rmsnorm_f64(const uint16_t *x, const uint16_t *g, long T, long H, double eps, double *y,
+                       double *ms)
+{
+    if (!x || !g || !y || !ms || T < 0 || H <= 0 || !(eps >= 0.0))
+        return -1;
+    for (long t = 0; t < T; ++t) {
+        double s = 0.0;
+        for (long h = 0; h < H; ++h) {
+            double v = bf16_to_f64(x[t * H + h]);
+            s += v * v;
+        }
+        ms[t] = s / (double)H;
+        double inv = 1.0 / sqrt(ms[t] + eps);
+        for (long h = 0; h < H; ++h)
+            y[t * H + h] = bf16_to_f64(x[t * H + h]) * bf16_to_f64(g[h]) * inv;
+    }
+    return 0;
+}

@@ -290,6 +290,47 @@ def pin_moe_combine(lib=None):
     assert np.array_equal(y1, o[row_of[:, 0]].astype(np.float64))
 
 
+def pin_rmsnorm(lib=None):
+    """RMSNorm against closed forms, scale invariance, exact rational sums of
+    squares and numpy's fp64 formula."""
+    h = 64
+    one = synth.f32_to_bf16_bits(np.ones(h, np.float32))
+    # a constant row c: ms = c^2, y = g * c / sqrt(c^2 + eps); with eps = 0 it is g * sign(c)
+    for c in (3.0, -0.5, 2.0 ** -20):
+        x = synth.f32_to_bf16_bits(np.full((1, h), c, np.float32))
+        y, ms = oracle.rmsnorm_f64(x, one, 0.0, lib=lib)
+        assert ms[0] == c * c and np.all(y == np.sign(c)), (c, y[0, :3])
+        y, _ = oracle.rmsnorm_f64(x, one, 1e-5, lib=lib)
+        assert np.allclose(y, c / np.sqrt(c * c + 1e-5), rtol=1e-15, atol=0)
+    # one nonzero entry v at k: ms = v^2 / H, y[k] = g[k] * sqrt(H) * sign(v), others 0
+    g = synth.normal_bf16(950, (h,), 1.0)
+    gf = synth.bf16_bits_to_f32(g).astype(np.float64)
+    x = np.zeros((1, h), np.uint16)
+    x[0, 5] = synth.f32_to_bf16_bits(np.array([-0.75], np.float32))[0]
+    y, ms = oracle.rmsnorm_f64(x, g, 0.0, lib=lib)
+    assert ms[0] == 0.5625 / h
+    assert abs(y[0, 5] / (-gf[5] * np.sqrt(h)) - 1) < 1e-15 and np.all(np.delete(y[0], 5) == 0)
+    # scaling a row by a power of two changes nothing when eps = 0
+    x = synth.normal_bf16(951, (4, h))
+    xs = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(x) * np.float32(8.0))
+    y1, _ = oracle.rmsnorm_f64(x, g, 0.0, lib=lib)
+    y2, _ = oracle.rmsnorm_f64(xs, g, 0.0, lib=lib)
+    assert np.array_equal(y1, y2)
+    # the mean of squares against exact rationals
+    x = synth.normal_bf16(952, (3, 40))
+    _, ms = oracle.rmsnorm_f64(x, synth.f32_to_bf16_bits(np.ones(40, np.float32)), 0.0, lib=lib)
+    for t in range(3):
+        exact = sum(Fraction(float(v)) ** 2 for v in synth.bf16_bits_to_f32(x[t])) / 40
+        assert abs(Fraction(ms[t]) - exact) <= exact * Fraction(1, 2 ** 50)
+    # numpy's fp64 formula, an independent library routine
+    x = synth.normal_bf16(953, (7, 96), 3.0)
+    g = synth.normal_bf16(954, (96,), 0.3)
+    y, _ = oracle.rmsnorm_f64(x, g, 1e-6, lib=lib)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    want = xf * synth.bf16_bits_to_f32(g).astype(np.float64) / np.sqrt(np.mean(xf * xf, axis=1, keepdims=True) + 1e-6)
+    assert np.allclose(y, want, rtol=1e-14, atol=0)
+
+
 ALL_PINS = [
     pin_exact_rationals,
     pin_golden_gemm,
@@ -304,4 +345,5 @@ ALL_PINS = [
     pin_moe_permute,
     pin_swiglu,
     pin_moe_combine,
+    pin_rmsnorm,
 ]

@@ -41,6 +41,10 @@ MUTANTS = [
     ("combine_drops_last_expert", "for (long j = 0; j < k; ++j) {\n                double p = (double)w",
      "for (long j = 0; j < k - 1; ++j) {\n                double p = (double)w", 0),
     ("combine_ignores_weight", "double p = (double)w[t * k + j] * ", "double p = 1.0 * ", 0),
+    ("rmsnorm_no_eps", "double inv = 1.0 / sqrt(ms[t] + eps);", "double inv = 1.0 / sqrt(ms[t]);", 0),
+    ("rmsnorm_sum_not_mean", "ms[t] = s / (double)H;", "ms[t] = s;", 0),
+    ("rmsnorm_no_gain", "y[t * H + h] = bf16_to_f64(x[t * H + h]) * bf16_to_f64(g[h]) * inv;",
+     "y[t * H + h] = bf16_to_f64(x[t * H + h]) * inv;", 0),
 ]
 
 
