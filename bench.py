@@ -557,12 +557,123 @@ def moe_layer_cpu_baseline(wr, wu, wd, target_s=15.0):
             "sample": "fp64 oracle steps of the layer chained on the first %d of the 4096 tokens, %.1f s" % (n, dt)}
 
 
+def run_norm_gate_up(args, bg):
+    """One step = at every M of the gate+up sweep, RMSNorm of the raw hidden
+    rows (bf16 [M, 4096], rows at scales 2^-4 .. 2^4, gain near 1) followed
+    by the gate+up projection of the normalised rows (W bf16 [28672, 4096]),
+    weights rotating over copies as in the dense sweep.  Reports the GEMM
+    throughput of the pair (TFLOPS), and the norm's own time and HBM rate."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import synth
+
+    wl = WORKLOADS["llama8b_gate_up"]
+    n, k, ms = wl["n"], wl["k"], list(wl["ms"])
+    if args.m:
+        ms = [int(v) for v in args.m.split(",")]
+    mmax = max(ms)
+    w0 = to_dev(synth.normal_bf16(42, (n, k), wl["std"]))
+    copies = max(1, int(np.ceil(args.rotate_gib * 2 ** 30 / (2 * n * k))))
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+    handles = [bg.Gemm(w) for w in ws]
+    raw = synth.normal_bf16(43, (mmax, k))
+    scale = np.exp2(synth.rng(44).integers(-4, 5, size=(mmax, 1))).astype(np.float32)
+    xraw = to_dev(synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(raw) * scale))
+    gain = to_dev(synth.f32_to_bf16_bits((1.0 + synth.bf16_bits_to_f32(synth.normal_bf16(45, (k,), 0.1))).astype(np.float32)))
+    xn = torch.empty((mmax, k), dtype=torch.bfloat16, device="cuda:0")
+    ys = {m: torch.empty((m, n), dtype=torch.float32, device="cuda:0") for m in ms}
+    lib = bg.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    hps = [h._h for h in handles]
+    call_no = [0]
+
+    def step(events=None):
+        for j, m in enumerate(ms):
+            h = hps[call_no[0] % copies]
+            call_no[0] += 1
+            if events is not None:
+                events[j][0].record()
+            st = lib.bi_rmsnorm(P(xraw), P(gain), m, k, ctypes.c_float(1e-5), P(xn), stream)
+            if st != 0:
+                bg.check(st)
+            if events is not None:
+                events[j][1].record()
+            st = lib.bi_gemm_run(h, P(xn), m, P(ys[m]), stream)
+            if st != 0:
+                bg.check(st)
+            if events is not None:
+                events[j][2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in ms] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s_ in range(args.steps):
+        step(ev[s_])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    norm_us = {m: 1e3 * float(np.mean([ev[s_][j][0].elapsed_time(ev[s_][j][1]) for s_ in range(args.steps)]))
+               for j, m in enumerate(ms)}
+    gemm_us = {m: 1e3 * float(np.mean([ev[s_][j][1].elapsed_time(ev[s_][j][2]) for s_ in range(args.steps)]))
+               for j, m in enumerate(ms)}
+    flops = {m: 2.0 * m * n * k for m in ms}
+    norm_bytes = {m: 4.0 * m * k + 2.0 * k for m in ms}
+    names = {m: handles[0].kernel_name(m) for m in ms}
+    # dominant kernel: the GEMM kernel with the most time per step
+    by_kernel = {}
+    for m in ms:
+        d = by_kernel.setdefault(names[m], [0.0, 0.0, 0.0, 0])
+        d[0] += gemm_us[m]
+        d[1] += flops[m]
+        d[2] += 2.0 * n * k + 2.0 * m * k + 4.0 * m * n
+        d[3] += 1
+    dom = max(by_kernel, key=lambda kn: by_kernel[kn][0])
+    us, fl, by, launches = by_kernel[dom]
+    roof = _roof(fl, by, us)
+    roof.update({"traffic": None, "kernel": dom, "launches_per_step": launches, "avg_launch_us": us / launches})
+    norm_total_us = sum(norm_us.values())
+    norm_roof = _roof(0.0, sum(norm_bytes.values()), norm_total_us)
+    per = [{"M": m, "norm_us": round(norm_us[m], 2), "norm_gbs": round(norm_bytes[m] / (norm_us[m] * 1e-6) / 1e9, 0),
+            "gemm_us": round(gemm_us[m], 2), "gemm_kernel": names[m],
+            "gemm_tflops": round(flops[m] / (gemm_us[m] * 1e-6) / 1e12, 1)} for m in ms]
+    out = {
+        "metric": "batch-invariant bf16 GEMM TFLOPS (M sweep) + % MFMA/HBM roofline, 1 GPU",
+        "value": round(sum(flops.values()) / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; W ~ N(0,%g), raw rows N(0,1) at scales 2^-4..2^4, gain ~ 1+N(0,0.1))" % wl["std"],
+        "config": {"workload": "Llama-3.1-8B RMSNorm (H=4096, eps 1e-5) then fused gate+up GEMM, "
+                               "W bf16 [28672,4096], M in {32,544,2080,8224}",
+                   "m_sweep": ms, "weight_copies_rotated": copies, "kernel_source_sha256_16": kernel_hash()},
+        "roofline": roof,
+        "norm_roofline": dict(norm_roof, kernel="rmsnorm_rows", share_of_step=round(norm_total_us / (ms_per_step * 1e3), 4)),
+        "cpu_baseline": None,
+        "per_m": per,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama8b_down", choices=sorted(WORKLOADS) + ["moe", "moe_layer"])
+    ap.add_argument("--workload", default="llama8b_down", choices=sorted(WORKLOADS) + ["moe", "moe_layer", "norm_gate_up"])
     ap.add_argument("--rotate-gib", type=float, default=1.0,
                     help="weight copies to rotate over, in GiB (defeats the Infinity Cache)")
     ap.add_argument("--m", type=str, default=None,
@@ -593,6 +704,8 @@ def main(argv=None):
         return run_moe(args, bg)
     if args.workload == "moe_layer":
         return run_moe_layer(args, bg)
+    if args.workload == "norm_gate_up":
+        return run_norm_gate_up(args, bg)
     wl = dict(WORKLOADS[args.workload])
     if args.m:
         wl["ms"] = [int(v) for v in args.m.split(",")]

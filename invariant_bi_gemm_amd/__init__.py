@@ -3,8 +3,9 @@
 ``y = x @ W.T`` in fp32 with bits of every row independent of the batch:
 row count, row position and the other rows never change a row's result.
 The compute runs in the hand-written HIP library ``libbigemm.so`` (C ABI in
-``include/bi_gemm.h``, and ``include/bi_moe.h`` for the MoE expert layer built
-around the grouped GEMM); this package is its thin Python binding.
+``include/bi_gemm.h``; ``include/bi_moe.h`` for the MoE expert layer built
+around the grouped GEMM; ``include/bi_norm.h`` for the RMSNorm before a
+projection); this package is its thin Python binding.
 """
 from ._lib import (  # noqa: F401
     LIB_PATH,
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     moe_combine,
     moe_permute,
     moe_topk,
+    rmsnorm,
     status_string,
     swiglu,
 )

@@ -1,4 +1,5 @@
-"""ctypes binding of the C ABI declared in include/bi_gemm.h and include/bi_moe.h.
+"""ctypes binding of the C ABI declared in include/bi_gemm.h, include/bi_moe.h
+and include/bi_norm.h.
 
 Argument marshalling only: every step of the GEMM runs in the HIP library
 ``libbigemm.so``.  Tensors are PyTorch device tensors (PyTorch provides device
@@ -74,6 +75,7 @@ def _declare(lib):
         "bi_moe_create": ([I, I, I, I, P, P, P, I, ctypes.POINTER(P)], S),
         "bi_moe_run": ([P, P, I, P, P], S),
         "bi_moe_destroy": ([P], None),
+        "bi_rmsnorm": ([P, P, I, I, ctypes.c_float, P, P], S),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -390,3 +392,26 @@ class MoeLayer:
             self.close()
         except Exception:  # noqa: BLE001
             pass
+
+
+# ---- RMSNorm (include/bi_norm.h) -----------------------------------------------
+
+def rmsnorm(x, gain, eps: float = 1e-5, out=None, stream=None):
+    """bf16 ``x * gain / sqrt(mean(x^2) + eps)`` per row of a bf16 [T, H]
+    tensor, each row reduced by a tree fixed by H alone."""
+    import torch
+
+    lib = load()
+    _need(x, torch.bfloat16, 2, "x")
+    _need(gain, torch.bfloat16, 1, "gain")
+    t, h = (int(v) for v in x.shape)
+    if int(gain.shape[0]) != h:
+        raise ValueError("gain must have H = %d entries" % h)
+    if out is None:
+        out = torch.empty((t, h), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, torch.bfloat16, 2, "out")
+        if tuple(out.shape) != (t, h):
+            raise ValueError("out must be [%d, %d]" % (t, h))
+    check(lib.bi_rmsnorm(_p(x), _p(gain), t, h, float(eps), _p(out), _stream_ptr(stream)))
+    return out

@@ -13,6 +13,7 @@
 
 #include <math.h>
 
+#include "bf16_round.h"
 #include "moe_internal.h"
 
 namespace bimoe {
@@ -253,15 +254,6 @@ __global__ void __launch_bounds__(256)
     }
 }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t to_bf16(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (uint16_t)((u >> 16) | 0x40u);
-    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-
 // ---------------------------------------------------------------------------
 // SwiGLU: a[r][i] = bf16(g / (1 + exp(-g)) * u), g = h[r][i], u = h[r][I+i],
 // four columns per thread (I is a multiple of 4).
@@ -282,7 +274,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float sg = gg[j] / (1.0f + expf(-gg[j]));
-            out[j] = to_bf16(sg * uu[j]);
+            out[j] = bi::to_bf16(sg * uu[j]);
         }
         uint2 packed;
         packed.x = (uint32_t)out[0] | ((uint32_t)out[1] << 16);

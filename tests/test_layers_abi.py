@@ -1,4 +1,4 @@
-"""The MoE layer's C ABI on the host, without a GPU: every entry point rejects
+"""The MoE layer's and RMSNorm's C ABI on the host, without a GPU: every entry point rejects
 bad sizes, NULL and misaligned pointers, and bad handles before any HIP call,
 and empty calls return without one (not gpu)."""
 import ctypes
@@ -124,3 +124,24 @@ def test_layer_run_rejects_bad_handles(lib):
     assert lib.bi_moe_run(ctypes.cast(bogus, P), A, 1, A, None) == INV
     lib.bi_moe_destroy(None)
     lib.bi_moe_destroy(ctypes.cast(bogus, P))
+
+
+@pytest.mark.parametrize("args,want", [
+    ((A, A, 4, 4, 1e-5, A), INV),        # H below 8
+    ((A, A, 4, 100, 1e-5, A), INV),      # H not a multiple of 8
+    ((A, A, 4, 65544, 1e-5, A), INV),    # H above 65536
+    ((A, A, -1, 64, 1e-5, A), INV),      # T < 0
+    ((A, A, 1 << 20, 4096, 1e-5, A), INV),  # T*H >= 2^31
+    ((A, A, 4, 64, -1.0, A), INV),       # eps < 0
+    ((A, A, 4, 64, float("inf"), A), INV),  # eps not finite
+    ((A, None, 4, 64, 1e-5, A), INV),    # gain NULL
+    ((A4, A, 4, 64, 1e-5, P(1 << 20)), MIS),  # x not 16-byte aligned
+    ((A, A, 4, 64, 1e-5, P(4096 + 64)), INV),  # y overlaps x
+])
+def test_rmsnorm_rejects(lib, args, want):
+    assert lib.bi_rmsnorm(*args, None) == want
+    assert lib.bi_last_error().decode()
+
+
+def test_rmsnorm_empty_launches_nothing(lib):
+    assert lib.bi_rmsnorm(None, None, 0, 4096, 1e-5, None, None) == 0
