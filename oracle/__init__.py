@@ -16,6 +16,8 @@ Contents:
                     grouping by expert, SwiGLU and the weighted combine;
 * ``rmsnorm_f64``   RMSNorm over the hidden dimension (the step before the
                     gate+up projection);
+* ``decode_attn_f64`` decode attention of one query token per sequence against
+                    its KV cache (grouped-query heads), by the definition;
 * ``exact``         exact-rational brute force (``oracle/exact.py``).
 
 Each function cites the passage it follows in ``oracle.c``.  Every function is
@@ -75,10 +77,11 @@ def open_library(path: str):
     lib.oracle_swiglu_f64.argtypes = [P, L, L, P]
     lib.oracle_moe_combine_f64.argtypes = [P, L, P, P, L, L, L, P, P]
     lib.oracle_rmsnorm_f64.argtypes = [P, P, L, L, ctypes.c_double, P, P]
+    lib.oracle_decode_attn_f64.argtypes = [P, P, P, P, L, L, L, L, L, ctypes.c_double, P, P, P]
     for f in (lib.oracle_gemm_f64, lib.oracle_gemm_i64, lib.oracle_grouped_f64,
               lib.oracle_fold_f32, lib.oracle_max_threads, lib.oracle_moe_topk,
               lib.oracle_moe_permute, lib.oracle_swiglu_f64, lib.oracle_moe_combine_f64,
-              lib.oracle_rmsnorm_f64):
+              lib.oracle_rmsnorm_f64, lib.oracle_decode_attn_f64):
         f.restype = ctypes.c_int
     return lib
 
@@ -273,6 +276,30 @@ def rmsnorm_f64(x_bits, g_bits, eps: float, lib=None):
     if rc != 0:
         raise ValueError("oracle_rmsnorm_f64 rejected its arguments (%d)" % rc)
     return y, ms
+
+
+def decode_attn_f64(q_bits, k_bits, v_bits, seq_start, scale: float, lib=None):
+    """Decode attention by the definition in fp64.  ``q_bits`` [B, Hq, D],
+    ``k_bits`` and ``v_bits`` [Ntok, Hkv, D] (bf16 bits), ``seq_start``
+    [B+1] int32.  Returns ``(out [B,Hq,D], mag [B,Hq,D], qk [B,Hq])``: the
+    output, sum_t p_t |v_t| and the largest scale * sum |q k| over the keys."""
+    q = _u16(q_bits, 3)
+    k = _u16(k_bits, 3)
+    v = _u16(v_bits, 3)
+    st = np.ascontiguousarray(seq_start, dtype=np.int32)
+    b, hq, d = q.shape
+    ntok, hkv, d2 = k.shape
+    if v.shape != k.shape or d2 != d or st.shape != (b + 1,):
+        raise ValueError("shape mismatch")
+    out = np.empty((b, hq, d), np.float64)
+    mag = np.empty((b, hq, d), np.float64)
+    qk = np.empty((b, hq), np.float64)
+    rc = _load(lib).oracle_decode_attn_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, st.ctypes.data, b, hq,
+                                        hkv, d, ntok, float(scale), out.ctypes.data, mag.ctypes.data,
+                                        qk.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_decode_attn_f64 rejected its arguments (%d)" % rc)
+    return out, mag, qk
 
 
 def within_bound(y_gpu, y_ref, a, rel: float = 1e-4):

@@ -370,3 +370,88 @@ int oracle_rmsnorm_f64(const uint16_t *x, const uint16_t *g, long T, long H, dou
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Decode attention: one new query token per sequence against its KV cache.
+ * Split-KV kernels partition a sequence's keys across blocks when the batch
+ * is small; batch invariance needs split boundaries that do not depend on
+ * the batch -- a fixed split size (Detent, §8.1 Kernels: a rebuilt FA3 that
+ * keeps split-KV with the fixed split-size principle; CoRun, §IV-C and
+ * §V-F: Split-KV turned off for decode instead).  The oracle is the
+ * definition, with no split at all.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * For sequence b (keys seq_start[b] .. seq_start[b+1]-1 of the cache) and
+ * query head h (kv head h / (Hq / Hkv)), in fp64:
+ *   s_t = scale * sum_i q[b][h][i] * k[t][kvh][i]
+ *   p_t = exp(s_t - max_u s_u) / sum_u exp(s_u - max_u s_u)
+ *   out[b][h][i] = sum_t p_t * v[t][kvh][i]
+ * and, for the accuracy bound, mag[b][h][i] = sum_t p_t |v[t][kvh][i]| and
+ * qk[b][h] = max_t scale * sum_i |q[b][h][i] * k[t][kvh][i]|.  q: bf16
+ * [B, Hq, D]; k, v: bf16 [Ntok, Hkv, D]; a sequence with no keys gives
+ * out = mag = qk = 0.  Returns 0, or -1 on a bad argument (Hq not a multiple
+ * of Hkv, offsets outside 0..Ntok or decreasing).
+ */
+int oracle_decode_attn_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const int32_t *seq_start, long B, long Hq, long Hkv, long D, long Ntok,
+                           double scale, double *out, double *mag, double *qk)
+{
+    if (!q || !k || !v || !seq_start || !out || !mag || !qk || B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 ||
+        Hq % Hkv != 0 || Ntok < 0)
+        return -1;
+    for (long b = 0; b < B; ++b)
+        if (seq_start[b] < 0 || seq_start[b + 1] < seq_start[b] || seq_start[b + 1] > Ntok)
+            return -1;
+    const long G = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic)
+    for (long bh = 0; bh < B * Hq; ++bh) {
+        const long b = bh / Hq, h = bh % Hq, kvh = h / G;
+        const long t0 = seq_start[b], n = seq_start[b + 1] - t0;
+        const uint16_t *qv = q + (b * Hq + h) * D;
+        double *o = out + (b * Hq + h) * D;
+        double *mg = mag + (b * Hq + h) * D;
+        for (long i = 0; i < D; ++i)
+            o[i] = mg[i] = 0.0;
+        qk[bh] = 0.0;
+        if (n == 0)
+            continue;
+        double smax = -INFINITY, amax = 0.0;
+        for (long t = 0; t < n; ++t) {
+            const uint16_t *kt = k + ((t0 + t) * Hkv + kvh) * D;
+            double s = 0.0, a = 0.0;
+            for (long i = 0; i < D; ++i) {
+                double p = bf16_to_f64(qv[i]) * bf16_to_f64(kt[i]);
+                s += p;
+                a += fabs(p);
+            }
+            s *= scale;
+            a *= fabs(scale);
+            if (s > smax)
+                smax = s;
+            if (a > amax)
+                amax = a;
+        }
+        qk[bh] = amax;
+        double den = 0.0;
+        for (long t = 0; t < n; ++t) {
+            const uint16_t *kt = k + ((t0 + t) * Hkv + kvh) * D;
+            const uint16_t *vt = v + ((t0 + t) * Hkv + kvh) * D;
+            double s = 0.0;
+            for (long i = 0; i < D; ++i)
+                s += bf16_to_f64(qv[i]) * bf16_to_f64(kt[i]);
+            const double e = exp(s * scale - smax);
+            den += e;
+            for (long i = 0; i < D; ++i) {
+                const double vi = bf16_to_f64(vt[i]);
+                o[i] += e * vi;
+                mg[i] += e * fabs(vi);
+            }
+        }
+        for (long i = 0; i < D; ++i) {
+            o[i] /= den;
+            mg[i] /= den;
+        }
+    }
+    return 0;
+}

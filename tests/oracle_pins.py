@@ -331,6 +331,67 @@ def pin_rmsnorm(lib=None):
     assert np.allclose(y, want, rtol=1e-14, atol=0)
 
 
+def pin_decode_attn(lib=None):
+    """Decode attention against closed forms (one key; equal keys or q = 0
+    give the mean of the values; one dominant key), the grouped-head mapping,
+    scipy's softmax and key-order invariance."""
+    from scipy.special import softmax
+
+    f = lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)  # noqa: E731
+    b16 = lambda a: synth.f32_to_bf16_bits(np.asarray(a, np.float32))  # noqa: E731
+    d = 16
+    # one key: the output is its value; an empty sequence gives zeros
+    q = synth.normal_bf16(960, (2, 4, d))
+    k = synth.normal_bf16(961, (1, 2, d))
+    v = synth.normal_bf16(962, (1, 2, d))
+    o, mg, _ = oracle.decode_attn_f64(q, k, v, np.array([0, 1, 1], np.int32), 0.25, lib=lib)
+    for h in range(4):
+        assert np.array_equal(o[0, h], f(v[0, h // 2])) and np.array_equal(mg[0, h], np.abs(f(v[0, h // 2])))
+    assert np.all(o[1] == 0)
+    # equal keys, or q = 0: every weight 1/n, the output is the mean of the values
+    n = 8
+    v = synth.normal_bf16(963, (n, 1, d))
+    keq = np.repeat(synth.normal_bf16(964, (1, 1, d)), n, axis=0)
+    qz = np.zeros((1, 2, d), np.uint16)
+    want = np.array([float(sum(Fraction(float(x)) for x in f(v[:, 0, i])) / n) for i in range(d)])
+    for qq, kk in ((synth.normal_bf16(965, (1, 2, d)), keq), (qz, synth.normal_bf16(966, (n, 1, d)))):
+        o, _, _ = oracle.decode_attn_f64(qq, kk, v, np.array([0, n], np.int32), 0.5, lib=lib)
+        assert np.allclose(o[0, 0], want, rtol=0, atol=1e-15) and np.allclose(o[0, 1], want, rtol=0, atol=1e-15)
+    # one dominant key: its score exceeds the others' by 200, so the output is its value
+    k = np.zeros((n, 1, d), np.uint16)
+    k[3, 0, 0] = b16([200.0])[0]
+    q = np.zeros((1, 1, d), np.uint16)
+    q[0, 0, 0] = b16([1.0])[0]
+    o, _, qk = oracle.decode_attn_f64(q, k, v, np.array([0, n], np.int32), 1.0, lib=lib)
+    assert np.allclose(o[0, 0], f(v[3, 0]), rtol=1e-12, atol=1e-80) and qk[0, 0] == 200.0
+    # grouped heads: query head h reads kv head h // (Hq / Hkv); values constant per kv head
+    hq, hkv, n = 8, 4, 5
+    v = np.stack([b16(np.full((hkv, d), 0.0) + np.arange(hkv)[:, None] + 1) for _ in range(n)])
+    k = synth.normal_bf16(967, (n, hkv, d))
+    q = synth.normal_bf16(968, (1, hq, d))
+    o, _, _ = oracle.decode_attn_f64(q, k, v, np.array([0, n], np.int32), 0.25, lib=lib)
+    for h in range(hq):
+        assert np.allclose(o[0, h], h // 2 + 1, rtol=1e-15, atol=0), h
+    # scipy's softmax, ragged sequences; and key order does not matter
+    hq, hkv, d = 6, 2, 32
+    st = np.array([0, 7, 7, 20, 21], np.int32)
+    q = synth.normal_bf16(969, (4, hq, d))
+    k = synth.normal_bf16(970, (21, hkv, d), 2.0)
+    v = synth.normal_bf16(971, (21, hkv, d))
+    sc = 1.0 / np.sqrt(d)
+    o, _, _ = oracle.decode_attn_f64(q, k, v, st, sc, lib=lib)
+    for b in range(4):
+        for h in range(hq):
+            ks, vs = f(k[st[b]:st[b + 1], h // 3]), f(v[st[b]:st[b + 1], h // 3])
+            if len(ks) == 0:
+                assert np.all(o[b, h] == 0)
+                continue
+            assert np.allclose(o[b, h], softmax(sc * (ks @ f(q[b, h]))) @ vs, rtol=1e-13, atol=1e-15)
+    perm = np.concatenate([np.arange(7), 7 + synth.rng(972).permutation(13), [20]])
+    o2, _, _ = oracle.decode_attn_f64(q, k[perm], v[perm], st, sc, lib=lib)
+    assert np.allclose(o, o2, rtol=1e-13, atol=1e-15)
+
+
 ALL_PINS = [
     pin_exact_rationals,
     pin_golden_gemm,
@@ -346,4 +407,5 @@ ALL_PINS = [
     pin_swiglu,
     pin_moe_combine,
     pin_rmsnorm,
+    pin_decode_attn,
 ]

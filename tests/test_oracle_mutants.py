@@ -45,6 +45,11 @@ MUTANTS = [
     ("rmsnorm_sum_not_mean", "ms[t] = s / (double)H;", "ms[t] = s;", 0),
     ("rmsnorm_no_gain", "y[t * H + h] = bf16_to_f64(x[t * H + h]) * bf16_to_f64(g[h]) * inv;",
      "y[t * H + h] = bf16_to_f64(x[t * H + h]) * inv;", 0),
+    ("attn_kv_head_modulo", "kvh = h / G;", "kvh = h % Hkv;", 0),
+    ("attn_no_scale", "const double e = exp(s * scale - smax);", "const double e = exp(s - smax);", 0),
+    ("attn_drops_last_key", "n = seq_start[b + 1] - t0;", "n = seq_start[b + 1] - t0 - (seq_start[b + 1] > t0);", 0),
+    ("attn_values_from_keys", "const uint16_t *vt = v + ((t0 + t) * Hkv + kvh) * D;",
+     "const uint16_t *vt = k + ((t0 + t) * Hkv + kvh) * D;", 0),
 ]
 
 
