@@ -668,12 +668,137 @@ def run_norm_gate_up(args, bg):
     return 0
 
 
+ATTN = dict(batch=256, hq=32, hkv=8, d=128, split=512, splits_tried=[256, 512, 1024, 2048], median=1024.0,
+            sigma=0.8, lo=16, hi=8192, pool=32768)
+
+
+def run_decode_attn(args, bg):
+    """One step = one decode-attention call over a Llama-3.1-8B decode batch:
+    256 sequences (a decode batch of CoRun's size) with ragged KV lengths
+    (lognormal, median 1024, clipped to 16 .. 8192), 32 query heads, 8 kv
+    heads, head dim 128, split size 512.  The KV cache is bf16, token-major;
+    its values come from a seeded pool of 32768 token rows repeated to the
+    batch's length (values do not change the work).  Roofline: HBM, with the
+    keys, values, queries and outputs as the algorithmic bytes."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import synth
+
+    a = ATTN
+    lengths = synth.decode_lengths(800, a["batch"], a["median"], a["sigma"], a["lo"], a["hi"])
+    st = np.zeros(a["batch"] + 1, np.int32)
+    st[1:] = np.cumsum(lengths)
+    ntok = int(st[-1])
+    row = a["hkv"] * a["d"]
+    pool_k = to_dev(synth.normal_bf16(801, (a["pool"], row)))
+    pool_v = to_dev(synth.normal_bf16(802, (a["pool"], row)))
+    reps = (ntok + a["pool"] - 1) // a["pool"]
+    k = pool_k.repeat(reps, 1)[:ntok].reshape(ntok, a["hkv"], a["d"]).contiguous()
+    v = pool_v.repeat(reps, 1)[:ntok].reshape(ntok, a["hkv"], a["d"]).contiguous()
+    del pool_k, pool_v
+    q = to_dev(synth.normal_bf16(803, (a["batch"], a["hq"], a["d"])))
+    std = torch.as_tensor(st, device="cuda:0")
+    out = torch.empty((a["batch"], a["hq"], a["d"]), dtype=torch.float32, device="cuda:0")
+    scale = 1.0 / np.sqrt(a["d"])
+    kv_bytes = 2.0 * 2 * ntok * row
+    alg_bytes = kv_bytes + 2.0 * q.numel() + 4.0 * out.numel()
+    flops = 4.0 * float(lengths.sum()) * a["hq"] * a["d"]
+    lib = bg.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def timed(split, steps, warmup):
+        att = bg.DecodeAttention(a["hq"], a["hkv"], split, a["batch"], a["hi"])
+        args_ = (att._h, P(q), P(k), P(v), P(std), a["batch"], ntok, ctypes.c_float(scale), P(out), stream)
+        for _ in range(warmup):
+            bg.check(lib.bi_attn_decode(*args_))
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for e0, e1 in ev:
+            e0.record()
+            st_ = lib.bi_attn_decode(*args_)
+            if st_ != 0:
+                bg.check(st_)
+            e1.record()
+        t1.record()
+        torch.cuda.synchronize()
+        att.close()
+        return t0.elapsed_time(t1) / steps, float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+    sweep = {}
+    for split in a["splits_tried"]:
+        if split != a["split"]:
+            sweep[split] = round(timed(split, 5, 2)[1] * 1e3, 2)
+    ms_per_step, per_call = timed(a["split"], args.steps, args.warmup)
+    sweep[a["split"]] = round(per_call * 1e3, 2)
+    roof = _roof(0.0, alg_bytes, per_call * 1e3)
+    roof.update({"traffic": None, "kernel": "attn_split + attn_combine (one call)", "launches_per_step": 1,
+                 "avg_launch_us": per_call * 1e3})
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = attn_cpu_baseline(q, k, v, st, scale)
+    out_j = {
+        "metric": "batch-invariant bf16 GEMM TFLOPS (M sweep) + % MFMA/HBM roofline, 1 GPU",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q, K, V ~ N(0,1); lengths lognormal median 1024, 16..8192)",
+        "config": {"workload": "Llama-3.1-8B decode attention: 256 sequences, 32 q heads, 8 kv heads, head dim 128, "
+                               "ragged KV lengths, split size 512",
+                   "total_keys": ntok, "kv_bytes": kv_bytes, "split": a["split"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "split_sweep_us": sweep,
+        "kv_gbs": round(kv_bytes / (per_call * 1e-3) / 1e9, 0),
+    }
+    print(json.dumps(out_j), flush=True)
+    return 0
+
+
+def attn_cpu_baseline(q, k, v, st, scale, target_s=10.0):
+    """The oracle on the host cores, on a bounded sample: the first sequences
+    of the batch, as many as fit in about `target_s` seconds."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    qb = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    b = 0
+    t_total = 0.0
+    keys = 0
+    while b < len(st) - 1 and t_total < target_s:
+        lo, hi = int(st[b]), int(st[b + 1])
+        kb = k[lo:hi].view(torch.int16).cpu().numpy().view(np.uint16)
+        vb = v[lo:hi].view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oracle.decode_attn_f64(qb[b:b + 1], kb, vb, np.array([0, hi - lo], np.int32), scale)
+        t_total += time.perf_counter() - t0
+        keys += hi - lo
+        b += 1
+    flops = 4.0 * keys * q.shape[1] * q.shape[2]
+    return {"value": flops / t_total / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "fp64 oracle on the first %d sequences (%d keys) of the batch, %.1f s" % (b, keys, t_total)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama8b_down", choices=sorted(WORKLOADS) + ["moe", "moe_layer", "norm_gate_up"])
+    ap.add_argument("--workload", default="llama8b_down", choices=sorted(WORKLOADS) + ["moe", "moe_layer", "norm_gate_up", "decode_attn"])
     ap.add_argument("--rotate-gib", type=float, default=1.0,
                     help="weight copies to rotate over, in GiB (defeats the Infinity Cache)")
     ap.add_argument("--m", type=str, default=None,
@@ -706,6 +831,8 @@ def main(argv=None):
         return run_moe_layer(args, bg)
     if args.workload == "norm_gate_up":
         return run_norm_gate_up(args, bg)
+    if args.workload == "decode_attn":
+        return run_decode_attn(args, bg)
     wl = dict(WORKLOADS[args.workload])
     if args.m:
         wl["ms"] = [int(v) for v in args.m.split(",")]

@@ -5,7 +5,8 @@ row count, row position and the other rows never change a row's result.
 The compute runs in the hand-written HIP library ``libbigemm.so`` (C ABI in
 ``include/bi_gemm.h``; ``include/bi_moe.h`` for the MoE expert layer built
 around the grouped GEMM; ``include/bi_norm.h`` for the RMSNorm before a
-projection); this package is its thin Python binding.
+projection; ``include/bi_attn.h`` for decode attention with a pinned split
+size); this package is its thin Python binding.
 """
 from ._lib import (  # noqa: F401
     LIB_PATH,
@@ -14,6 +15,7 @@ from ._lib import (  # noqa: F401
     STATUS_CODE,
     BiGemmError,
     BiPinInfo,
+    DecodeAttention,
     Gemm,
     GroupedGemm,
     MoeLayer,

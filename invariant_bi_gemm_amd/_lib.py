@@ -1,5 +1,5 @@
-"""ctypes binding of the C ABI declared in include/bi_gemm.h, include/bi_moe.h
-and include/bi_norm.h.
+"""ctypes binding of the C ABI declared in include/bi_gemm.h, include/bi_moe.h,
+include/bi_norm.h and include/bi_attn.h.
 
 Argument marshalling only: every step of the GEMM runs in the HIP library
 ``libbigemm.so``.  Tensors are PyTorch device tensors (PyTorch provides device
@@ -76,6 +76,9 @@ def _declare(lib):
         "bi_moe_run": ([P, P, I, P, P], S),
         "bi_moe_destroy": ([P], None),
         "bi_rmsnorm": ([P, P, I, I, ctypes.c_float, P, P], S),
+        "bi_attn_create": ([I, I, I, I, I, I, ctypes.POINTER(P)], S),
+        "bi_attn_decode": ([P, P, P, P, P, I, I, ctypes.c_float, P, P], S),
+        "bi_attn_destroy": ([P], None),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -415,3 +418,61 @@ def rmsnorm(x, gain, eps: float = 1e-5, out=None, stream=None):
             raise ValueError("out must be [%d, %d]" % (t, h))
     check(lib.bi_rmsnorm(_p(x), _p(gain), t, h, float(eps), _p(out), _stream_ptr(stream)))
     return out
+
+
+# ---- decode attention (include/bi_attn.h) --------------------------------------
+
+class DecodeAttention:
+    """Decode attention with a pinned split size: one query token per
+    sequence against its KV cache, grouped-query heads, D = 128.  The handle
+    owns the split workspace for up to ``max_batch`` sequences of up to
+    ``max_seq_len`` keys."""
+
+    def __init__(self, hq: int, hkv: int, split: int, max_batch: int, max_seq_len: int, head_dim: int = 128,
+                 device=None):
+        import torch
+
+        lib = load()
+        self.hq, self.hkv, self.d, self.split = int(hq), int(hkv), int(head_dim), int(split)
+        self.max_batch, self.max_seq_len = int(max_batch), int(max_seq_len)
+        self._lib = lib
+        h = ctypes.c_void_p()
+        with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+            st = lib.bi_attn_create(self.hq, self.hkv, self.d, self.split, self.max_batch, self.max_seq_len,
+                                    ctypes.byref(h))
+        check(st)
+        self._h = h
+
+    def __call__(self, q, k, v, seq_start, scale=None, out=None, stream=None):
+        """q bf16 [B, Hq, D]; k, v bf16 [Ntok, Hkv, D]; seq_start int32 [B+1] on
+        the device.  Returns fp32 [B, Hq, D]."""
+        import torch
+
+        _need(q, torch.bfloat16, 3, "q")
+        _need(k, torch.bfloat16, 3, "k")
+        _need(v, torch.bfloat16, 3, "v")
+        _need(seq_start, torch.int32, 1, "seq_start")
+        b = int(q.shape[0])
+        if tuple(q.shape[1:]) != (self.hq, self.d) or tuple(k.shape[1:]) != (self.hkv, self.d) \
+                or k.shape != v.shape or int(seq_start.shape[0]) != b + 1:
+            raise ValueError("shape mismatch")
+        if scale is None:
+            scale = 1.0 / float(self.d) ** 0.5
+        if out is None:
+            out = torch.empty((b, self.hq, self.d), dtype=torch.float32, device=q.device)
+        else:
+            _need(out, torch.float32, 3, "out")
+        check(self._lib.bi_attn_decode(self._h, _p(q), _p(k), _p(v), _p(seq_start), b, int(k.shape[0]),
+                                       float(scale), _p(out), _stream_ptr(stream)))
+        return out
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.bi_attn_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001
+            pass

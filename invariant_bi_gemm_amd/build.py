@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbigemm.so")
 SOURCES = ["bigemm_api.cpp", "bigemm_kernels.hip", "moe_api.cpp", "moe_kernels.hip", "norm_api.cpp",
-           "norm_kernels.hip"]
+           "norm_kernels.hip", "attn_api.cpp", "attn_kernels.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

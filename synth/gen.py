@@ -37,6 +37,7 @@ __all__ = [
     "moe_routing",
     "router_logits",
     "probe_rows",
+    "decode_lengths",
 ]
 
 
@@ -168,3 +169,13 @@ def probe_rows(seed: int, m: int, count: int = 64) -> np.ndarray:
         return np.arange(m, dtype=np.int64)
     g = rng(seed)
     return np.sort(g.choice(m, size=count, replace=False)).astype(np.int64)
+
+
+def decode_lengths(seed: int, batch: int, median: float = 1024.0, sigma: float = 0.8, lo: int = 16,
+                   hi: int = 8192) -> np.ndarray:
+    """KV lengths of a decode batch: lognormal around ``median`` with spread
+    ``sigma``, clipped to ``lo .. hi`` -- a ragged mix of short and long
+    contexts such as conversation and summarisation prompts give.  int32 [batch]."""
+    g = rng(seed)
+    n = np.exp(np.log(median) + sigma * g.standard_normal(batch))
+    return np.clip(np.rint(n), lo, hi).astype(np.int32)

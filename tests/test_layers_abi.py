@@ -1,4 +1,4 @@
-"""The MoE layer's and RMSNorm's C ABI on the host, without a GPU: every entry point rejects
+"""The MoE layer's, RMSNorm's and decode attention's C ABI on the host, without a GPU: every entry point rejects
 bad sizes, NULL and misaligned pointers, and bad handles before any HIP call,
 and empty calls return without one (not gpu)."""
 import ctypes
@@ -145,3 +145,28 @@ def test_rmsnorm_rejects(lib, args, want):
 
 def test_rmsnorm_empty_launches_nothing(lib):
     assert lib.bi_rmsnorm(None, None, 0, 4096, 1e-5, None, None) == 0
+
+
+@pytest.mark.parametrize("hq,hkv,d,split,mb,ml", [
+    (32, 8, 64, 256, 4, 1024),      # D not 128
+    (32, 6, 128, 256, 4, 1024),     # Hq not a multiple of Hkv
+    (48, 8, 128, 256, 4, 1024),     # Hq / Hkv = 6
+    (32, 8, 128, 100, 4, 1024),     # split not a multiple of 64
+    (64, 8, 128, 16448, 4, 1024),   # split above 16384
+    (32, 8, 128, 256, 0, 1024),     # max_batch = 0
+    (32, 8, 128, 256, 70000, 1024),  # max_batch above 65535
+    (32, 8, 128, 256, 4, 0),        # max_seq_len = 0
+])
+def test_attn_create_rejects(lib, hq, hkv, d, split, mb, ml):
+    out = P()
+    assert lib.bi_attn_create(hq, hkv, d, split, mb, ml, ctypes.byref(out)) == INV
+    assert not out.value
+
+
+def test_attn_decode_rejects_bad_handles(lib):
+    assert lib.bi_attn_create(32, 8, 128, 256, 4, 1024, None) == INV
+    assert lib.bi_attn_decode(None, A, A, A, A, 1, 1, 0.1, A, None) == INV
+    bogus = ctypes.create_string_buffer(256)
+    assert lib.bi_attn_decode(ctypes.cast(bogus, P), A, A, A, A, 1, 1, 0.1, A, None) == INV
+    lib.bi_attn_destroy(None)
+    lib.bi_attn_destroy(ctypes.cast(bogus, P))
