@@ -346,8 +346,8 @@ def moe_layer_work(t, touched_up, touched_down):
         ("router GEMM", 2.0 * t * E * H, 2.0 * E * H + 2.0 * t * H + 4.0 * t * E),
         ("top-k", 0.0, 4.0 * t * E + 8.0 * t * k),
         ("grouping", 0.0, 4.0 * t * k + 4.0 * (E + 1) + 8.0 * r),
-        ("gather", 0.0, 2.0 * t * H + 2.0 * r * H + 4.0 * r),
-        ("up GEMM", 2.0 * r * 2 * I * H, 2.0 * touched_up * 2 * I * H + 2.0 * r * H + 4.0 * r * 2 * I),
+        ("up GEMM (rows read from x by index)", 2.0 * r * 2 * I * H,
+         2.0 * touched_up * 2 * I * H + 2.0 * t * H + 4.0 * r + 4.0 * r * 2 * I),
         ("SwiGLU", 0.0, 4.0 * r * 2 * I + 2.0 * r * I),
         ("down GEMM", 2.0 * r * H * I, 2.0 * touched_down * H * I + 2.0 * r * I + 4.0 * r * H),
         ("combine", 0.0, 4.0 * r * H + 12.0 * t * k + 4.0 * t * H),
@@ -365,8 +365,9 @@ def _roof(flops, nbytes, us):
 
 
 def run_moe_layer(args, bg):
-    """One step = the whole expert layer (router, top-k, grouping, gather, up
-    projection, SwiGLU, down projection, combine; one bi_moe_run call) at
+    """One step = the whole expert layer (router, top-k, grouping, up
+    projection reading token rows by index, SwiGLU, down projection, combine;
+    one bi_moe_run call) at
     every token count T of the sweep.  Two layer handles over two copies of
     the weights alternate, so the Infinity Cache does not keep a call's
     experts for the next call of the same T.  A second pass runs the steps
@@ -488,7 +489,6 @@ def _moe_steps_timed(bg, lib, dev, x, t, reps):
     off = torch.empty(E + 1, dtype=torch.int32, device=d)
     tok = torch.empty(r, dtype=torch.int32, device=d)
     row_of = torch.empty((t, k), dtype=torch.int32, device=d)
-    xg = torch.empty((r, H), dtype=torch.bfloat16, device=d)
     h = torch.empty((r, 2 * I), dtype=torch.float32, device=d)
     a = torch.empty((r, I), dtype=torch.bfloat16, device=d)
     o = torch.empty((r, H), dtype=torch.float32, device=d)
@@ -500,8 +500,7 @@ def _moe_steps_timed(bg, lib, dev, x, t, reps):
         lambda g: g[0].run_ptr(x.data_ptr(), t, logits.data_ptr()),
         lambda g: lib.bi_moe_topk(P(logits), t, E, k, P(ids), P(w), st),
         lambda g: lib.bi_moe_permute(P(ids), t, E, k, P(off), P(tok), P(row_of), st),
-        lambda g: lib.bi_gather_rows(P(x), t, P(tok), r, H, P(xg), st),
-        lambda g: lib.bi_grouped_gemm_run(g[1]._h, P(xg), P(off), r, P(h), st),
+        lambda g: lib.bi_grouped_gemm_run_indexed(g[1]._h, P(x), t, P(tok), P(off), r, P(h), st),
         lambda g: lib.bi_swiglu(P(h), r, I, P(a), st),
         lambda g: lib.bi_grouped_gemm_run(g[2]._h, P(a), P(off), r, P(o), st),
         lambda g: lib.bi_moe_combine(P(o), r, P(ids), P(w), P(row_of), t, k, H, P(y), st),

@@ -154,6 +154,20 @@ bi_status_t bi_grouped_gemm_create(int E, int N, int K, const void *W, bi_gemm_t
 bi_status_t bi_grouped_gemm_run(bi_gemm_t h, const void *x, const int32_t *expert_offsets,
                                 int R, float *y, void *stream);
 
+/*
+ * Grouped run over indexed rows: grouped row i is row row_index[i] of x, so
+ * y[i] = x[row_index[i]] W[e]^T for the rows i of expert e.  This is the
+ * MoE layer's gather of token rows into expert order (each token appears
+ * once per expert it is routed to) done by the kernels' own loads; the
+ * result is bit for bit that of bi_grouped_gemm_run on the gathered rows.
+ *   x: device bf16 [x_rows, K], 16-byte aligned; 1 <= x_rows, x_rows*K < 2^31.
+ *   row_index: DEVICE int32 [R], 4-byte aligned; an index outside
+ *       0..x_rows-1 is clamped into it.
+ * Other arguments and guarantees as bi_grouped_gemm_run.
+ */
+bi_status_t bi_grouped_gemm_run_indexed(bi_gemm_t h, const void *x, int x_rows, const int32_t *row_index,
+                                        const int32_t *expert_offsets, int R, float *y, void *stream);
+
 /* Release a handle (dense or grouped).  NULL is ignored. */
 void bi_gemm_destroy(bi_gemm_t h);
 

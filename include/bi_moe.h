@@ -8,7 +8,8 @@
  *   logits = x W_r^T                        router, the dense GEMM [E, H]
  *   (ids, w) = top-k(logits)                k experts, weights softmax(chosen)
  *   rows grouped by expert                  (token, slot) pairs, stable
- *   h = x_row W_up[e]^T                     grouped GEMM [E, 2I, H]
+ *   h = x_row W_up[e]^T                     grouped GEMM [E, 2I, H], each row
+ *                                           read from its token's row of x
  *   a = bf16(silu(h[:, :I]) * h[:, I:])     SwiGLU
  *   o = a W_down[e]^T                       grouped GEMM [E, H, I]
  *   y[t] = sum_j w[t][j] o[row(t, j)]       in ascending expert id

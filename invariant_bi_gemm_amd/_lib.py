@@ -67,6 +67,7 @@ def _declare(lib):
         "bi_status_string": ([S], ctypes.c_char_p),
         "bi_gemm_kernel_name": ([P, I], ctypes.c_char_p),
         "bi_last_error": ([], ctypes.c_char_p),
+        "bi_grouped_gemm_run_indexed": ([P, P, I, P, P, I, P, P], S),
         "bi_moe_topk": ([P, I, I, I, P, P, P], S),
         "bi_moe_permute": ([P, I, I, I, P, P, P, P], S),
         "bi_gather_rows": ([P, I, P, I, I, P, P], S),
@@ -249,6 +250,27 @@ class GroupedGemm:
         check(self._lib.bi_grouped_gemm_run(self._h, ctypes.c_void_p(x.data_ptr()),
                                             ctypes.c_void_p(expert_offsets.data_ptr()), r,
                                             ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)))
+        return out
+
+    def run_indexed(self, x, row_index, expert_offsets, out=None, stream=None):
+        """``y[i] = x[row_index[i]] @ W[e].T`` for the rows i of expert e: the
+        gather into expert order done by the kernels' loads."""
+        import torch
+
+        _need(x, torch.bfloat16, 2, "x")
+        _need(row_index, torch.int32, 1, "row_index")
+        _need(expert_offsets, torch.int32, 1, "expert_offsets")
+        if x.shape[1] != self.k or expert_offsets.shape[0] != self.e + 1:
+            raise ValueError("shape mismatch")
+        r = int(row_index.shape[0])
+        if out is None:
+            out = torch.empty((r, self.n), dtype=torch.float32, device=x.device)
+        else:
+            _need(out, torch.float32, 2, "out")
+        check(self._lib.bi_grouped_gemm_run_indexed(self._h, ctypes.c_void_p(x.data_ptr()), int(x.shape[0]),
+                                                    ctypes.c_void_p(row_index.data_ptr()),
+                                                    ctypes.c_void_p(expert_offsets.data_ptr()), r,
+                                                    ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)))
         return out
 
     def close(self):

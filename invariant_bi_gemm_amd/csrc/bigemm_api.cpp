@@ -423,8 +423,10 @@ bi_status_t bi_gemm_run(bi_gemm_t hh, const void* x, int M, float* y, void* stre
     return BI_OK;
 }
 
-bi_status_t bi_grouped_gemm_run(bi_gemm_t hh, const void* x, const int32_t* expert_offsets, int R,
-                                float* y, void* stream)
+namespace {
+
+bi_status_t grouped_run(bi_gemm_t hh, const void* x, int xn, const int32_t* xidx, const int32_t* expert_offsets,
+                        int R, float* y, void* stream)
 {
     bi_gemm* h = handle_of(hh);
     if (!h)
@@ -444,14 +446,36 @@ bi_status_t bi_grouped_gemm_run(bi_gemm_t hh, const void* x, const int32_t* expe
     const long long wide = h->plan.n > h->plan.k ? h->plan.n : h->plan.k;
     if ((long long)R * wide >= (1LL << 31))
         return fail(BI_ERR_INVALID_ARGUMENT, "R*max(N,K) must be below 2^31");
+    if (xidx) {
+        if (xn < 1 || (long long)xn * h->plan.k >= (1LL << 31))
+            return fail(BI_ERR_INVALID_ARGUMENT, "need 1 <= x_rows and x_rows*K below 2^31");
+        if ((reinterpret_cast<uintptr_t>(xidx) & 3u) != 0)
+            return fail(BI_ERR_MISALIGNED, "row_index must be 4-byte aligned");
+    }
     bi_status_t st = check_run_device(h);
     if (st != BI_OK)
         return st;
-    hipError_t e = bigemm::launch_grouped(h->plan, h->W, x, expert_offsets, R, y,
+    hipError_t e = bigemm::launch_grouped(h->plan, h->W, x, expert_offsets, R, y, xidx, xn,
                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(BI_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return BI_OK;
+}
+
+}  // namespace
+
+bi_status_t bi_grouped_gemm_run(bi_gemm_t hh, const void* x, const int32_t* expert_offsets, int R,
+                                float* y, void* stream)
+{
+    return grouped_run(hh, x, 0, nullptr, expert_offsets, R, y, stream);
+}
+
+bi_status_t bi_grouped_gemm_run_indexed(bi_gemm_t hh, const void* x, int x_rows, const int32_t* row_index,
+                                        const int32_t* expert_offsets, int R, float* y, void* stream)
+{
+    if (R > 0 && !row_index)
+        return fail(BI_ERR_INVALID_ARGUMENT, "row_index is NULL");
+    return grouped_run(hh, x, x_rows, R > 0 ? row_index : nullptr, expert_offsets, R, y, stream);
 }
 
 void bi_gemm_destroy(bi_gemm_t hh)

@@ -52,7 +52,9 @@ bi_status_t api_device(int* dev, int* num_cus);
 // Launchers (bigemm_kernels.hip).  They assume validated arguments.
 hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, float* y,
                         hipStream_t stream);
+// xidx (optional): row i of the grouped x is row xidx[i] of x (xn rows).
 hipError_t launch_grouped(const Plan& p, const void* W, const void* x,
-                          const int32_t* offsets, int R, float* y, hipStream_t stream);
+                          const int32_t* offsets, int R, float* y, const int32_t* xidx, int xn,
+                          hipStream_t stream);
 
 }  // namespace bigemm

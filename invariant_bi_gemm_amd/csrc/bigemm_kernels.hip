@@ -211,11 +211,15 @@ struct TiledCfg {
 // One BM x BN output block: rows m0 .. m0+BM-1 of x/y (rows at or past
 // row_hi are clamped on load and never stored), columns n0 .. n0+BN-1 of y
 // (rows of Wb past N are clamped likewise).
-template <int BM, int BN, int WM, int WN, int BK, int NS>
+// With kIdx, row i of the logical x is row xidx[i] of the stored x (xn rows;
+// an index outside 0..xn-1 is clamped into it): the MoE layer's gather of
+// token rows into expert order, done by the loads themselves.
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool kIdx = false>
 __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ Wb,
                                             float* __restrict__ y, int m0, int row_hi, int n0,
-                                            int N, int K, Split sp)
+                                            int N, int K, Split sp,
+                                            const int32_t* __restrict__ xidx = nullptr, int xn = 0)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     constexpr int kCh = C::kCh;
@@ -228,7 +232,8 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
     const int wrows = min(BN, N - n0);
     const int xrows = min(BM, row_hi - m0);
     const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wb + (size_t)n0 * K, (uint32_t)wrows * rowb);
-    const __amdgpu_buffer_rsrc_t rX = make_rsrc(x + (size_t)m0 * K, (uint32_t)xrows * rowb);
+    const __amdgpu_buffer_rsrc_t rX =
+        kIdx ? make_rsrc(x, (uint32_t)xn * rowb) : make_rsrc(x + (size_t)m0 * K, (uint32_t)xrows * rowb);
 
     // Byte offset of each of this lane's loads within a stage's rows.  Unit
     // u of the stage (lane-linear in LDS) holds logical chunk swz(r, u % kCh)
@@ -243,7 +248,12 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
         } else {
             const int uu = u - BN * kCh;
             const int r = uu / kCh;
-            voff[j] = (uint32_t)min(r, xrows - 1) * rowb + swz<kCh>(r, uu % kCh) * 16;
+            uint32_t row = (uint32_t)min(r, xrows - 1);
+            if constexpr (kIdx) {
+                const int t = xidx[m0 + (int)row];
+                row = (uint32_t)(t < 0 ? 0 : (t >= xn ? xn - 1 : t));
+            }
+            voff[j] = row * rowb + swz<kCh>(r, uu % kCh) * 16;
         }
     }
     auto issue = [&](int s, int buf) {
@@ -402,11 +412,13 @@ __global__ void __launch_bounds__(WM * WN * 64)
 // device and cut into 8 contiguous ranges, one per XCD (hardware hands block b
 // to XCD b % 8; the grid is a multiple of 8), so each XCD's L2 holds few
 // experts at a time and every XCD gets the same share whatever the routing.
-template <int BM, int BN, int WM, int WN, int BK, int NS>
+// kIdx: x rows are read through xidx.
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool kIdx>
 __global__ void __launch_bounds__(WM * WN * 64)
     bigemm_tiled_grouped(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                          float* __restrict__ y, const int32_t* __restrict__ off, int E, int R,
-                         int N, int K, Split sp, int tiles_n, int cmin)
+                         int N, int K, Split sp, int tiles_n, int cmin,
+                         const int32_t* __restrict__ xidx, int xn)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     __shared__ uint4 lds[NS * C::kStageUnits];
@@ -421,8 +433,8 @@ __global__ void __launch_bounds__(WM * WN * 64)
         int m0, hi;
         const int e = grouped_slot(s_off, s_first, E, BM, t / tiles_n, &m0, &hi);
         barrier_after_lds_reads();  // every wave is done with the previous tile's stages
-        tiled_block<BM, BN, WM, WN, BK, NS>(lds, x, W + (size_t)e * N * K, y, m0, hi,
-                                            (t % tiles_n) * BN, N, K, sp);
+        tiled_block<BM, BN, WM, WN, BK, NS, kIdx>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * BN,
+                                                  N, K, sp, xidx, xn);
     }
 }
 
@@ -487,13 +499,15 @@ struct StreamItem {
     const uint16_t* Wb;
 };
 
-template <int MB, int XR, int BKS, int NP>
+template <int MB, int XR, int BKS, int NP, bool kIdx = false>
 __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ W, float* __restrict__ y,
                                             int N, int K, Split sp, int tiles_n, int nitems,
                                             // dense: M rows; grouped: clamped offsets and
                                             // the expert list, both in LDS
-                                            int M, const int* sh_off, const int* elist)
+                                            int M, const int* sh_off, const int* elist,
+                                            // grouped, kIdx: row indices into x (xn rows)
+                                            const int32_t* __restrict__ xidx = nullptr, int xn = 0)
 {
     using C = StreamCfg<MB, XR, BKS, NP>;
     constexpr int kCh = C::kChunks;
@@ -532,6 +546,22 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
             __amdgpu_buffer_rsrc_t rW = make_rsrc(W, 16), rX = make_rsrc(x, 16);
             uint32_t voff[kI];
             int cur_it = -1, k_stage = nst;
+            // indexed x rows: each item's row indices are loaded while the
+            // item before it streams (pend), not when the item starts
+            int pend[kI];
+            auto load_idx = [&](int it) {
+                if (!kIdx || it >= mine)
+                    return;
+                const StreamItem s = item_at(it);
+                const int xrows = min(XR, s.row_hi - s.m0);
+#pragma unroll
+                for (int j = 0; j < kI; ++j) {
+                    const int r = ((first + j) * 64 + lane) / kCh;
+                    pend[j] = r >= 16 ? xidx[s.m0 + min(r - 16, xrows - 1)] : 0;
+                }
+            };
+            if constexpr (kIdx)
+                load_idx(0);
             // stages are issued in order q = 0, 1, 2, ...: nst stages per item
             auto issue = [&](int q) {
                 if (k_stage == nst) {  // entering the next item: its rows, once
@@ -540,14 +570,24 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
                     const StreamItem s = item_at(cur_it);
                     const int xrows = min(XR, s.row_hi - s.m0);
                     rW = make_rsrc(s.Wb + (size_t)s.n0 * K, 16 * rowb);
-                    rX = make_rsrc(x + (size_t)s.m0 * K, (uint32_t)xrows * rowb);
+                    rX = kIdx ? make_rsrc(x, (uint32_t)xn * rowb)
+                              : make_rsrc(x + (size_t)s.m0 * K, (uint32_t)xrows * rowb);
 #pragma unroll
                     for (int j = 0; j < kI; ++j) {
                         const int u = (first + j) * 64 + lane;
                         const int r = u / kCh;
                         const int c = swz<kCh>(r, u % kCh);
-                        voff[j] = (r < 16 ? (uint32_t)r : (uint32_t)min(r - 16, xrows - 1)) * rowb + c * 16;
+                        uint32_t row = r < 16 ? (uint32_t)r : (uint32_t)min(r - 16, xrows - 1);
+                        if constexpr (kIdx) {
+                            if (r >= 16) {
+                                const int t = pend[j];
+                                row = (uint32_t)(t < 0 ? 0 : (t >= xn ? xn - 1 : t));
+                            }
+                        }
+                        voff[j] = row * rowb + c * 16;
                     }
+                    if constexpr (kIdx)
+                        load_idx(cur_it + 1);
                 }
                 uint4* dst = ring + (q % NR) * C::kStageUnits;
 #pragma unroll
@@ -636,12 +676,12 @@ __global__ void __launch_bounds__((MB + NP) * 64)
 }
 
 // Grouped: one m-block per expert whose row count c satisfies 0 < c <= cmax
-// (cmax <= XR).
-template <int MB, int XR, int BKS, int NP>
+// (cmax <= XR).  kIdx: x rows are read through xidx.
+template <int MB, int XR, int BKS, int NP, bool kIdx>
 __global__ void __launch_bounds__((MB + NP) * 64)
     bigemm_stream_grouped(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                           float* __restrict__ y, const int32_t* __restrict__ off, int E, int R,
-                          int N, int K, Split sp, int cmax)
+                          int N, int K, Split sp, int cmax, const int32_t* __restrict__ xidx, int xn)
 {
     using C = StreamCfg<MB, XR, BKS, NP>;
     __shared__ uint4 ring[C::NR * C::kStageUnits];
@@ -658,7 +698,8 @@ __global__ void __launch_bounds__((MB + NP) * 64)
     }
     __syncthreads();
     const int tiles_n = N / 16;
-    stream_body<MB, XR, BKS, NP>(ring, x, W, y, N, K, sp, tiles_n, count * tiles_n, 0, sh_off, elist);
+    stream_body<MB, XR, BKS, NP, kIdx>(ring, x, W, y, N, K, sp, tiles_n, count * tiles_n, 0, sh_off, elist, xidx,
+                                       xn);
 }
 
 // ---------------------------------------------------------------------------
@@ -710,19 +751,25 @@ hipError_t run_stream_k(const void* W, const void* x, int M, float* y, int N, in
 
 template <int MB, int XR, int BKS, int NP>
 hipError_t run_stream_grouped(const void* W, const void* x, const int32_t* off, int E, int R,
-                              float* y, int N, int K, Split sp, int cmax, int num_cus, hipStream_t stream)
+                              float* y, int N, int K, Split sp, int cmax, int num_cus, const int32_t* xidx,
+                              int xn, hipStream_t stream)
 {
     using C = StreamCfg<MB, XR, BKS, NP>;
-    hipLaunchKernelGGL((bigemm_stream_grouped<MB, XR, BKS, NP>), dim3(num_cus), dim3(C::kThreads), 0,
-                       stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y,
-                       off, E, R, N, K, sp, cmax);
+    if (xidx)
+        hipLaunchKernelGGL((bigemm_stream_grouped<MB, XR, BKS, NP, true>), dim3(num_cus), dim3(C::kThreads), 0,
+                           stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y,
+                           off, E, R, N, K, sp, cmax, xidx, xn);
+    else
+        hipLaunchKernelGGL((bigemm_stream_grouped<MB, XR, BKS, NP, false>), dim3(num_cus), dim3(C::kThreads), 0,
+                           stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y,
+                           off, E, R, N, K, sp, cmax, xidx, xn);
     return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int NS>
 hipError_t run_tiled_grouped(const void* W, const void* x, const int32_t* off, int E, int R,
                              float* y, int N, int K, Split sp, int cmin, int num_cus,
-                             hipStream_t stream)
+                             const int32_t* xidx, int xn, hipStream_t stream)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     if (R <= cmin)
@@ -732,9 +779,14 @@ hipError_t run_tiled_grouped(const void* W, const void* x, const int32_t* off, i
     // to whole sets of 8 (one per XCD)
     const int per_cu = 2 * (C::kLdsBytes + 4 * (2 * kMaxExperts + 2)) <= 160 * 1024 ? 2 : 1;
     const int grid = (num_cus * per_cu + 7) / 8 * 8;
-    hipLaunchKernelGGL((bigemm_tiled_grouped<BM, BN, WM, WN, BK, NS>), dim3(grid), dim3(C::kThreads),
-                       0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y,
-                       off, E, R, N, K, sp, tiles_n, cmin);
+    if (xidx)
+        hipLaunchKernelGGL((bigemm_tiled_grouped<BM, BN, WM, WN, BK, NS, true>), dim3(grid), dim3(C::kThreads),
+                           0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y,
+                           off, E, R, N, K, sp, tiles_n, cmin, xidx, xn);
+    else
+        hipLaunchKernelGGL((bigemm_tiled_grouped<BM, BN, WM, WN, BK, NS, false>), dim3(grid), dim3(C::kThreads),
+                           0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y,
+                           off, E, R, N, K, sp, tiles_n, cmin, xidx, xn);
     return hipGetLastError();
 }
 
@@ -848,7 +900,7 @@ hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, floa
 }
 
 hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int32_t* offsets,
-                          int R, float* y, hipStream_t stream)
+                          int R, float* y, const int32_t* xidx, int xn, hipStream_t stream)
 {
     // Experts with 1..smax rows go to the streaming kernel, the rest to the
     // tiled kernel; both realise the same tree, so the split point only
@@ -860,17 +912,17 @@ hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int
         hipError_t err = hipSuccess;
         if (smax > 0) {
             if (klen % 512 == 0)
-                err = run_stream_grouped<1, 16, 512, stream_producers<1, 512>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, stream);
+                err = run_stream_grouped<1, 16, 512, stream_producers<1, 512>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, xidx, xn, stream);
             else if (klen % 256 == 0)
-                err = run_stream_grouped<1, 16, 256, stream_producers<1, 256>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, stream);
+                err = run_stream_grouped<1, 16, 256, stream_producers<1, 256>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, xidx, xn, stream);
             else if (klen % 128 == 0)
-                err = run_stream_grouped<1, 16, 128, stream_producers<1, 128>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, stream);
+                err = run_stream_grouped<1, 16, 128, stream_producers<1, 128>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, xidx, xn, stream);
             else
-                err = run_stream_grouped<1, 16, 64, stream_producers<1, 64>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, stream);
+                err = run_stream_grouped<1, 16, 64, stream_producers<1, 64>()>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, xidx, xn, stream);
             if (err != hipSuccess)
                 return err;
         }
-        err = run_tiled_grouped<128, 128, 2, 2, 64, 2>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, stream);
+        err = run_tiled_grouped<128, 128, 2, 2, 64, 2>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, xidx, xn, stream);
         if (err != hipSuccess)
             return err;
     }

@@ -119,7 +119,6 @@ struct bi_moe {
     int32_t* offsets;
     int32_t* tok;
     int32_t* row_of;
-    void* xp;  // bf16 [maxT*k, H]
     float* h;  // fp32 [maxT*k, 2I]
     void* a;   // bf16 [maxT*k, I]
     float* o;  // fp32 [maxT*k, H]
@@ -253,11 +252,10 @@ bi_status_t bi_moe_create(int E, int k, int H, int I, const void* W_router, cons
     const long long b_logits = up256((long long)max_tokens * E * 4);
     const long long b_pair = up256(rows * 4);
     const long long b_off = up256((long long)(E + 1) * 4);
-    const long long b_xp = up256(rows * H * 2);
     const long long b_h = up256(rows * 2 * I * 4);
     const long long b_a = up256(rows * I * 2);
     const long long b_o = up256(rows * H * 4);
-    const long long total = b_logits + 4 * b_pair + b_off + b_xp + b_h + b_a + b_o;
+    const long long total = b_logits + 4 * b_pair + b_off + b_h + b_a + b_o;
     hipError_t e = hipMalloc(&m->ws, (size_t)total);
     if (e != hipSuccess) {
         m->ws = nullptr;
@@ -278,8 +276,6 @@ bi_status_t bi_moe_create(int E, int k, int H, int I, const void* W_router, cons
     p += b_pair;
     m->offsets = reinterpret_cast<int32_t*>(p);
     p += b_off;
-    m->xp = p;
-    p += b_xp;
     m->h = reinterpret_cast<float*>(p);
     p += b_h;
     m->a = p;
@@ -321,9 +317,8 @@ bi_status_t bi_moe_run(bi_moe_t hh, const void* x, int T, float* y, void* stream
         return st;
     if ((st = launched(bimoe::launch_permute(m->ids, T, m->E, m->k, m->offsets, m->tok, m->row_of, s))) != BI_OK)
         return st;
-    if ((st = launched(bimoe::launch_gather(x, T, m->tok, R, m->H, m->xp, s))) != BI_OK)
-        return st;
-    if ((st = bi_grouped_gemm_run(m->up, m->xp, m->offsets, R, m->h, stream)) != BI_OK)
+    // the up projection reads each row's token straight from x (no gathered copy)
+    if ((st = bi_grouped_gemm_run_indexed(m->up, x, T, m->tok, m->offsets, R, m->h, stream)) != BI_OK)
         return st;
     if ((st = launched(bimoe::launch_swiglu(m->h, R, m->I, m->a, s))) != BI_OK)
         return st;

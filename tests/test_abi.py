@@ -96,6 +96,7 @@ def test_run_rejects_bad_handles(lib):
     assert lib.bi_gemm_run(ctypes.cast(bogus, ctypes.c_void_p), ctypes.c_void_p(4096), 1,
                            ctypes.c_void_p(4096), None) == INV
     assert lib.bi_grouped_gemm_run(None, None, None, 4, None, None) == INV
+    assert lib.bi_grouped_gemm_run_indexed(None, None, 4, None, None, 4, None, None) == INV
     info = BiPinInfo()
     assert lib.bi_gemm_get_pin(None, ctypes.byref(info)) == INV
     lib.bi_gemm_destroy(None)

@@ -108,3 +108,25 @@ def test_grouped_empty_and_single_expert(gpu, experts):
     rows = synth.probe_rows(172, r, 32)
     yr, a = oracle.grouped_f64(x, w, offs, rows=rows)
     assert_parity(y.cpu().numpy()[rows], yr, a, "single expert")
+
+
+@pytest.mark.parametrize("tokens", [1, 16, 256, 4096])
+def test_indexed_rows_equal_gathered_rows(gpu, experts, tokens):
+    """The run over indexed token rows is, bit for bit, the run over the
+    gathered rows; indices outside the token rows are clamped into them."""
+    n, k = SHAPES["up"]
+    w, wd = experts["up"]
+    g = gpu.GroupedGemm(wd)
+    tok, off, _ = synth.moe_routing(180 + tokens, tokens, E, TOPK)
+    x_tok = synth.normal_bf16(181 + tokens, (tokens, k))
+    offd = torch.as_tensor(off, device=DEV)
+    y_gather = bits32(g(to_dev(np.ascontiguousarray(x_tok[tok])), offd))
+    y_index = bits32(g.run_indexed(to_dev(x_tok), torch.as_tensor(tok, device=DEV), offd))
+    assert_bits_equal(y_gather, y_index, "indexed vs gathered rows, T=%d" % tokens)
+    bad = tok.copy()
+    bad[::7] = -3
+    bad[1::11] = tokens + 5
+    clamped = np.clip(bad, 0, tokens - 1)
+    y_bad = bits32(g.run_indexed(to_dev(x_tok), torch.as_tensor(bad, device=DEV), offd))
+    y_cl = bits32(g(to_dev(np.ascontiguousarray(x_tok[clamped])), offd))
+    assert_bits_equal(y_bad, y_cl, "out-of-range indices clamp, T=%d" % tokens)
