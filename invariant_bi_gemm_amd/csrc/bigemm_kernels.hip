@@ -20,7 +20,9 @@
 // Kernel families:
 //   bigemm_tiled   mid and large M: an NS-stage LDS pipeline fed by direct
 //                  buffer->LDS loads, one barrier per stage, output blocks
-//                  from 64x32 to 256x256 (x rows by W rows) chosen by M.  MFMA bound at large M.
+//                  from 64x32 to 128x256 (x rows by W rows) chosen by M.
+//   bigemm_tiled4  large M: 256x256 blocks, four waves with their
+//                  accumulators in the accumulation registers.  MFMA bound.
 //   bigemm_stream  small M: a persistent, warp-specialised weight streamer.
 //                  Up to seven producer waves keep a deep LDS ring of W (and
 //                  x) full with direct buffer->LDS loads; consumer waves run
@@ -67,6 +69,23 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
                                       const void* lds_base)
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
+}
+
+// The same load, written out.  The compiler then does not see a store into
+// LDS and does not wait for the load before later LDS reads; the caller
+// orders them (vmcnt waits and barriers).  M0 takes the LDS address; an
+// SALU write of M0 needs one wait state before the load reads it (the nop).
+typedef int sgpr4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ sgpr4 rsrc_words(const void* base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return sgpr4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+__device__ __forceinline__ void dma16_asm(const sgpr4& r, uint32_t voff, uint32_t soff, const void* lds_base)
+{
+    const uint32_t m0v = (uint32_t)(uintptr_t)((lds_void*)lds_base);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0v)
+                 : "memory");
 }
 
 // Workgroup barrier for the pipelined loops.  __syncthreads() would add a
@@ -407,6 +426,229 @@ __global__ void __launch_bounds__(WM * WN * 64)
     tiled_block<BM, BN, WM, WN, BK, NS>(lds, x, W, y, tm * BM, M, tn * BN, N, K, sp);
 }
 
+// ---------------------------------------------------------------------------
+// Four-wave 256x256 block (large M)
+// ---------------------------------------------------------------------------
+// Same tree as tiled_block, 256x256 output blocks, but four waves of 128x128
+// each instead of eight of 128x64: a CU reads each stage from LDS 8 times
+// instead of 12 and half as many waves meet at each barrier.  A wave's 64
+// accumulator tiles (256 values per lane) live in the accumulation registers
+// a0..a255, which the MFMAs read and write directly.  They are written only
+// by the inline-asm MFMAs below and read only by the epilogue; the compiler
+// never allocates them, because the kernel keeps its own registers below 256
+// and never spills (a CPU test checks the built code for exactly this).  The
+// compiler still places the fragment reads and loads, which sit between the
+// MFMA statements in source order, and inserts the waits for the fragments
+// each MFMA reads.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Declares a0..a255 used, so that the kernel descriptor reserves them.
+#define BIG_AGPRS10(p) "a" #p "0", "a" #p "1", "a" #p "2", "a" #p "3", "a" #p "4", "a" #p "5", "a" #p "6", \
+    "a" #p "7", "a" #p "8", "a" #p "9"
+__device__ __forceinline__ void claim_agprs()
+{
+    asm volatile("" ::: "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", BIG_AGPRS10(1),
+                 BIG_AGPRS10(2), BIG_AGPRS10(3), BIG_AGPRS10(4), BIG_AGPRS10(5), BIG_AGPRS10(6),
+                 BIG_AGPRS10(7), BIG_AGPRS10(8), BIG_AGPRS10(9), BIG_AGPRS10(10), BIG_AGPRS10(11),
+                 BIG_AGPRS10(12), BIG_AGPRS10(13), BIG_AGPRS10(14), BIG_AGPRS10(15), BIG_AGPRS10(16),
+                 BIG_AGPRS10(17), BIG_AGPRS10(18), BIG_AGPRS10(19), BIG_AGPRS10(20), BIG_AGPRS10(21),
+                 BIG_AGPRS10(22), BIG_AGPRS10(23), BIG_AGPRS10(24), "a250", "a251", "a252", "a253",
+                 "a254", "a255");
+}
+#undef BIG_AGPRS10
+
+// Accumulator tile T is a[4T .. 4T+3].  kZero starts the chain from +0 (the
+// inline constant), as the first k-step of every split does.
+template <int T, bool kZero>
+__device__ __forceinline__ void mfma_agpr(const uint4& a, const uint4& b)
+{
+    if constexpr (kZero)
+        asm volatile("v_mfma_f32_16x16x32_bf16 a[%c2:%c3], %0, %1, 0" ::"v"(__builtin_bit_cast(i32x4, a)),
+                     "v"(__builtin_bit_cast(i32x4, b)), "n"(4 * T), "n"(4 * T + 3));
+    else
+        asm volatile("v_mfma_f32_16x16x32_bf16 a[%c2:%c3], %0, %1, a[%c2:%c3]" ::"v"(__builtin_bit_cast(i32x4, a)),
+                     "v"(__builtin_bit_cast(i32x4, b)), "n"(4 * T), "n"(4 * T + 3));
+}
+
+template <int T>
+__device__ __forceinline__ f32x4 read_agpr_tile()
+{
+    f32x4 v;
+    asm volatile("v_accvgpr_read_b32 %0, a%c4\n\t"
+                 "v_accvgpr_read_b32 %1, a%c5\n\t"
+                 "v_accvgpr_read_b32 %2, a%c6\n\t"
+                 "v_accvgpr_read_b32 %3, a%c7"
+                 : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3])
+                 : "n"(4 * T), "n"(4 * T + 1), "n"(4 * T + 2), "n"(4 * T + 3));
+    return v;
+}
+
+// f(integral_constant<int, T>) for T = 0 .. n-1, in order, unrolled.
+template <typename F, int... T>
+__device__ __forceinline__ void for_each_t(F&& f, std::integer_sequence<int, T...>)
+{
+    (f(std::integral_constant<int, T>{}), ...);
+}
+
+// LDS: W triple-buffered (3 x 32 KB) and x double-buffered (2 x 32 KB), the
+// whole 160 KB.  A stage is 64 values of k (two MFMA k-steps, full 128-byte
+// row segments).  Stage t's W is loaded during k-step 0 of stage t-2 and its
+// x during k-step 1 of stage t-2, 8 loads per wave spread over each k-step's
+// 64 MFMAs: loads issued in bursts stall the issuing wave (a CU accepts one
+// 1 KB load about every 16 cycles) and, with one wave per SIMD, the MFMA
+// pipe with it.
+
+template <bool kIdx = false>
+__device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restrict__ x,
+                                              const uint16_t* __restrict__ Wb, float* __restrict__ y, int m0,
+                                              int row_hi, int n0, int N, int K, Split sp,
+                                              const int32_t* __restrict__ xidx = nullptr, int xn = 0)
+{
+    constexpr int BM = 256, BN = 256, BK = 64, kCh = BK / 8;
+    constexpr int kPart = 256 * kCh;      // units (16 B) of one 256-row part of a stage: 32 KB
+    constexpr int kXBase = 3 * kPart;     // x buffers follow the three W buffers
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave & 1;
+    const int wn = wave >> 1;
+    const uint32_t rowb = (uint32_t)K * 2;
+
+    const int wrows = min(BN, N - n0);
+    const int xrows = min(BM, row_hi - m0);
+    const sgpr4 aW = rsrc_words(Wb + (size_t)n0 * K, (uint32_t)wrows * rowb);
+    const sgpr4 aX = kIdx ? rsrc_words(x, (uint32_t)xn * rowb) : rsrc_words(x + (size_t)m0 * K, (uint32_t)xrows * rowb);
+
+    // load j < 8: W unit (8 wave + j) 64 + lane; j >= 8: the same unit of x
+    uint32_t voff[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int u = (wave * 8 + (j & 7)) * 64 + lane;
+        const int r = u / kCh;
+        const int c = swz<kCh>(r, u % kCh);
+        if (j < 8) {
+            voff[j] = (uint32_t)min(r, wrows - 1) * rowb + c * 16;
+        } else {
+            uint32_t row = (uint32_t)min(r, xrows - 1);
+            if constexpr (kIdx) {
+                const int t = xidx[m0 + (int)row];
+                row = (uint32_t)(t < 0 ? 0 : (t >= xn ? xn - 1 : t));
+            }
+            voff[j] = row * rowb + c * 16;
+        }
+    }
+    auto issueW = [&](int j, int t, int wbuf) {
+        dma16_asm(aW, voff[j], (uint32_t)(sp.k0 + t * BK) * 2, lds + wbuf * kPart + (wave * 8 + j) * 64);
+    };
+    auto issueX = [&](int j, int t, int xbuf) {
+        dma16_asm(aX, voff[8 + j], (uint32_t)(sp.k0 + t * BK) * 2, lds + kXBase + xbuf * kPart + (wave * 8 + j) * 64);
+    };
+    // fragment q of k-step ks of the stage in W buffer wbuf and x buffer
+    // xbuf: q = 0 is W tile 0, 1..8 are x tiles 0..7, 9..15 are W tiles 1..7
+    auto read1 = [&](int q, int wbuf, int xbuf, int ks, uint4* fa, uint4* fb) {
+        const int cl = ks * 4 + (lane >> 4);
+        if (q >= 1 && q <= 8) {
+            const int r = wm * 128 + (q - 1) * 16 + (lane & 15);
+            fb[q - 1] = lds[kXBase + xbuf * kPart + r * kCh + swz<kCh>(r, cl)];
+        } else {
+            const int tt = q == 0 ? 0 : q - 8;
+            const int r = wn * 128 + tt * 16 + (lane & 15);
+            fa[tt] = lds[wbuf * kPart + r * kCh + swz<kCh>(r, cl)];
+        }
+    };
+
+    uint4 fa0[8], fb0[8], fa1[8], fb1[8];
+    const int nk = sp.klen / BK;
+
+    // Step 0 of stage t: MFMAs of k-step 0, the fragments of k-step 1, and
+    // W of stage t+2 into W buffer (t+2) % 3 (freed by the barrier of
+    // stage t-1).  Step 1: after two MFMAs, wait for stage t+1 (all but the
+    // 8 W loads just issued) and the barrier (every wave has read stage t);
+    // then the fragments of stage t+1's k-step 0 and x of stage t+2 into x
+    // buffer t % 2.  Loads past the last stage repeat the last one into a
+    // buffer that is not read again.
+    auto step0 = [&](auto zero, int t, int wb, int xb) {
+        constexpr bool kZ = decltype(zero)::value;
+        const int tl = min(t + 2, nk - 1);
+        const int wl = wb == 0 ? 2 : wb - 1;  // (t + 2) % 3
+        for_each_t([&](auto tc) {
+            constexpr int T = decltype(tc)::value;
+            mfma_agpr<T, kZ>(fa0[T / 8], fb0[T % 8]);
+            if constexpr (T % 4 == 3)
+                read1(T / 4, wb, xb, 1, fa1, fb1);
+            if constexpr (T % 8 == 5)  // after MFMAs 5, 13, ..., 61
+                issueW(T / 8, tl, wl);
+        }, std::make_integer_sequence<int, 64>{});
+    };
+    auto step1 = [&](int t, int wb, int xb) {
+        const int tl = min(t + 2, nk - 1);
+        const int wn1 = wb == 2 ? 0 : wb + 1;  // (t + 1) % 3
+        for_each_t([&](auto tc) {
+            constexpr int T = decltype(tc)::value;
+            mfma_agpr<T, false>(fa1[T / 8], fb1[T % 8]);
+            if constexpr (T == 1) {
+                wait_vmcnt<8>();
+                barrier_after_lds_reads();
+            }
+            if constexpr (T >= 2 && T < 34 && T % 2 == 0)
+                read1((T - 2) / 2, wn1, xb ^ 1, 0, fa0, fb0);
+            if constexpr (T % 8 == 3)  // after MFMAs 3, 11, ..., 59
+                issueX(T / 8, tl, xb);
+        }, std::make_integer_sequence<int, 64>{});
+    };
+
+    claim_agprs();
+    const int t1 = min(1, nk - 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        issueW(j, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        issueX(j, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        issueW(j, t1, 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        issueX(j, t1, 1);
+    wait_vmcnt<16>();  // stage 0 has landed
+    barrier_after_lds_reads();
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        read1(q, 0, 0, 0, fa0, fb0);
+    step0(std::true_type{}, 0, 0, 0);
+    step1(0, 0, 0);
+    int wb = 1;
+    for (int t = 1; t < nk; ++t) {
+        step0(std::false_type{}, t, wb, t & 1);
+        step1(t, wb, t & 1);
+        wb = wb == 2 ? 0 : wb + 1;
+    }
+    wait_vmcnt<0>();  // no load into LDS may outlive the block
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+    // x tile j outer, W tile i inner: the two 64-byte halves of a 128-byte
+    // line of y (tiles i and i+1 of one row) are stored back to back
+    for_each_t([&](auto uc) {
+        constexpr int U = decltype(uc)::value;
+        constexpr int j = U / 8, i = U % 8, T = 8 * i + j;
+        const int m = m0 + wm * 128 + j * 16 + (lane & 15);
+        const int n = n0 + wn * 128 + i * 16 + 4 * (lane >> 4);
+        const f32x4 v = read_agpr_tile<T>();
+        if (m < row_hi && n < N)
+            emit4(y + (size_t)m * N + n, v, sp.fold);
+    }, std::make_integer_sequence<int, 64>{});
+}
+
+__global__ void __launch_bounds__(256)
+    bigemm_tiled4(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ y, int M,
+                   int N, int K, Split sp, int tiles_m, int tiles_n, int group_m)
+{
+    __shared__ uint4 lds[5 * 256 * 8];
+    int tm, tn;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
+    tiled4_block(lds, x, W, y, tm * 256, M, tn * 256, N, K, sp);
+}
+
 // Grouped, persistent: the output tiles (slot, tn) -- slot enumerating the
 // m-blocks of the experts with more than cmin rows -- are counted on the
 // device and cut into 8 contiguous ranges, one per XCD (hardware hands block b
@@ -719,6 +961,16 @@ hipError_t run_tiled(const void* W, const void* x, int M, float* y, int N, int K
     return hipGetLastError();
 }
 
+hipError_t run_tiled4(const void* W, const void* x, int M, float* y, int N, int K, Split sp, hipStream_t stream)
+{
+    const int tiles_m = (M + 255) / 256;
+    const int tiles_n = (N + 255) / 256;
+    hipLaunchKernelGGL(bigemm_tiled4, dim3(tiles_m * tiles_n), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K, sp, tiles_m,
+                       tiles_n, 4);
+    return hipGetLastError();
+}
+
 template <int MB, int XR, int BKS, int NP>
 hipError_t run_stream(const void* W, const void* x, int M, float* y, int N, int K, Split sp,
                       int num_cus, hipStream_t stream)
@@ -865,7 +1117,7 @@ hipError_t launch_dense_split(const Plan& p, DenseKernel kind, const void* W, co
     case DenseKernel::kStream64:
         return run_stream_k<4, 64>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
     case DenseKernel::kTiled256:
-        return run_tiled<256, 256, 2, 4, 64, 2>(W, x, M, y, p.n, p.k, sp, stream);
+        return run_tiled4(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled128x256:
         return run_tiled<128, 256, 2, 4, 64, 3>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled128:
