@@ -78,8 +78,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 typedef int sgpr4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ sgpr4 rsrc_words(const void* base, uint32_t bytes)
 {
+    // the arguments are wave-uniform; readfirstlane makes that plain to the
+    // compiler, which must keep the descriptor in scalar registers
     const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return sgpr4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+    return sgpr4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
+                 __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
 }
 __device__ __forceinline__ void dma16_asm(const sgpr4& r, uint32_t voff, uint32_t soff, const void* lds_base)
 {
@@ -147,13 +151,21 @@ __device__ __forceinline__ int swz(int r, int c)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int clamp_off(int v, int R) { return v < 0 ? 0 : (v > R ? R : v); }
 
+// The four-wave kernel takes an expert's rows in blocks of 256: every whole
+// block, and a last partial block of at least 128 rows (a 256-row block at
+// half occupancy still outruns the 128-row tiles).  big_count: its blocks
+// for an expert with c rows; big_rows: the rows they cover (big = 0: the
+// kernel is not launched).  The other kernels serve the rest.
+__device__ __forceinline__ int big_count(int c) { return c / 256 + (c % 256 >= 128 ? 1 : 0); }
+__device__ __forceinline__ int big_rows(int c, int big) { return big > 0 ? min(c, big_count(c) * 256) : 0; }
+
 // Plan of a grouped call, built by every block in its own LDS: s_off[e] =
 // offsets[e] clamped to 0..R, and s_first[e] = the m-blocks of the experts
-// before e that the kernel serves (row count c with cmin < c <= cmax, each
-// taking ceil(c / bm) m-blocks, or one when bm is 0); s_first[E] is their
-// total.  Wave 0 scans 64 experts at a time.
+// before e that the kernel serves (row count c with cmin < c <= cmax; the
+// rows past big_rows(c, big), in ceil(rows / bm) m-blocks, or one when bm
+// is 0); s_first[E] is their total.  Wave 0 scans 64 experts at a time.
 __device__ void grouped_plan(const int32_t* __restrict__ off, int E, int R, int bm, int cmin,
-                             int cmax, int* s_off, int* s_first)
+                             int cmax, int big, int* s_off, int* s_first)
 {
     for (int e = threadIdx.x; e <= E; e += blockDim.x)
         s_off[e] = clamp_off(off[e], R);
@@ -164,7 +176,8 @@ __device__ void grouped_plan(const int32_t* __restrict__ off, int E, int R, int 
         for (int base = 0; base < E; base += 64) {
             const int e = base + lane;
             const int c = e < E ? max(s_off[e + 1] - s_off[e], 0) : 0;
-            const int mine = (c > cmin && c <= cmax) ? (bm > 0 ? (c - 1) / bm + 1 : 1) : 0;
+            const int rest = c - big_rows(c, big);
+            const int mine = (c > cmin && c <= cmax && rest > 0) ? (bm > 0 ? (rest - 1) / bm + 1 : 1) : 0;
             int v = mine;
             for (int d = 1; d < 64; d <<= 1) {
                 const int u = __shfl_up(v, d, 64);
@@ -184,7 +197,7 @@ __device__ void grouped_plan(const int32_t* __restrict__ off, int E, int R, int 
 // The expert owning m-block `slot` (0 <= slot < s_first[E]): the last e with
 // s_first[e] <= slot, which serves at least one m-block.  Sets its block
 // index and row range.
-__device__ __forceinline__ int grouped_slot(const int* s_off, const int* s_first, int E, int bm,
+__device__ __forceinline__ int grouped_slot(const int* s_off, const int* s_first, int E, int bm, int big,
                                             int slot, int* m0, int* hi)
 {
     int lo = 0, up = E;
@@ -195,9 +208,73 @@ __device__ __forceinline__ int grouped_slot(const int* s_off, const int* s_first
         else
             up = mid;
     }
-    *m0 = s_off[lo] + (slot - s_first[lo]) * bm;
-    *hi = s_off[lo] + max(s_off[lo + 1] - s_off[lo], 0);
+    const int c = max(s_off[lo + 1] - s_off[lo], 0);
+    *m0 = s_off[lo] + big_rows(c, big) + (slot - s_first[lo]) * bm;
+    *hi = s_off[lo] + c;
     return lo;
+}
+
+// The four-wave kernel's share of a grouped call, found without LDS (its
+// stages fill all of it): every wave scans the offsets itself, 64 experts at
+// a time.  An expert with c > cmin rows has big_count(c) blocks.
+__device__ __forceinline__ int big_blocks(const int32_t* __restrict__ off, int e, int E, int R, int cmin, int* lo)
+{
+    if (e >= E) {
+        *lo = 0;
+        return 0;
+    }
+    const int a = clamp_off(off[e], R);
+    const int c = max(clamp_off(off[e + 1], R) - a, 0);
+    *lo = a;
+    return c > cmin ? big_count(c) : 0;
+}
+
+__device__ int big_total(const int32_t* __restrict__ off, int E, int R, int cmin)
+{
+    const int lane = threadIdx.x & 63;
+    int total = 0;
+    for (int base = 0; base < E; base += 64) {
+        int lo;
+        int v = big_blocks(off, base + lane, E, R, cmin, &lo);
+        for (int d = 32; d > 0; d >>= 1)
+            v += __shfl_xor(v, d, 64);
+        total += v;
+    }
+    return __builtin_amdgcn_readfirstlane(total);
+}
+
+// Expert, first row and row end of 256-row block `slot` (0 <= slot <
+// big_total): the blocks are numbered expert by expert, in order.
+__device__ int big_slot(const int32_t* __restrict__ off, int E, int R, int cmin, int slot, int* m0, int* hi)
+{
+    const int lane = threadIdx.x & 63;
+    int carry = 0;
+    for (int base = 0; base < E; base += 64) {
+        int lo;
+        const int nb = big_blocks(off, base + lane, E, R, cmin, &lo);
+        int v = nb;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(v, d, 64);
+            if (lane >= d)
+                v += u;
+        }
+        const int chunk = __builtin_amdgcn_readfirstlane(__shfl(v, 63, 64));
+        if (slot < carry + chunk) {
+            const uint64_t hit = __ballot(carry + v > slot);
+            const int L = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+            const int first = carry + __shfl(v - nb, L, 64);
+            const int a = __shfl(lo, L, 64);
+            const int e = base + L;
+            const int c = max(clamp_off(off[e + 1], R) - a, 0);
+            *m0 = __builtin_amdgcn_readfirstlane(a + (slot - first) * 256);
+            *hi = __builtin_amdgcn_readfirstlane(a + c);
+            return __builtin_amdgcn_readfirstlane(e);
+        }
+        carry += chunk;
+    }
+    *m0 = 0;
+    *hi = 0;
+    return 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -649,6 +726,29 @@ __global__ void __launch_bounds__(256)
     tiled4_block(lds, x, W, y, tm * 256, M, tn * 256, N, K, sp);
 }
 
+// Grouped, persistent: the 256-row blocks (big_count) of the experts with
+// more than cmin rows, by 256 W rows; the tiles are cut into 8 contiguous ranges,
+// one per XCD, as in bigemm_tiled_grouped.  kIdx: x rows are read through
+// xidx.
+template <bool kIdx>
+__global__ void __launch_bounds__(256)
+    bigemm_tiled4_grouped(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ y,
+                          const int32_t* __restrict__ off, int E, int R, int N, int K, Split sp, int tiles_n,
+                          int cmin, const int32_t* __restrict__ xidx, int xn)
+{
+    __shared__ uint4 lds[5 * 256 * 8];
+    const int total = big_total(off, E, R, cmin) * tiles_n;
+    const int xcd = blockIdx.x % 8;
+    const int per_xcd = gridDim.x / 8;
+    const int t_end = (int)((long long)total * (xcd + 1) / 8);
+    for (int t = (int)((long long)total * xcd / 8) + (int)(blockIdx.x / 8); t < t_end; t += per_xcd) {
+        int m0, hi;
+        const int e = big_slot(off, E, R, cmin, t / tiles_n, &m0, &hi);
+        barrier_after_lds_reads();  // every wave is done with the previous tile's stages
+        tiled4_block<kIdx>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K, sp, xidx, xn);
+    }
+}
+
 // Grouped, persistent: the output tiles (slot, tn) -- slot enumerating the
 // m-blocks of the experts with more than cmin rows -- are counted on the
 // device and cut into 8 contiguous ranges, one per XCD (hardware hands block b
@@ -659,21 +759,21 @@ template <int BM, int BN, int WM, int WN, int BK, int NS, bool kIdx>
 __global__ void __launch_bounds__(WM * WN * 64)
     bigemm_tiled_grouped(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                          float* __restrict__ y, const int32_t* __restrict__ off, int E, int R,
-                         int N, int K, Split sp, int tiles_n, int cmin,
+                         int N, int K, Split sp, int tiles_n, int cmin, int big,
                          const int32_t* __restrict__ xidx, int xn)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     __shared__ uint4 lds[NS * C::kStageUnits];
     __shared__ int s_off[kMaxExperts + 1];
     __shared__ int s_first[kMaxExperts + 1];
-    grouped_plan(off, E, R, BM, cmin, 0x7fffffff, s_off, s_first);
+    grouped_plan(off, E, R, BM, cmin, 0x7fffffff, big, s_off, s_first);
     const int total = s_first[E] * tiles_n;
     const int xcd = blockIdx.x % 8;
     const int per_xcd = gridDim.x / 8;
     const int t_end = (int)((long long)total * (xcd + 1) / 8);
     for (int t = (int)((long long)total * xcd / 8) + (int)(blockIdx.x / 8); t < t_end; t += per_xcd) {
         int m0, hi;
-        const int e = grouped_slot(s_off, s_first, E, BM, t / tiles_n, &m0, &hi);
+        const int e = grouped_slot(s_off, s_first, E, BM, big, t / tiles_n, &m0, &hi);
         barrier_after_lds_reads();  // every wave is done with the previous tile's stages
         tiled_block<BM, BN, WM, WN, BK, NS, kIdx>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * BN,
                                                   N, K, sp, xidx, xn);
@@ -931,7 +1031,7 @@ __global__ void __launch_bounds__((MB + NP) * 64)
     __shared__ int first[kMaxExperts + 1];
     __shared__ int elist[kMaxExperts];
     // compact, ascending list of the experts this kernel serves
-    grouped_plan(off, E, R, 0, 0, cmax, sh_off, first);
+    grouped_plan(off, E, R, 0, 0, cmax, 0, sh_off, first);
     const int count = first[E];
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         const int c = sh_off[e + 1] - sh_off[e];
@@ -1020,7 +1120,7 @@ hipError_t run_stream_grouped(const void* W, const void* x, const int32_t* off, 
 
 template <int BM, int BN, int WM, int WN, int BK, int NS>
 hipError_t run_tiled_grouped(const void* W, const void* x, const int32_t* off, int E, int R,
-                             float* y, int N, int K, Split sp, int cmin, int num_cus,
+                             float* y, int N, int K, Split sp, int cmin, int big, int num_cus,
                              const int32_t* xidx, int xn, hipStream_t stream)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
@@ -1034,11 +1134,30 @@ hipError_t run_tiled_grouped(const void* W, const void* x, const int32_t* off, i
     if (xidx)
         hipLaunchKernelGGL((bigemm_tiled_grouped<BM, BN, WM, WN, BK, NS, true>), dim3(grid), dim3(C::kThreads),
                            0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y,
-                           off, E, R, N, K, sp, tiles_n, cmin, xidx, xn);
+                           off, E, R, N, K, sp, tiles_n, cmin, big, xidx, xn);
     else
         hipLaunchKernelGGL((bigemm_tiled_grouped<BM, BN, WM, WN, BK, NS, false>), dim3(grid), dim3(C::kThreads),
                            0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y,
-                           off, E, R, N, K, sp, tiles_n, cmin, xidx, xn);
+                           off, E, R, N, K, sp, tiles_n, cmin, big, xidx, xn);
+    return hipGetLastError();
+}
+
+// The 256-row blocks of the experts with more than cmin rows: one block
+// per CU (its LDS holds one), a multiple of 8.
+hipError_t run_tiled4_grouped(const void* W, const void* x, const int32_t* off, int E, int R, float* y, int N,
+                              int K, Split sp, int cmin, int num_cus, const int32_t* xidx, int xn,
+                              hipStream_t stream)
+{
+    const int tiles_n = (N + 255) / 256;
+    const int grid = (num_cus + 7) / 8 * 8;
+    if (xidx)
+        hipLaunchKernelGGL(bigemm_tiled4_grouped<true>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, off, E, R, N, K,
+                           sp, tiles_n, cmin, xidx, xn);
+    else
+        hipLaunchKernelGGL(bigemm_tiled4_grouped<false>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, off, E, R, N, K,
+                           sp, tiles_n, cmin, xidx, xn);
     return hipGetLastError();
 }
 
@@ -1154,9 +1273,10 @@ hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, floa
 hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int32_t* offsets,
                           int R, float* y, const int32_t* xidx, int xn, hipStream_t stream)
 {
-    // Experts with 1..smax rows go to the streaming kernel, the rest to the
-    // tiled kernel; both realise the same tree, so the split point only
-    // moves work, never bits.
+    // Experts with 1..smax rows go to the streaming kernel; of the others,
+    // 256-row blocks (whole, or at least half full) go to the four-wave
+    // kernel and the remaining rows to the tiled kernel.  All realise the same tree, so the split points
+    // only move work, never bits.
     const int smax = p.stream_max_m < 16 ? p.stream_max_m : 16;
     const int klen = p.k / p.splits;
     for (int s = 0; s < p.splits; ++s) {
@@ -1174,7 +1294,17 @@ hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int
             if (err != hipSuccess)
                 return err;
         }
-        err = run_tiled_grouped<128, 128, 2, 2, 64, 2>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, xidx, xn, stream);
+        // 256-row blocks of the experts with at least 128 rows, launched when
+        // the experts average 64 rows or more (below that, few experts reach
+        // 128 rows and an empty launch costs more than it saves)
+        const int big = (R >= 128 && R >= 64 * p.experts) ? 256 : 0;
+        if (big) {
+            err = run_tiled4_grouped(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, xidx, xn, stream);
+            if (err != hipSuccess)
+                return err;
+        }
+        err = run_tiled_grouped<128, 128, 2, 4, 64, 2>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, big,
+                                                       p.num_cus, xidx, xn, stream);
         if (err != hipSuccess)
             return err;
     }

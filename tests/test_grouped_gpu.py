@@ -130,3 +130,44 @@ def test_indexed_rows_equal_gathered_rows(gpu, experts, tokens):
     y_bad = bits32(g.run_indexed(to_dev(x_tok), torch.as_tensor(bad, device=DEV), offd))
     y_cl = bits32(g(to_dev(np.ascontiguousarray(x_tok[clamped])), offd))
     assert_bits_equal(y_bad, y_cl, "out-of-range indices clamp, T=%d" % tokens)
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_block_boundaries_every_row_equals_dense(gpu, experts, name):
+    """Experts on both sides of the 256-row blocks of the four-wave kernel
+    (127 .. 640 rows, a 3000-row one) and of the streaming kernel (1, 16, 17):
+    rows at every block edge equal the dense rows of their expert, bit
+    for bit, for plain and (up) indexed rows; sampled rows pass the oracle."""
+    n, k = SHAPES[name]
+    w, wd = experts[name]
+    g = gpu.GroupedGemm(wd)
+    counts = np.zeros(E, np.int64)
+    sizes = [127, 128, 129, 255, 256, 257, 383, 384, 385, 511, 512, 640, 17, 16, 1, 3000, 1500]
+    counts[np.arange(0, 2 * len(sizes), 2)] = sizes  # every other expert, so empty ones sit between
+    off = np.zeros(E + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    r = int(off[-1])
+    assert r >= 64 * E  # the four-wave kernel takes part
+    x = synth.normal_bf16(190 + k, (r, k))
+    offd = torch.as_tensor(off, device=DEV)
+    y = g(to_dev(x), offd)
+    torch.cuda.synchronize()
+    yb = bits32(y)
+    rows = synth.probe_rows(191, r, 48)
+    yr, a = oracle.grouped_f64(x, w, off, rows=rows)
+    assert_parity(y.cpu().numpy()[rows], yr, a, "block boundaries %s" % name)
+    for e in np.nonzero(counts)[0]:
+        e = int(e)
+        lo, hi = int(off[e]), int(off[e + 1])
+        edges = sorted({lo + d for d in (0, 127, 128, 255, 256, 257, 383, 384, 511, 512) if lo + d < hi} | {hi - 1})
+        dense = gpu.Gemm(wd[e])
+        yd = bits32(dense(to_dev(x[edges])))
+        for j, rr in enumerate(edges):
+            assert_bits_equal(yb[rr], yd[j], "expert %d (%d rows) row %d" % (e, hi - lo, rr - lo))
+    if name == "up":
+        # the same rows read through an index from a shuffled copy of x
+        perm = synth.rng(192).permutation(r)
+        x_store = np.empty_like(x)
+        x_store[perm] = x
+        yi = bits32(g.run_indexed(to_dev(x_store), torch.as_tensor(perm.astype(np.int32), device=DEV), offd))
+        assert_bits_equal(yb, yi, "indexed rows across the block boundaries")

@@ -1,4 +1,5 @@
-"""The built code of the four-wave 256x256 kernel, checked on the CPU.
+"""The built code of the four-wave 256x256 kernels (dense and grouped),
+checked on the CPU.
 
 Its accumulators live in a0..a255, written only by inline-asm MFMAs and read
 only by the epilogue; the compiler does not know they are live.  So the
@@ -19,7 +20,10 @@ import pytest
 from invariant_bi_gemm_amd import build
 
 SRC = os.path.join(build.CSRC, "bigemm_kernels.hip")
-KERNEL = "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4E"
+# the dense kernel and the grouped one (plain and indexed rows)
+KERNELS = ["_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4E",
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb0E",
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1E"]
 MFMA_AGPR = re.compile(r"v_mfma_f32_16x16x32_bf16 a\[\d+:\d+\], v\[\d+:\d+\], v\[\d+:\d+\], (a\[\d+:\d+\]|0)$")
 AGPR = re.compile(r"\ba\d+\b|\ba\[\d+:\d+\]")
 
@@ -57,8 +61,9 @@ def body(asm, name):
     return m.group(1), lines
 
 
-def test_accumulation_registers_only_in_the_chains(asm):
-    _, ins = body(asm, KERNEL)
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_accumulation_registers_only_in_the_chains(asm, kernel):
+    _, ins = body(asm, kernel)
     bad = [t for t in ins if AGPR.search(t) and not MFMA_AGPR.match(t)
            and not re.match(r"v_accvgpr_read_b32 v\d+, a\d+$", t)]
     assert not bad, "compiler-placed accumulation-register use: %s" % bad[:5]
@@ -66,8 +71,9 @@ def test_accumulation_registers_only_in_the_chains(asm):
     assert sum(1 for t in ins if t.startswith("v_accvgpr_read_b32")) == 256
 
 
-def test_descriptor_reserves_the_accumulators(asm):
-    name, _ = body(asm, KERNEL)
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_descriptor_reserves_the_accumulators(asm, kernel):
+    name, _ = body(asm, kernel)
     d = asm[asm.index(".amdhsa_kernel " + name):]
     d = d[:d.index(".end_amdhsa_kernel")]
     nv = int(re.search(r"\.amdhsa_next_free_vgpr (\d+)", d).group(1))
@@ -82,8 +88,9 @@ def test_no_kernel_spills_to_scratch(asm):
     assert all(int(n) == 0 for _, n in sizes), [k for k, n in sizes if int(n)]
 
 
-def test_mfma_inputs_not_written_just_before(asm):
-    _, ins = body(asm, KERNEL)
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_mfma_inputs_not_written_just_before(asm, kernel):
+    _, ins = body(asm, kernel)
     for i, t in enumerate(ins):
         if not t.startswith("v_mfma"):
             continue
@@ -95,9 +102,14 @@ def test_mfma_inputs_not_written_just_before(asm):
                 assert not dst & src, "vector write right before an MFMA reads it: %r then %r" % (p, t)
 
 
-def test_results_read_after_the_wait_states(asm):
-    _, ins = body(asm, KERNEL)
-    first = next(i for i, t in enumerate(ins) if t.startswith("v_accvgpr_read_b32"))
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_results_read_after_the_wait_states(asm, kernel):
+    _, ins = body(asm, kernel)
+    reads = [i for i, t in enumerate(ins) if t.startswith("v_accvgpr_read_b32")]
+    first = reads[0]
     last_mfma = max(i for i, t in enumerate(ins[:first]) if t.startswith("v_mfma"))
     nops = sum(int(t.split()[1]) + 1 for t in ins[last_mfma + 1:first] if t.startswith("s_nop"))
     assert nops >= 18, "only %d wait states between the last MFMA and the first result read" % nops
+    # and no MFMA among the result reads (a grouped kernel loops over tiles:
+    # the next tile's MFMAs come after all 256 reads)
+    assert not any(t.startswith("v_mfma") for t in ins[first:reads[-1]])

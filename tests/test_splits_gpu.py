@@ -121,3 +121,35 @@ def test_grouped_uses_the_dense_split_tree(gpu, tmp_path):
             assert_bits_equal(y[lo:hi], bits32(dense(to_dev(x[lo:hi]))), "expert %d" % ex)
     finally:
         assert lib.bi_gemm_load_pins(bg.PIN_TABLE.encode()) == 0
+
+
+def test_grouped_big_blocks_use_the_dense_split_tree(gpu, tmp_path):
+    """With an S = 2 pin and experts of 2 .. 700 rows (256-row blocks of the
+    four-wave kernel, remainders, streaming rows), every row equals the dense
+    S = 2 result of its expert."""
+    import invariant_bi_gemm_amd as bg
+
+    e, n, k = 8, 256, 1024
+    table = tmp_path / "pins.txt"
+    table.write_text("version 7\ngfx950 %d %d 2 16\n" % (n, k))
+    lib = bg.load()
+    assert lib.bi_gemm_load_pins(str(table).encode()) == 0
+    try:
+        w = synth.normal_bf16(222, (e, n, k), 0.02)
+        wd = to_dev(w)
+        gg = gpu.GroupedGemm(wd)
+        assert gg.pin["splits"] == 2
+        counts = np.array([300, 0, 700, 129, 2, 0, 256, 5])
+        off = np.zeros(e + 1, np.int32)
+        off[1:] = np.cumsum(counts)
+        assert off[-1] >= 64 * e  # the four-wave kernel takes part
+        x = synth.normal_bf16(223, (int(off[-1]), k))
+        y = bits32(gg(to_dev(x), torch.as_tensor(off, device=DEV)))
+        for ex in range(e):
+            if counts[ex] == 0:
+                continue
+            dense = gpu.Gemm(wd[ex])
+            lo, hi = int(off[ex]), int(off[ex + 1])
+            assert_bits_equal(y[lo:hi], bits32(dense(to_dev(x[lo:hi]))), "expert %d" % ex)
+    finally:
+        assert lib.bi_gemm_load_pins(bg.PIN_TABLE.encode()) == 0
