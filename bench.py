@@ -275,7 +275,7 @@ def run_moe(args, bg):
         ach = by / (per[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": None,
-                 "kernel": "grouped %s GEMM at T=%d (streaming + tiled grouped kernels)" % (name, t),
+                 "kernel": "grouped %s GEMM at T=%d (all its grouped kernels)" % (name, t),
                  "launches_per_step": 1, "avg_launch_us": per[dom] * 1e3})
     cpu = None
     if not args.no_cpu_baseline:
