@@ -52,6 +52,24 @@ def test_integer_exact(gpu, n, k):
         assert np.all(np.abs(got) <= 9 * k)
 
 
+@pytest.mark.parametrize("m", [4100, 8195])
+def test_integer_exact_large_m(gpu, m):
+    """x, W in {-3..3} through the 256x256 four-wave kernel (one round of
+    blocks plus a ragged 4-row tail; two rounds plus a 3-row tail): exact
+    integers on sampled rows, the tail rows included."""
+    n, k = 4096, 1024
+    w = synth.int_bf16(51, (n, k))
+    xs = synth.int_bf16(52, (m, k))
+    g = gpu.Gemm(to_dev(w))
+    assert g.kernel_name(m) == "bigemm_tiled<256x256>"
+    y = g(to_dev(xs))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([synth.probe_rows(53 + m, m, 24), np.arange(m - 4, m)]))
+    ref = oracle.gemm_i64(xs, w, rows=rows)
+    got = y.cpu().numpy()[rows]
+    assert np.array_equal(got, ref.astype(np.float32)), "n=%d k=%d M=%d" % (n, k, m)
+
+
 @pytest.mark.parametrize("m", [1, 3, 16, 17, 31, 64, 100, 255, 256, 257, 700, 1024, 1100])
 def test_tiles_and_ragged_tails(gpu, m):
     """N=768 (three 256-wide or six 128-wide column blocks), K=1024: several
