@@ -58,7 +58,10 @@ typedef struct bi_attn *bi_attn_t;
  * multiple of 64 within 64 .. 16384: the pinned split stride), and the
  * largest batch and sequence length it serves (they size its workspace:
  * max_batch * Hq * ceil(max_seq_len / S) * (D + 2) floats of split partials
- * and a work list of max_batch + 1 ints, allocated here once).  1 <= max_batch, 1 <= max_seq_len <= 2^24.
+ * and a work list of max_batch + 1 ints, allocated here once).  1 <= max_batch, 1 <= max_seq_len <= 2^24,
+ * and S * Hkv * D * 2 < 2^32 (one split of a kv head is addressed with 32-bit byte offsets; a split's
+ * reads end at its last key, so keys past it read as zero and never outside the caches).
+ * BI_ERR_INVALID_ARGUMENT otherwise.
  */
 bi_status_t bi_attn_create(int Hq, int Hkv, int D, int split, int max_batch, int max_seq_len,
                            bi_attn_t *out);

@@ -60,6 +60,9 @@ bi_status_t bi_attn_create(int Hq, int Hkv, int D, int split, int max_batch, int
         return api_fail(BI_ERR_INVALID_ARGUMENT, "Hq / Hkv must be 1, 2, 4 or 8");
     if (split < 64 || split > 16384 || split % 64 != 0)
         return api_fail(BI_ERR_INVALID_ARGUMENT, "the split size must be a multiple of 64 within 64..16384");
+    // the kernel addresses one split's keys of a kv head with 32-bit offsets
+    if ((long long)split * Hkv * D * 2 >= (1LL << 32))
+        return api_fail(BI_ERR_INVALID_ARGUMENT, "split * Hkv * D * 2 bytes must stay below 4 GiB");
     if (max_batch < 1 || max_batch > 65535 || max_seq_len < 1 || max_seq_len > (1 << 24))
         return api_fail(BI_ERR_INVALID_ARGUMENT, "need 1 <= max_batch <= 65535 and 1 <= max_seq_len <= 2^24");
     const long long splits = (max_seq_len + (long long)split - 1) / split;

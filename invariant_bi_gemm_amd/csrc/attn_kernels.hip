@@ -62,6 +62,40 @@ __device__ __forceinline__ void widen8(const uint4& v, float* f)
     }
 }
 
+// A raw buffer resource over `bytes` bytes at `base`: a load whose offset
+// reaches past the end returns zeros (the hardware's range check on the
+// per-lane offset), which is what a key past the end of a split must read.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// Sum over the 16 lanes of a row for n values at once: the same four DPP
+// levels as row_sum16, each level applied to all n values before the next,
+// so that no add waits on the one just before it.
+template <int N>
+__device__ __forceinline__ void row_sum16_n(float* x)
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] = x[i] + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[i]), 0x128, 0xf, 0xf, false));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] = x[i] + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[i]), 0x124, 0xf, 0xf, false));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] = x[i] + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[i]), 0x122, 0xf, 0xf, false));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] = x[i] + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[i]), 0x121, 0xf, 0xf, false));
+}
+
 // Sequence b's length, clamped as the kernels read it.
 __device__ __forceinline__ int seq_len(const int32_t* __restrict__ seq_start, int b, int Ntok, int max_len,
                                        int* t0out)
@@ -149,8 +183,13 @@ __global__ void __launch_bounds__(kThreads)
     const int cnt = min(S, n - first);
     const int Hq = Hkv * G;
     const size_t row16 = (size_t)Hkv * (kHeadDim / 8);  // uint4 per token row
-    const uint4* kb = k + (size_t)(t0 + first) * row16 + (size_t)kvh * (kHeadDim / 8) + r;
-    const uint4* vb = v + (size_t)(t0 + first) * row16 + (size_t)kvh * (kHeadDim / 8) + r;
+    // the split's keys and values of this kv head as buffers that end after
+    // key cnt-1; lane r reads bytes 16r .. 16r+15 of a key's head row
+    const uint32_t rowb = (uint32_t)row16 * 16;
+    const __amdgpu_buffer_rsrc_t rK =
+        make_rsrc(k + (size_t)(t0 + first) * row16 + (size_t)kvh * (kHeadDim / 8), (uint32_t)cnt * rowb);
+    const __amdgpu_buffer_rsrc_t rV =
+        make_rsrc(v + (size_t)(t0 + first) * row16 + (size_t)kvh * (kHeadDim / 8), (uint32_t)cnt * rowb);
 
     // query slices of the G heads, dims 8r .. 8r+7, as four bf16 pairs
     uint32_t qp[G][4];
@@ -175,27 +214,34 @@ __global__ void __launch_bounds__(kThreads)
     // group grp takes keys grp, grp+16, ..., kUnroll at a time in ascending order
     constexpr int kUnroll = unroll_of<G>();
     for (int t = grp; t < cnt; t += kGroups * kUnroll) {
+        // keys past the split read as zeros (the buffers end there)
         uint4 kk[kUnroll], vv[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int tt = t + kGroups * u;
-            kk[u] = tt < cnt ? kb[(size_t)tt * row16] : uint4{0u, 0u, 0u, 0u};
-            vv[u] = tt < cnt ? vb[(size_t)tt * row16] : uint4{0u, 0u, 0u, 0u};
+            const uint32_t off = (uint32_t)(t + kGroups * u) * rowb + (uint32_t)r * 16;
+            kk[u] = load16(rK, off);
+            vv[u] = load16(rV, off);
         }
         float sc[kUnroll][G];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint32_t kp[4] = {kk[u].x, kk[u].y, kk[u].z, kk[u].w};
-            const bool live = t + kGroups * u < cnt;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 float a = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     a = dot2(kp[e], qp[g][e], a);
-                a = row_sum16(a);
-                sc[u][g] = live ? a * scale_l2 : -INFINITY;
+                sc[u][g] = a;
             }
+        }
+        row_sum16_n<kUnroll * G>(&sc[0][0]);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const bool live = t + kGroups * u < cnt;
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                sc[u][g] = live ? sc[u][g] * scale_l2 : -INFINITY;
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
