@@ -156,6 +156,7 @@ def test_rmsnorm_empty_launches_nothing(lib):
     (32, 8, 128, 256, 0, 1024),     # max_batch = 0
     (32, 8, 128, 256, 70000, 1024),  # max_batch above 65535
     (32, 8, 128, 256, 4, 0),        # max_seq_len = 0
+    (2048, 2048, 128, 8192, 4, 1024),  # a split of a kv head spans 4 GiB: past 32-bit offsets
 ])
 def test_attn_create_rejects(lib, hq, hkv, d, split, mb, ml):
     out = P()
