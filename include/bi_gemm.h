@@ -94,12 +94,17 @@ void bi_gemm_set_strict(int strict);
  * Create a dense handle for a layer with weight W.
  *   N, K: layer shape; N % 16 == 0, K % 64 == 0, both > 0, N*K < 2^31.
  *   W:    device pointer, bf16 [N,K] row-major (nn.Linear layout, K
- *         contiguous), 16-byte aligned.  BORROWED: the caller keeps it alive
- *         and unchanged until bi_gemm_destroy.
+ *         contiguous), 16-byte aligned.  COPIED: create packs W into the
+ *         handle's own device memory (N*K*2 bytes, freed by bi_gemm_destroy)
+ *         in the layout the kernels stream, each 64-wide k range of all N
+ *         rows contiguous: element (n, k) at (k/64)*64N + 64n + k%64.  The
+ *         copy is bitwise.  W may be freed or changed once create returns.
  *   out:  receives the handle.
- * The tree is looked up by (device arch, N, K) and frozen here.  No kernel
- * runs and no device memory is allocated.  The current HIP device must be a
- * gfx950; the handle is bound to it.
+ * The tree is looked up by (device arch, N, K) and frozen here.  Create
+ * synchronizes the device (every earlier write to W has completed when the
+ * copy starts), runs the packing kernel and waits for it; it fails with
+ * BI_ERR_OUT_OF_MEMORY when the copy cannot be allocated.  The current HIP
+ * device must be a gfx950; the handle is bound to it.
  */
 bi_status_t bi_gemm_create(int N, int K, const void *W, bi_gemm_t *out);
 
@@ -132,8 +137,9 @@ bi_status_t bi_gemm_run(bi_gemm_t h, const void *x, int M, float *y, void *strea
 
 /*
  * Create a grouped (MoE expert) handle: E experts, each with weight
- * W[e] = W + e*N*K (bf16 [E,N,K], row-major, 16-byte aligned, BORROWED as
- * above).  Every expert uses the tree of the dense layer (N, K), so a row
+ * W[e] = W + e*N*K (bf16 [E,N,K], row-major, 16-byte aligned, COPIED as
+ * above: E*N*K*2 bytes, each expert packed on its own).  Every expert uses
+ * the tree of the dense layer (N, K), so a row
  * computed here has the bits it would have in a dense handle over W[e].
  */
 bi_status_t bi_grouped_gemm_create(int E, int N, int K, const void *W, bi_gemm_t *out);
@@ -168,7 +174,8 @@ bi_status_t bi_grouped_gemm_run(bi_gemm_t h, const void *x, const int32_t *exper
 bi_status_t bi_grouped_gemm_run_indexed(bi_gemm_t h, const void *x, int x_rows, const int32_t *row_index,
                                         const int32_t *expert_offsets, int R, float *y, void *stream);
 
-/* Release a handle (dense or grouped).  NULL is ignored. */
+/* Release a handle (dense or grouped) and its packed weights; waits for the
+ * device work that may still read them.  NULL is ignored. */
 void bi_gemm_destroy(bi_gemm_t h);
 
 /* The tree and tiling of a handle. */

@@ -101,9 +101,10 @@ bi_status_t bi_moe_combine(const float *o, int R, const int32_t *ids, const floa
 /*
  * The whole expert layer on one device.  W_router: bf16 [E, H]; W_up: bf16
  * [E, 2I, H] (gate rows 0..I-1 then up rows of each expert); W_down: bf16
- * [E, H, I]; all borrowed until destroy, 16-byte aligned.  The router and
- * the two expert projections are bi_gemm handles with the pins of their
- * shapes.  Create allocates the layer's workspace for up to max_tokens
+ * [E, H, I]; all 16-byte aligned.  The router and the two expert
+ * projections are bi_gemm handles with the pins of their shapes, so create
+ * packs copies of all three weights (bi_gemm_create) and they may be freed
+ * once it returns.  Create allocates the layer's workspace for up to max_tokens
  * tokens once; run allocates nothing.  Limits: E a multiple of 16 within
  * 16..1024; 1 <= k <= min(E, 64); H a multiple of 64; I a multiple of 64;
  * 1 <= max_tokens, max_tokens*k*max(H, 2I) < 2^31.

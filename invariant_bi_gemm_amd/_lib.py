@@ -141,8 +141,9 @@ def _need(t, dtype, ndim, what):
 class Gemm:
     """A dense layer handle: ``y = x @ W.T`` with batch-invariant rows.
 
-    ``W`` is a contiguous bf16 [N, K] CUDA tensor; the handle keeps a reference
-    to it (the C library borrows the memory).  ``pin`` (optional) is a dict
+    ``W`` is a contiguous bf16 [N, K] CUDA tensor.  The C library packs its
+    own copy at create, so W may be freed or changed afterwards.  ``pin``
+    (optional) is a dict
     with ``splits`` and ``stream_max_m`` to override the pin table.
     """
 
@@ -152,7 +153,6 @@ class Gemm:
         lib = load()
         _need(W, torch.bfloat16, 2, "W")
         self.n, self.k = (int(v) for v in W.shape)
-        self._W = W
         self._lib = lib
         h = ctypes.c_void_p()
         with torch.cuda.device(W.device):
@@ -211,7 +211,8 @@ class Gemm:
 
 
 class GroupedGemm:
-    """MoE experts: ``W`` is bf16 [E, N, K]; rows of x are grouped by expert."""
+    """MoE experts: ``W`` is bf16 [E, N, K] (copied at create); rows of x are
+    grouped by expert."""
 
     def __init__(self, W):
         import torch
@@ -219,7 +220,6 @@ class GroupedGemm:
         lib = load()
         _need(W, torch.bfloat16, 3, "W")
         self.e, self.n, self.k = (int(v) for v in W.shape)
-        self._W = W
         self._lib = lib
         h = ctypes.c_void_p()
         with torch.cuda.device(W.device):
@@ -370,7 +370,8 @@ class MoeLayer:
     """The expert layer: router, top-k, grouping, up projection, SwiGLU, down
     projection and the weighted combine, every token's output independent of
     the batch.  ``W_router`` bf16 [E, H], ``W_up`` bf16 [E, 2I, H] (gate rows
-    then up rows), ``W_down`` bf16 [E, H, I]; the handle keeps references."""
+    then up rows), ``W_down`` bf16 [E, H, I]; the handle packs its own copies
+    at create."""
 
     def __init__(self, W_router, W_up, W_down, k: int, max_tokens: int):
         import torch
@@ -384,7 +385,6 @@ class MoeLayer:
         self.k, self.max_tokens = int(k), int(max_tokens)
         if tuple(W_up.shape) != (self.e, 2 * self.i, self.h) or tuple(W_down.shape) != (self.e, self.h, self.i):
             raise ValueError("W_up must be [E, 2I, H] and W_down [E, H, I]")
-        self._w = (W_router, W_up, W_down)
         self._lib = lib
         h = ctypes.c_void_p()
         with torch.cuda.device(W_router.device):

@@ -190,7 +190,7 @@ bi_status_t current_device(int* dev, DeviceInfo* info)
 struct bi_gemm {
     uint32_t magic;
     int device;
-    const void* W;
+    void* W;  // the handle's packed copy of the weights (slab-major), owned
     bigemm::Plan plan;
     bi_pin_info pin;
 };
@@ -272,12 +272,35 @@ bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info*
         }
     }
 
+    // The packed copy of W: every earlier write to W on the device has
+    // completed when the copy starts, and the copy has when create returns,
+    // so the caller may then free or change W.
+    const size_t wbytes = (size_t)(E > 0 ? E : 1) * N * K * 2;
+    void* packed = nullptr;
+    hipError_t he = hipDeviceSynchronize();
+    if (he != hipSuccess)
+        return fail(BI_ERR_HIP, std::string("hipDeviceSynchronize: ") + hipGetErrorString(he));
+    if (hipMalloc(&packed, wbytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(BI_ERR_OUT_OF_MEMORY, "out of device memory for the packed weights (" +
+                                              std::to_string(wbytes) + " bytes)");
+    }
+    he = bigemm::pack_weights(W, packed, E, N, K, nullptr);
+    if (he == hipSuccess)
+        he = hipStreamSynchronize(nullptr);
+    if (he != hipSuccess) {
+        (void)hipFree(packed);
+        return fail(BI_ERR_HIP, std::string("packing W: ") + hipGetErrorString(he));
+    }
+
     bi_gemm* h = new (std::nothrow) bi_gemm;
-    if (!h)
+    if (!h) {
+        (void)hipFree(packed);
         return fail(BI_ERR_OUT_OF_MEMORY, "out of host memory");
+    }
     h->magic = kMagic;
     h->device = dev;
-    h->W = W;
+    h->W = packed;
     h->plan.n = N;
     h->plan.k = K;
     h->plan.experts = E;
@@ -303,6 +326,7 @@ bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info*
         std::lock_guard<std::mutex> g(g_live_mu);
         g_live.insert(h);
     } catch (...) {
+        (void)hipFree(h->W);
         delete h;
         return fail(BI_ERR_OUT_OF_MEMORY, "out of host memory");
     }
@@ -488,6 +512,8 @@ void bi_gemm_destroy(bi_gemm_t hh)
             return;
     }
     hh->magic = 0;
+    // hipFree waits for the device work that may still read the weights
+    (void)hipFree(hh->W);
     delete hh;
 }
 

@@ -49,7 +49,10 @@ const char* dense_kernel_name(DenseKernel k);
 bi_status_t api_fail(bi_status_t st, const char* msg);
 bi_status_t api_device(int* dev, int* num_cus);
 
-// Launchers (bigemm_kernels.hip).  They assume validated arguments.
+// Launchers (bigemm_kernels.hip).  They assume validated arguments.  The
+// weights they take are packed by pack_weights: slab-major, element (n, k)
+// of an [N, K] matrix at index (k / 64) * 64N + 64n + k % 64.
+hipError_t pack_weights(const void* W, void* packed, int E, int N, int K, hipStream_t stream);
 hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, float* y,
                         hipStream_t stream);
 // xidx (optional): row i of the grouped x is row xidx[i] of x (xn rows).

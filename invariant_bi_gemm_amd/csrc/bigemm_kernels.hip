@@ -92,6 +92,24 @@ __device__ __forceinline__ void dma16_asm(const sgpr4& r, uint32_t voff, uint32_
                  : "memory");
 }
 
+// Packed weights.  A handle holds W (per expert) slab-major: slab s is the
+// k range 64s .. 64s+63 of all N rows, one contiguous [N][64] block, so
+// element (n, k) sits at bf16 index (k / 64) * 64N + 64n + k % 64.  A stage
+// of BN rows is then BN * 128 contiguous bytes instead of 128 bytes in each
+// of BN rows 2K bytes apart, and the blocks that run together read one
+// contiguous region.  The offsets below are in bytes, relative to row n0 of
+// slab 0 (base W + 64 n0).
+constexpr int kSlab = 64;
+// 16-byte chunk c (0..7) of row n0 + r within a slab
+__device__ __forceinline__ uint32_t wpk_row(int r, int c) { return (uint32_t)r * (kSlab * 2) + (uint32_t)c * 16; }
+// the slab that starts at k (a multiple of 64)
+__device__ __forceinline__ uint32_t wpk_slab(int k, int N) { return (uint32_t)k * (uint32_t)N * 2; }
+// bytes from row n0 of slab 0 to the end of row n0 + rows - 1 of the last slab
+__device__ __forceinline__ uint32_t wpk_bytes(int N, int K, int rows)
+{
+    return wpk_slab(K - kSlab, N) + (uint32_t)rows * (kSlab * 2);
+}
+
 // Workgroup barrier for the pipelined loops.  __syncthreads() would add a
 // release fence, which the compiler implements by draining every outstanding
 // direct-to-LDS load (vmcnt(0)) -- including the prefetch of later stages.
@@ -295,7 +313,7 @@ struct TiledCfg {
     static constexpr int kInstr = kStageUnits / (64 * kWaves);  // loads per wave per stage
     static constexpr int kLdsBytes = NS * kStageUnits * 16;
     static constexpr int kSteps = BK / 32;
-    static_assert(BK == 32 || BK == 64, "a stage holds one or two MFMA k-steps");
+    static_assert(BK == kSlab, "a stage is one slab of the packed W: two MFMA k-steps");
     static_assert(NS >= 2, "at least double buffering");
     static_assert(kStageUnits % (64 * kWaves) == 0, "a stage must split evenly over the waves");
     static_assert((BN * kCh) % 64 == 0, "one load instruction must not straddle W and x");
@@ -306,7 +324,7 @@ struct TiledCfg {
 
 // One BM x BN output block: rows m0 .. m0+BM-1 of x/y (rows at or past
 // row_hi are clamped on load and never stored), columns n0 .. n0+BN-1 of y
-// (rows of Wb past N are clamped likewise).
+// (rows of Wb past N are clamped likewise).  Wb is the packed W (slab-major).
 // With kIdx, row i of the logical x is row xidx[i] of the stored x (xn rows;
 // an index outside 0..xn-1 is clamped into it): the MoE layer's gather of
 // token rows into expert order, done by the loads themselves.
@@ -327,20 +345,21 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
 
     const int wrows = min(BN, N - n0);
     const int xrows = min(BM, row_hi - m0);
-    const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wb + (size_t)n0 * K, (uint32_t)wrows * rowb);
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wb + (size_t)n0 * kSlab, wpk_bytes(N, K, wrows));
     const __amdgpu_buffer_rsrc_t rX =
         kIdx ? make_rsrc(x, (uint32_t)xn * rowb) : make_rsrc(x + (size_t)m0 * K, (uint32_t)xrows * rowb);
 
     // Byte offset of each of this lane's loads within a stage's rows.  Unit
     // u of the stage (lane-linear in LDS) holds logical chunk swz(r, u % kCh)
-    // of row r; rows past the valid range re-read the last valid row.
+    // of row r; rows past the valid range re-read the last valid row.  W
+    // rows of a stage are 128 bytes apart (one slab), x rows 2K bytes.
     uint32_t voff[C::kInstr];
 #pragma unroll
     for (int j = 0; j < C::kInstr; ++j) {
         const int u = (wave * C::kInstr + j) * 64 + lane;
         if (u < BN * kCh) {
             const int r = u / kCh;
-            voff[j] = (uint32_t)min(r, wrows - 1) * rowb + swz<kCh>(r, u % kCh) * 16;
+            voff[j] = wpk_row(min(r, wrows - 1), swz<kCh>(r, u % kCh));
         } else {
             const int uu = u - BN * kCh;
             const int r = uu / kCh;
@@ -356,7 +375,8 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
 #pragma unroll
         for (int j = 0; j < C::kInstr; ++j) {
             const int u0 = (wave * C::kInstr + j) * 64;
-            dma16(u0 < BN * kCh ? rW : rX, voff[j], (uint32_t)(sp.k0 + s * BK) * 2,
+            const int k = sp.k0 + s * BK;
+            dma16(u0 < BN * kCh ? rW : rX, voff[j], u0 < BN * kCh ? wpk_slab(k, N) : (uint32_t)k * 2,
                   lds + buf * C::kStageUnits + u0);
         }
     };
@@ -592,7 +612,7 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
 
     const int wrows = min(BN, N - n0);
     const int xrows = min(BM, row_hi - m0);
-    const sgpr4 aW = rsrc_words(Wb + (size_t)n0 * K, (uint32_t)wrows * rowb);
+    const sgpr4 aW = rsrc_words(Wb + (size_t)n0 * kSlab, wpk_bytes(N, K, wrows));
     const sgpr4 aX = kIdx ? rsrc_words(x, (uint32_t)xn * rowb) : rsrc_words(x + (size_t)m0 * K, (uint32_t)xrows * rowb);
 
     // load j < 8: W unit (8 wave + j) 64 + lane; j >= 8: the same unit of x
@@ -603,7 +623,7 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
         const int r = u / kCh;
         const int c = swz<kCh>(r, u % kCh);
         if (j < 8) {
-            voff[j] = (uint32_t)min(r, wrows - 1) * rowb + c * 16;
+            voff[j] = wpk_row(min(r, wrows - 1), c);
         } else {
             uint32_t row = (uint32_t)min(r, xrows - 1);
             if constexpr (kIdx) {
@@ -614,7 +634,7 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
         }
     }
     auto issueW = [&](int j, int t, int wbuf) {
-        dma16_asm(aW, voff[j], (uint32_t)(sp.k0 + t * BK) * 2, lds + wbuf * kPart + (wave * 8 + j) * 64);
+        dma16_asm(aW, voff[j], wpk_slab(sp.k0 + t * BK, N), lds + wbuf * kPart + (wave * 8 + j) * 64);
     };
     auto issueX = [&](int j, int t, int xbuf) {
         dma16_asm(aX, voff[8 + j], (uint32_t)(sp.k0 + t * BK) * 2, lds + kXBase + xbuf * kPart + (wave * 8 + j) * 64);
@@ -911,7 +931,7 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
                     k_stage = 0;
                     const StreamItem s = item_at(cur_it);
                     const int xrows = min(XR, s.row_hi - s.m0);
-                    rW = make_rsrc(s.Wb + (size_t)s.n0 * K, 16 * rowb);
+                    rW = make_rsrc(s.Wb + (size_t)s.n0 * kSlab, wpk_bytes(N, K, 16));
                     rX = kIdx ? make_rsrc(x, (uint32_t)xn * rowb)
                               : make_rsrc(x + (size_t)s.m0 * K, (uint32_t)xrows * rowb);
 #pragma unroll
@@ -926,7 +946,8 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
                                 row = (uint32_t)(t < 0 ? 0 : (t >= xn ? xn - 1 : t));
                             }
                         }
-                        voff[j] = row * rowb + c * 16;
+                        // W: chunk c of the stage is chunk c % 8 of its slab c / 8
+                        voff[j] = r < 16 ? wpk_slab(kSlab * (c / 8), N) + wpk_row(r, c % 8) : row * rowb + c * 16;
                     }
                     if constexpr (kIdx)
                         load_idx(cur_it + 1);
@@ -935,7 +956,9 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
 #pragma unroll
                 for (int j = 0; j < kI; ++j) {
                     const int u0 = (first + j) * 64;
-                    dma16(u0 < 16 * kCh ? rW : rX, voff[j], (uint32_t)(sp.k0 + k_stage * BKS) * 2, dst + u0);
+                    const int k = sp.k0 + k_stage * BKS;
+                    dma16(u0 < 16 * kCh ? rW : rX, voff[j], u0 < 16 * kCh ? wpk_slab(k, N) : (uint32_t)k * 2,
+                          dst + u0);
                 }
                 ++k_stage;
             };
@@ -1178,7 +1201,33 @@ constexpr TileShape kTileShapes[] = {
     {DenseKernel::kTiled64x32, DenseKernel::kTiled64x32, 64, 32},
 };
 
+// W [E][N][K] row-major -> the packed slab-major layout, 16 bytes per
+// thread and step; a bitwise copy.  Thread v reads unit v of W (row n, the 8
+// values from k = 8c) and writes it where the packed layout puts (n, 8c).
+__global__ void __launch_bounds__(256)
+    bigemm_pack_w(const uint4* __restrict__ W, uint4* __restrict__ P, int N, int K, long long units)
+{
+    const long long per = (long long)N * K / 8;  // units per expert
+    const int rowu = K / 8;                      // units per W row
+    for (long long v = (long long)blockIdx.x * blockDim.x + threadIdx.x; v < units;
+         v += (long long)gridDim.x * blockDim.x) {
+        const long long e = v / per;
+        const long long w = v - e * per;
+        const int n = (int)(w / rowu), c = (int)(w % rowu);
+        P[e * per + (long long)(c / 8) * N * 8 + n * 8 + c % 8] = W[v];
+    }
+}
+
 }  // namespace
+
+hipError_t pack_weights(const void* W, void* packed, int E, int N, int K, hipStream_t stream)
+{
+    const long long units = (long long)(E > 0 ? E : 1) * N * K / 8;
+    const long long blocks = (units + 255) / 256;
+    hipLaunchKernelGGL(bigemm_pack_w, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, stream,
+                       static_cast<const uint4*>(W), static_cast<uint4*>(packed), N, K, units);
+    return hipGetLastError();
+}
 
 DenseKernel choose_dense(const Plan& p, int M)
 {

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import DEV, assert_parity, to_dev
+from gpu_util import DEV, assert_bits_equal, assert_parity, bits32, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -133,3 +133,31 @@ def test_zero_rows_and_empty(gpu):
     yz = g(z)
     torch.cuda.synchronize()
     assert np.all(yz.cpu().numpy() == 0)
+
+
+def test_weights_copied_at_create(gpu):
+    """A handle packs its own copy of W at create: overwriting the caller's W
+    afterwards, or dropping it, leaves every result bit unchanged (dense at
+    the streaming, tiled and 256x256 sizes; grouped)."""
+    n, k = 2048, 512
+    w = to_dev(synth.normal_bf16(56, (n, k), 0.02))
+    xs = to_dev(synth.normal_bf16(57, (8200, k)))
+    g = gpu.Gemm(w)
+    ms = (1, 40, 300, 8200)
+    before = [bits32(g(xs[:m])) for m in ms]
+    w.fill_(0)
+    del w
+    torch.cuda.synchronize()
+    for m, b in zip(ms, before):
+        assert_bits_equal(bits32(g(xs[:m])), b, "dense M=%d after W was overwritten" % m)
+    assert g.kernel_name(8200) == "bigemm_tiled<256x256>"
+
+    e = 8
+    wg = to_dev(synth.normal_bf16(58, (e, n, k), 0.02))
+    off = torch.as_tensor(np.array([0, 3, 3, 200, 700, 701, 1500, 1516, 2000], np.int32), device=DEV)
+    gg = gpu.GroupedGemm(wg)
+    yb = bits32(gg(xs[:2000], off))
+    wg.fill_(0)
+    del wg
+    torch.cuda.synchronize()
+    assert_bits_equal(bits32(gg(xs[:2000], off)), yb, "grouped after W was overwritten")
