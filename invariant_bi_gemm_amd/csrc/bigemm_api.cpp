@@ -512,8 +512,14 @@ void bi_gemm_destroy(bi_gemm_t hh)
             return;
     }
     hh->magic = 0;
-    // hipFree waits for the device work that may still read the weights
+    // hipFree waits for the device work that may still read the weights; it
+    // runs with the handle's device current
+    int cur = -1;
+    const bool switched = hipGetDevice(&cur) == hipSuccess && cur != hh->device &&
+                          hipSetDevice(hh->device) == hipSuccess;
     (void)hipFree(hh->W);
+    if (switched)
+        (void)hipSetDevice(cur);
     delete hh;
 }
 

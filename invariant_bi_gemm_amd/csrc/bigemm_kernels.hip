@@ -28,7 +28,8 @@
 //                  x) full with direct buffer->LDS loads; consumer waves run
 //                  the MFMA chain of one 16-column tile.  HBM bound.
 // Both have a grouped (MoE) variant whose per-expert row counts stay on the
-// device.
+// device.  Every kernel reads W from the handle's packed copy (slab-major,
+// made at create by bigemm_pack_w); x and y are row-major.
 
 #include <type_traits>
 

@@ -81,6 +81,36 @@ def test_tiles_and_ragged_tails(gpu, m):
     assert_parity(y, yr, a, "N=768 K=1024 M=%d" % m)
 
 
+@pytest.mark.parametrize("n,ms", [(272, (1, 17, 40, 300, 1100)), (2064, (1, 33, 700, 8200))])
+def test_ragged_columns(gpu, n, ms):
+    """N a multiple of 16 but of no block width (the last column block holds
+    16 rows) and K = 576, an odd number of 64-wide k slabs: the streaming,
+    tiled and (N = 2064, M = 8200) 256x256 kernels over a partial column block
+    of the packed weights.  All rows up to M = 1100, sampled rows beyond."""
+    k = 576
+    w = synth.normal_bf16(60 + n, (n, k), 0.02)
+    g = gpu.Gemm(to_dev(w))
+    x = synth.normal_bf16(61 + n, (max(ms), k))
+    xd = to_dev(x)
+    for m in ms:
+        y = g(xd[:m])
+        torch.cuda.synchronize()
+        rows = np.arange(m) if m <= 1100 else synth.probe_rows(62 + m, m, 24)
+        yr, a = oracle.gemm_f64(x[:m], w, rows=rows)
+        assert_parity(y[torch.as_tensor(rows, device=DEV)].cpu().numpy(), yr, a, "N=%d M=%d" % (n, m))
+    if n == 2064:
+        assert g.kernel_name(8200) == "bigemm_tiled<256x256>"
+    # grouped over the same ragged N: three experts with 5, 300 and 295 rows
+    # (streaming, four-wave and tiled kernels), each row equal to its dense row
+    wg = np.stack([w, synth.normal_bf16(63 + n, (n, k), 0.02), synth.normal_bf16(64 + n, (n, k), 0.02)])
+    off = np.array([0, 5, 305, 600], np.int32)
+    gg = gpu.GroupedGemm(to_dev(wg))
+    yg = bits32(gg(xd[:600], torch.as_tensor(off, device=DEV)))
+    for e in range(3):
+        yd = bits32(gpu.Gemm(to_dev(wg[e]))(xd[off[e]:off[e + 1]]))
+        assert_bits_equal(yg[off[e]:off[e + 1]], yd, "grouped N=%d expert %d" % (n, e))
+
+
 @pytest.mark.parametrize("smax", [0, 4096])
 def test_forced_paths_parity(gpu, smax):
     """Both kernel families on their own at awkward sizes."""
