@@ -319,30 +319,39 @@ __global__ void __launch_bounds__(256)
         }
     }
     __syncthreads();
-    for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
-        float4 acc = {0.f, 0.f, 0.f, 0.f};
-        // eight slots' rows are loaded before any of them is added
+    // Each thread owns columns c and c + 1024 of every 2048-column span; the
+    // eight slots' rows of both are loaded before any of them is added.
+    for (int c = threadIdx.x * 4; c < H; c += 2 * 256 * 4) {
+        const bool hi = c + 256 * 4 < H;
+        float4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
         for (int j0 = 0; j0 < k; j0 += 8) {
-            float4 v[8];
+            float4 v0[8], v1[8];
             bool ok[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int r = j0 + u < k ? s_row[j0 + u] : -1;
                 ok[u] = r >= 0 && r < R;
-                v[u] = ok[u] ? *reinterpret_cast<const float4*>(o + (size_t)r * H + c)
-                             : float4{0.f, 0.f, 0.f, 0.f};
+                const float* row = o + (size_t)(ok[u] ? r : 0) * H + c;
+                v0[u] = ok[u] ? *reinterpret_cast<const float4*>(row) : float4{0.f, 0.f, 0.f, 0.f};
+                v1[u] = ok[u] && hi ? *reinterpret_cast<const float4*>(row + 256 * 4) : float4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u)
                 if (ok[u]) {
                     const float ww = s_w[j0 + u];
-                    acc.x = acc.x + ww * v[u].x;
-                    acc.y = acc.y + ww * v[u].y;
-                    acc.z = acc.z + ww * v[u].z;
-                    acc.w = acc.w + ww * v[u].w;
+                    acc0.x = acc0.x + ww * v0[u].x;
+                    acc0.y = acc0.y + ww * v0[u].y;
+                    acc0.z = acc0.z + ww * v0[u].z;
+                    acc0.w = acc0.w + ww * v0[u].w;
+                    acc1.x = acc1.x + ww * v1[u].x;
+                    acc1.y = acc1.y + ww * v1[u].y;
+                    acc1.z = acc1.z + ww * v1[u].z;
+                    acc1.w = acc1.w + ww * v1[u].w;
                 }
         }
-        *reinterpret_cast<float4*>(y + (size_t)t * H + c) = acc;
+        *reinterpret_cast<float4*>(y + (size_t)t * H + c) = acc0;
+        if (hi)
+            *reinterpret_cast<float4*>(y + (size_t)t * H + c + 256 * 4) = acc1;
     }
 }
 
