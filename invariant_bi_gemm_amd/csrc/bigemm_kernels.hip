@@ -18,16 +18,16 @@
 // the batch, only the tiling of the output does.
 //
 // Kernel families:
-//   bigemm_tiled   mid and large M: an NS-stage LDS pipeline fed by direct
+//   bigemm_tiled   mid M: an NS-stage LDS pipeline fed by direct
 //                  buffer->LDS loads, one barrier per stage, output blocks
-//                  from 64x32 to 128x256 (x rows by W rows) chosen by M.
-//   bigemm_tiled4  large M: 256x256 blocks, four waves with their
-//                  accumulators in the accumulation registers.  MFMA bound.
+//                  from 64x32 to 128x128 (x rows by W rows) chosen by M.
+//   bigemm_tiled4  large M: 128x256 and 256x256 blocks, four waves with
+//                  their accumulators in the accumulation registers.
 //   bigemm_stream  small M: a persistent, warp-specialised weight streamer.
 //                  Up to seven producer waves keep a deep LDS ring of W (and
 //                  x) full with direct buffer->LDS loads; consumer waves run
 //                  the MFMA chain of one 16-column tile.  HBM bound.
-// Both have a grouped (MoE) variant whose per-expert row counts stay on the
+// Each has a grouped (MoE) variant whose per-expert row counts stay on the
 // device.  Every kernel reads W from the handle's packed copy (slab-major,
 // made at create by bigemm_pack_w); x and y are row-major.
 
@@ -588,23 +588,41 @@ __device__ __forceinline__ void for_each_t(F&& f, std::integer_sequence<int, T..
     (f(std::integral_constant<int, T>{}), ...);
 }
 
-// LDS: W triple-buffered (3 x 32 KB) and x double-buffered (2 x 32 KB), the
-// whole 160 KB.  A stage is 64 values of k (two MFMA k-steps, full 128-byte
-// row segments).  Stage t's W is loaded during k-step 0 of stage t-2 and its
-// x during k-step 1 of stage t-2, 8 loads per wave spread over each k-step's
-// 64 MFMAs: loads issued in bursts stall the issuing wave (a CU accepts one
+// LDS: W triple-buffered (3 x 32 KB) and x double-buffered (2 x 32 KB at
+// 256 x rows), 160 KB.  A stage is 64 values of k (two MFMA k-steps, full
+// 128-byte row segments).  Stage t's W is loaded during k-step 0 of stage t-2
+// and its x during k-step 1 of stage t-2, the loads spread over each k-step's
+// MFMAs: loads issued in bursts stall the issuing wave (a CU accepts one
 // 1 KB load about every 16 cycles) and, with one wave per SIMD, the MFMA
 // pipe with it.
+//
+// XT: x tiles per wave.  XT = 8 is the 256x256 block; XT = 4 the same block
+// over 128 x rows (each wave 64 x rows by 128 W rows, 128 accumulation
+// registers), for M too small to give every CU a 256-row block.
 
-template <bool kIdx = false>
+// The fragment read q (0 .. 7+XT) of the next k-step issued after MFMA T of
+// a k-step's 8 XT: spread evenly, in the order the MFMAs consume them.
+template <int XT>
+constexpr int tiled4_read_at(int T)
+{
+    for (int q = 0; q < 8 + XT; ++q)
+        if (((q + 1) * 8 * XT) / (8 + XT) - 1 == T)
+            return q;
+    return -1;
+}
+
+template <int XT, bool kIdx = false>
 __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restrict__ x,
                                               const uint16_t* __restrict__ Wb, float* __restrict__ y, int m0,
                                               int row_hi, int n0, int N, int K, Split sp,
                                               const int32_t* __restrict__ xidx = nullptr, int xn = 0)
 {
-    constexpr int BM = 256, BN = 256, BK = 64, kCh = BK / 8;
-    constexpr int kPart = 256 * kCh;      // units (16 B) of one 256-row part of a stage: 32 KB
+    static_assert(XT == 4 || XT == 8, "x tiles per wave");
+    constexpr int BM = 32 * XT, BN = 256, BK = 64, kCh = BK / 8;
+    constexpr int kPart = 256 * kCh;      // units (16 B) of one 256-row W part of a stage: 32 KB
+    constexpr int kXPart = BM * kCh;      // units of one stage's x rows
     constexpr int kXBase = 3 * kPart;     // x buffers follow the three W buffers
+    constexpr int kT = 8 * XT;            // MFMAs per k-step
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave & 1;
@@ -616,11 +634,12 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
     const sgpr4 aW = rsrc_words(Wb + (size_t)n0 * kSlab, wpk_bytes(N, K, wrows));
     const sgpr4 aX = kIdx ? rsrc_words(x, (uint32_t)xn * rowb) : rsrc_words(x + (size_t)m0 * K, (uint32_t)xrows * rowb);
 
-    // load j < 8: W unit (8 wave + j) 64 + lane; j >= 8: the same unit of x
-    uint32_t voff[16];
+    // load j < 8: W unit (8 wave + j) 64 + lane; j >= 8: x unit
+    // (XT wave + j - 8) 64 + lane
+    uint32_t voff[8 + XT];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int u = (wave * 8 + (j & 7)) * 64 + lane;
+    for (int j = 0; j < 8 + XT; ++j) {
+        const int u = (j < 8 ? wave * 8 + j : wave * XT + j - 8) * 64 + lane;
         const int r = u / kCh;
         const int c = swz<kCh>(r, u % kCh);
         if (j < 8) {
@@ -638,23 +657,23 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
         dma16_asm(aW, voff[j], wpk_slab(sp.k0 + t * BK, N), lds + wbuf * kPart + (wave * 8 + j) * 64);
     };
     auto issueX = [&](int j, int t, int xbuf) {
-        dma16_asm(aX, voff[8 + j], (uint32_t)(sp.k0 + t * BK) * 2, lds + kXBase + xbuf * kPart + (wave * 8 + j) * 64);
+        dma16_asm(aX, voff[8 + j], (uint32_t)(sp.k0 + t * BK) * 2, lds + kXBase + xbuf * kXPart + (wave * XT + j) * 64);
     };
     // fragment q of k-step ks of the stage in W buffer wbuf and x buffer
-    // xbuf: q = 0 is W tile 0, 1..8 are x tiles 0..7, 9..15 are W tiles 1..7
+    // xbuf: q = 0 is W tile 0, 1..XT are x tiles 0..XT-1, the rest W tiles 1..7
     auto read1 = [&](int q, int wbuf, int xbuf, int ks, uint4* fa, uint4* fb) {
         const int cl = ks * 4 + (lane >> 4);
-        if (q >= 1 && q <= 8) {
-            const int r = wm * 128 + (q - 1) * 16 + (lane & 15);
-            fb[q - 1] = lds[kXBase + xbuf * kPart + r * kCh + swz<kCh>(r, cl)];
+        if (q >= 1 && q <= XT) {
+            const int r = wm * 16 * XT + (q - 1) * 16 + (lane & 15);
+            fb[q - 1] = lds[kXBase + xbuf * kXPart + r * kCh + swz<kCh>(r, cl)];
         } else {
-            const int tt = q == 0 ? 0 : q - 8;
+            const int tt = q == 0 ? 0 : q - XT;
             const int r = wn * 128 + tt * 16 + (lane & 15);
             fa[tt] = lds[wbuf * kPart + r * kCh + swz<kCh>(r, cl)];
         }
     };
 
-    uint4 fa0[8], fb0[8], fa1[8], fb1[8];
+    uint4 fa0[8], fb0[XT], fa1[8], fb1[XT];
     const int nk = sp.klen / BK;
 
     // Step 0 of stage t: MFMAs of k-step 0, the fragments of k-step 1, and
@@ -670,28 +689,28 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
         const int wl = wb == 0 ? 2 : wb - 1;  // (t + 2) % 3
         for_each_t([&](auto tc) {
             constexpr int T = decltype(tc)::value;
-            mfma_agpr<T, kZ>(fa0[T / 8], fb0[T % 8]);
-            if constexpr (T % 4 == 3)
-                read1(T / 4, wb, xb, 1, fa1, fb1);
-            if constexpr (T % 8 == 5)  // after MFMAs 5, 13, ..., 61
-                issueW(T / 8, tl, wl);
-        }, std::make_integer_sequence<int, 64>{});
+            mfma_agpr<T, kZ>(fa0[T / XT], fb0[T % XT]);
+            if constexpr (tiled4_read_at<XT>(T) >= 0)
+                read1(tiled4_read_at<XT>(T), wb, xb, 1, fa1, fb1);
+            if constexpr (T % XT == (5 * XT) / 8)  // one W load per XT MFMAs
+                issueW(T / XT, tl, wl);
+        }, std::make_integer_sequence<int, kT>{});
     };
     auto step1 = [&](int t, int wb, int xb) {
         const int tl = min(t + 2, nk - 1);
         const int wn1 = wb == 2 ? 0 : wb + 1;  // (t + 1) % 3
         for_each_t([&](auto tc) {
             constexpr int T = decltype(tc)::value;
-            mfma_agpr<T, false>(fa1[T / 8], fb1[T % 8]);
+            mfma_agpr<T, false>(fa1[T / XT], fb1[T % XT]);
             if constexpr (T == 1) {
                 wait_vmcnt<8>();
                 barrier_after_lds_reads();
             }
-            if constexpr (T >= 2 && T < 34 && T % 2 == 0)
+            if constexpr (T >= 2 && T < 2 + 2 * (8 + XT) && T % 2 == 0)
                 read1((T - 2) / 2, wn1, xb ^ 1, 0, fa0, fb0);
-            if constexpr (T % 8 == 3)  // after MFMAs 3, 11, ..., 59
+            if constexpr (T % 8 == 3 && T / 8 < XT)  // after MFMAs 3, 11, ...
                 issueX(T / 8, tl, xb);
-        }, std::make_integer_sequence<int, 64>{});
+        }, std::make_integer_sequence<int, kT>{});
     };
 
     claim_agprs();
@@ -700,18 +719,18 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
     for (int j = 0; j < 8; ++j)
         issueW(j, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < XT; ++j)
         issueX(j, 0, 0);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         issueW(j, t1, 1);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < XT; ++j)
         issueX(j, t1, 1);
-    wait_vmcnt<16>();  // stage 0 has landed
+    wait_vmcnt<8 + XT>();  // stage 0 has landed
     barrier_after_lds_reads();
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
+    for (int q = 0; q < 8 + XT; ++q)
         read1(q, 0, 0, 0, fa0, fb0);
     step0(std::true_type{}, 0, 0, 0);
     step1(0, 0, 0);
@@ -728,23 +747,25 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
     // line of y (tiles i and i+1 of one row) are stored back to back
     for_each_t([&](auto uc) {
         constexpr int U = decltype(uc)::value;
-        constexpr int j = U / 8, i = U % 8, T = 8 * i + j;
-        const int m = m0 + wm * 128 + j * 16 + (lane & 15);
+        constexpr int j = U / 8, i = U % 8, T = XT * i + j;
+        const int m = m0 + wm * 16 * XT + j * 16 + (lane & 15);
         const int n = n0 + wn * 128 + i * 16 + 4 * (lane >> 4);
         const f32x4 v = read_agpr_tile<T>();
         if (m < row_hi && n < N)
             emit4(y + (size_t)m * N + n, v, sp.fold);
-    }, std::make_integer_sequence<int, 64>{});
+    }, std::make_integer_sequence<int, kT>{});
 }
 
+// (32 XT) x 256 output blocks, one per workgroup.
+template <int XT>
 __global__ void __launch_bounds__(256)
     bigemm_tiled4(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ y, int M,
                    int N, int K, Split sp, int tiles_m, int tiles_n, int group_m)
 {
-    __shared__ uint4 lds[5 * 256 * 8];
+    __shared__ uint4 lds[3 * 256 * 8 + 2 * 32 * XT * 8];
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
-    tiled4_block(lds, x, W, y, tm * 256, M, tn * 256, N, K, sp);
+    tiled4_block<XT>(lds, x, W, y, tm * 32 * XT, M, tn * 256, N, K, sp);
 }
 
 // Grouped, persistent: the 256-row blocks (big_count) of the experts with
@@ -766,7 +787,7 @@ __global__ void __launch_bounds__(256)
         int m0, hi;
         const int e = big_slot(off, E, R, cmin, t / tiles_n, &m0, &hi);
         barrier_after_lds_reads();  // every wave is done with the previous tile's stages
-        tiled4_block<kIdx>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K, sp, xidx, xn);
+        tiled4_block<8, kIdx>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K, sp, xidx, xn);
     }
 }
 
@@ -1085,11 +1106,12 @@ hipError_t run_tiled(const void* W, const void* x, int M, float* y, int N, int K
     return hipGetLastError();
 }
 
+template <int XT>
 hipError_t run_tiled4(const void* W, const void* x, int M, float* y, int N, int K, Split sp, hipStream_t stream)
 {
-    const int tiles_m = (M + 255) / 256;
+    const int tiles_m = (M + 32 * XT - 1) / (32 * XT);
     const int tiles_n = (N + 255) / 256;
-    hipLaunchKernelGGL(bigemm_tiled4, dim3(tiles_m * tiles_n), dim3(256), 0, stream,
+    hipLaunchKernelGGL(bigemm_tiled4<XT>, dim3(tiles_m * tiles_n), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K, sp, tiles_m,
                        tiles_n, 4);
     return hipGetLastError();
@@ -1286,9 +1308,9 @@ hipError_t launch_dense_split(const Plan& p, DenseKernel kind, const void* W, co
     case DenseKernel::kStream64:
         return run_stream_k<4, 64>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
     case DenseKernel::kTiled256:
-        return run_tiled4(W, x, M, y, p.n, p.k, sp, stream);
+        return run_tiled4<8>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled128x256:
-        return run_tiled<128, 256, 2, 4, 64, 3>(W, x, M, y, p.n, p.k, sp, stream);
+        return run_tiled4<4>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled128:
         return run_tiled<128, 128, 2, 2, 64, 2>(W, x, M, y, p.n, p.k, sp, stream);
     case DenseKernel::kTiled128x64:

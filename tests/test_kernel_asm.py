@@ -1,5 +1,5 @@
-"""The built code of the four-wave 256x256 kernels (dense and grouped),
-checked on the CPU.
+"""The built code of the four-wave kernels (dense 256x256 and 128x256
+blocks, grouped), checked on the CPU.
 
 Its accumulators live in a0..a255, written only by inline-asm MFMAs and read
 only by the epilogue; the compiler does not know they are live.  So the
@@ -20,10 +20,12 @@ import pytest
 from invariant_bi_gemm_amd import build
 
 SRC = os.path.join(build.CSRC, "bigemm_kernels.hip")
-# the dense kernel and the grouped one (plain and indexed rows)
-KERNELS = ["_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4E",
-           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb0E",
-           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1E"]
+# the dense kernels (8 and 4 x tiles per wave) and the grouped one (plain and
+# indexed rows), with the accumulator tiles each wave holds
+KERNELS = {"_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi8E": 64,
+           "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi4E": 32,
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb0E": 64,
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1E": 64}
 MFMA_AGPR = re.compile(r"v_mfma_f32_16x16x32_bf16 a\[\d+:\d+\], v\[\d+:\d+\], v\[\d+:\d+\], (a\[\d+:\d+\]|0)$")
 AGPR = re.compile(r"\ba\d+\b|\ba\[\d+:\d+\]")
 
@@ -67,8 +69,8 @@ def test_accumulation_registers_only_in_the_chains(asm, kernel):
     bad = [t for t in ins if AGPR.search(t) and not MFMA_AGPR.match(t)
            and not re.match(r"v_accvgpr_read_b32 v\d+, a\d+$", t)]
     assert not bad, "compiler-placed accumulation-register use: %s" % bad[:5]
-    assert sum(1 for t in ins if t.startswith("v_mfma")) >= 128
-    assert sum(1 for t in ins if t.startswith("v_accvgpr_read_b32")) == 256
+    assert sum(1 for t in ins if t.startswith("v_mfma")) >= 2 * KERNELS[kernel]
+    assert sum(1 for t in ins if t.startswith("v_accvgpr_read_b32")) == 4 * KERNELS[kernel]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)

@@ -52,16 +52,18 @@ def test_integer_exact(gpu, n, k):
         assert np.all(np.abs(got) <= 9 * k)
 
 
-@pytest.mark.parametrize("m", [4100, 8195])
-def test_integer_exact_large_m(gpu, m):
-    """x, W in {-3..3} through the 256x256 four-wave kernel (one round of
-    blocks plus a ragged 4-row tail; two rounds plus a 3-row tail): exact
-    integers on sampled rows, the tail rows included."""
+@pytest.mark.parametrize("m,kernel", [(2050, "bigemm_tiled<128x256>"), (4100, "bigemm_tiled<256x256>"),
+                                      (8195, "bigemm_tiled<256x256>")])
+def test_integer_exact_large_m(gpu, m, kernel):
+    """x, W in {-3..3} through the four-wave kernels: 128x256 blocks (one
+    round plus a 2-row tail), 256x256 blocks (one round plus a ragged 4-row
+    tail; two rounds plus a 3-row tail).  Exact integers on sampled rows, the
+    tail rows included."""
     n, k = 4096, 1024
     w = synth.int_bf16(51, (n, k))
     xs = synth.int_bf16(52, (m, k))
     g = gpu.Gemm(to_dev(w))
-    assert g.kernel_name(m) == "bigemm_tiled<256x256>"
+    assert g.kernel_name(m) == kernel
     y = g(to_dev(xs))
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([synth.probe_rows(53 + m, m, 24), np.arange(m - 4, m)]))
