@@ -170,13 +170,14 @@ __device__ __forceinline__ int swz(int r, int c)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int clamp_off(int v, int R) { return v < 0 ? 0 : (v > R ? R : v); }
 
-// The four-wave kernel takes an expert's rows in blocks of 256: every whole
-// block, and a last partial block of at least 128 rows (a 256-row block at
-// half occupancy still outruns the 128-row tiles).  big_count: its blocks
-// for an expert with c rows; big_rows: the rows they cover (big = 0: the
-// kernel is not launched).  The other kernels serve the rest.
-__device__ __forceinline__ int big_count(int c) { return c / 256 + (c % 256 >= 128 ? 1 : 0); }
-__device__ __forceinline__ int big_rows(int c, int big) { return big > 0 ? min(c, big_count(c) * 256) : 0; }
+// When it is launched, the four-wave kernel takes all the rows of every
+// expert above the streaming threshold, in blocks of 256 rows; the last block
+// holds the rest, as a 128x256 block when at most 128 rows are left.
+// big_count: the blocks of an expert with c rows; big_rows: the rows they
+// cover (big = 0: the kernel is not launched and the tiled kernel serves
+// them).
+__device__ __forceinline__ int big_count(int c) { return (c + 255) / 256; }
+__device__ __forceinline__ int big_rows(int c, int big) { return big > 0 ? c : 0; }
 
 // Plan of a grouped call, built by every block in its own LDS: s_off[e] =
 // offsets[e] clamped to 0..R, and s_first[e] = the m-blocks of the experts
@@ -768,10 +769,10 @@ __global__ void __launch_bounds__(256)
     tiled4_block<XT>(lds, x, W, y, tm * 32 * XT, M, tn * 256, N, K, sp);
 }
 
-// Grouped, persistent: the 256-row blocks (big_count) of the experts with
-// more than cmin rows, by 256 W rows; the tiles are cut into 8 contiguous ranges,
-// one per XCD, as in bigemm_tiled_grouped.  kIdx: x rows are read through
-// xidx.
+// Grouped, persistent: the row blocks (big_count) of the experts with more
+// than cmin rows, by 256 W rows; a block of at most 128 rows runs as a
+// 128x256 block.  The tiles are cut into 8 contiguous ranges, one per XCD,
+// as in bigemm_tiled_grouped.  kIdx: x rows are read through xidx.
 template <bool kIdx>
 __global__ void __launch_bounds__(256)
     bigemm_tiled4_grouped(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ y,
@@ -787,7 +788,10 @@ __global__ void __launch_bounds__(256)
         int m0, hi;
         const int e = big_slot(off, E, R, cmin, t / tiles_n, &m0, &hi);
         barrier_after_lds_reads();  // every wave is done with the previous tile's stages
-        tiled4_block<8, kIdx>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K, sp, xidx, xn);
+        if (hi - m0 <= 128)
+            tiled4_block<4, kIdx>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K, sp, xidx, xn);
+        else
+            tiled4_block<8, kIdx>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K, sp, xidx, xn);
     }
 }
 
@@ -1345,10 +1349,10 @@ hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, floa
 hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int32_t* offsets,
                           int R, float* y, const int32_t* xidx, int xn, hipStream_t stream)
 {
-    // Experts with 1..smax rows go to the streaming kernel; of the others,
-    // 256-row blocks (whole, or at least half full) go to the four-wave
-    // kernel and the remaining rows to the tiled kernel.  All realise the same tree, so the split points
-    // only move work, never bits.
+    // Experts with 1..smax rows go to the streaming kernel; the others to
+    // the four-wave kernel when the experts average 64 rows or more, else to
+    // the tiled kernel.  All realise the same tree, so the split points only
+    // move work, never bits.
     const int smax = p.stream_max_m < 16 ? p.stream_max_m : 16;
     const int klen = p.k / p.splits;
     for (int s = 0; s < p.splits; ++s) {
@@ -1366,17 +1370,15 @@ hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int
             if (err != hipSuccess)
                 return err;
         }
-        // 256-row blocks of the experts with at least 128 rows, launched when
-        // the experts average 64 rows or more (below that, few experts reach
-        // 128 rows and an empty launch costs more than it saves)
+        // the four-wave kernel (256- and 128-row blocks) when the experts
+        // average 64 rows or more; below that, most experts fill a 128-row
+        // block poorly and the tiled kernel's 128x128 tiles serve them
         const int big = (R >= 128 && R >= 64 * p.experts) ? 256 : 0;
-        if (big) {
+        if (big)  // every expert above the streaming threshold, whole
             err = run_tiled4_grouped(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, xidx, xn, stream);
-            if (err != hipSuccess)
-                return err;
-        }
-        err = run_tiled_grouped<128, 128, 2, 4, 64, 2>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, big,
-                                                       p.num_cus, xidx, xn, stream);
+        else
+            err = run_tiled_grouped<128, 128, 2, 4, 64, 2>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, big,
+                                                           p.num_cus, xidx, xn, stream);
         if (err != hipSuccess)
             return err;
     }

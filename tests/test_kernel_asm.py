@@ -21,11 +21,12 @@ from invariant_bi_gemm_amd import build
 
 SRC = os.path.join(build.CSRC, "bigemm_kernels.hip")
 # the dense kernels (8 and 4 x tiles per wave) and the grouped one (plain and
-# indexed rows), with the accumulator tiles each wave holds
-KERNELS = {"_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi8E": 64,
-           "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi4E": 32,
-           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb0E": 64,
-           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1E": 64}
+# indexed rows; both block heights in one kernel), with the accumulator tiles
+# each of their epilogues reads
+KERNELS = {"_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi8E": [64],
+           "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi4E": [32],
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb0E": [64, 32],
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1E": [64, 32]}
 MFMA_AGPR = re.compile(r"v_mfma_f32_16x16x32_bf16 a\[\d+:\d+\], v\[\d+:\d+\], v\[\d+:\d+\], (a\[\d+:\d+\]|0)$")
 AGPR = re.compile(r"\ba\d+\b|\ba\[\d+:\d+\]")
 
@@ -69,8 +70,8 @@ def test_accumulation_registers_only_in_the_chains(asm, kernel):
     bad = [t for t in ins if AGPR.search(t) and not MFMA_AGPR.match(t)
            and not re.match(r"v_accvgpr_read_b32 v\d+, a\d+$", t)]
     assert not bad, "compiler-placed accumulation-register use: %s" % bad[:5]
-    assert sum(1 for t in ins if t.startswith("v_mfma")) >= 2 * KERNELS[kernel]
-    assert sum(1 for t in ins if t.startswith("v_accvgpr_read_b32")) == 4 * KERNELS[kernel]
+    assert sum(1 for t in ins if t.startswith("v_mfma")) >= 2 * sum(KERNELS[kernel])
+    assert sum(1 for t in ins if t.startswith("v_accvgpr_read_b32")) == 4 * sum(KERNELS[kernel])
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -106,12 +107,18 @@ def test_mfma_inputs_not_written_just_before(asm, kernel):
 
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_results_read_after_the_wait_states(asm, kernel):
+    """Each epilogue (a run of result reads with no MFMA inside it) starts at
+    least 18 wait states after the MFMA before it, and reads every tile."""
     _, ins = body(asm, kernel)
-    reads = [i for i, t in enumerate(ins) if t.startswith("v_accvgpr_read_b32")]
-    first = reads[0]
-    last_mfma = max(i for i, t in enumerate(ins[:first]) if t.startswith("v_mfma"))
-    nops = sum(int(t.split()[1]) + 1 for t in ins[last_mfma + 1:first] if t.startswith("s_nop"))
-    assert nops >= 18, "only %d wait states between the last MFMA and the first result read" % nops
-    # and no MFMA among the result reads (a grouped kernel loops over tiles:
-    # the next tile's MFMAs come after all 256 reads)
-    assert not any(t.startswith("v_mfma") for t in ins[first:reads[-1]])
+    runs, last_mfma = [], None
+    for i, t in enumerate(ins):
+        if t.startswith("v_mfma"):
+            last_mfma = i
+        elif t.startswith("v_accvgpr_read_b32"):
+            if not runs or runs[-1]["mfma"] != last_mfma:
+                assert last_mfma is not None, "a result read before any MFMA"
+                nops = sum(int(x.split()[1]) + 1 for x in ins[last_mfma + 1:i] if x.startswith("s_nop"))
+                assert nops >= 18, "only %d wait states between the last MFMA and a first result read" % nops
+                runs.append({"mfma": last_mfma, "reads": 0})
+            runs[-1]["reads"] += 1
+    assert sorted(r["reads"] for r in runs) == sorted(4 * n for n in KERNELS[kernel])
