@@ -1350,7 +1350,7 @@ hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int
                           int R, float* y, const int32_t* xidx, int xn, hipStream_t stream)
 {
     // Experts with 1..smax rows go to the streaming kernel; the others to
-    // the four-wave kernel when the experts average 64 rows or more, else to
+    // the four-wave kernel when the experts average 16 rows or more, else to
     // the tiled kernel.  All realise the same tree, so the split points only
     // move work, never bits.
     const int smax = p.stream_max_m < 16 ? p.stream_max_m : 16;
@@ -1371,9 +1371,10 @@ hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int
                 return err;
         }
         // the four-wave kernel (256- and 128-row blocks) when the experts
-        // average 64 rows or more; below that, most experts fill a 128-row
-        // block poorly and the tiled kernel's 128x128 tiles serve them
-        const int big = (R >= 128 && R >= 64 * p.experts) ? 256 : 0;
+        // average 16 rows or more; below that, most experts stream and the
+        // few others fill a 128-row block poorly, so the tiled kernel's
+        // 128x128 tiles serve them
+        const int big = (R >= 128 && R >= 16 * p.experts) ? 256 : 0;
         if (big)  // every expert above the streaming threshold, whole
             err = run_tiled4_grouped(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, xidx, xn, stream);
         else
