@@ -168,13 +168,23 @@ __global__ void __launch_bounds__(kPermThreads)
     // pass 1: counts (every pair for "below e" and "equal to e", the pairs
     // before lo for "equal to e before the chunk")
     int below = 0, equal = 0, before = 0;
-#pragma unroll 8
-    for (int i = tid; i < n; i += kPermThreads) {
-        const int x = ids[i];
+    auto count = [&](int x, int i) {
         below += (x >= 0 && x < e);
         equal += (x == e);
         before += (x == e && i < lo);
+    };
+    // four ids per load when ids is 16-byte aligned, then the tail
+    const int n4 = (reinterpret_cast<uintptr_t>(ids) & 15u) == 0 ? n / 4 : 0;
+#pragma unroll 4
+    for (int i4 = tid; i4 < n4; i4 += kPermThreads) {
+        const int4 x = reinterpret_cast<const int4*>(ids)[i4];
+        count(x.x, 4 * i4);
+        count(x.y, 4 * i4 + 1);
+        count(x.z, 4 * i4 + 2);
+        count(x.w, 4 * i4 + 3);
     }
+    for (int i = 4 * n4 + tid; i < n; i += kPermThreads)
+        count(ids[i], i);
     below = wave_sum(below);
     equal = wave_sum(equal);
     before = wave_sum(before);
@@ -289,7 +299,8 @@ __global__ void __launch_bounds__(256)
 // breaks a tie), one fp32 multiply and one fp32 add per slot, in that order.
 // Lanes j < k of the first wave load slot j together and rank it by (id,
 // slot) against the others; the sorted slots go to LDS.  A row outside
-// 0..R-1 contributes nothing.  Four columns per thread.
+// 0..R-1 contributes nothing.  Each thread owns four columns in each half of
+// every 2048-column span.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
     moe_combine(const float* __restrict__ o, int R, const int32_t* __restrict__ ids,
