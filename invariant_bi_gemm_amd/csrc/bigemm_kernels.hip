@@ -1353,7 +1353,10 @@ hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int
     // the four-wave kernel when the experts average 16 rows or more, else to
     // the tiled kernel.  All realise the same tree, so the split points only
     // move work, never bits.
-    const int smax = p.stream_max_m < 16 ? p.stream_max_m : 16;
+    // When the experts average 64 rows or more, few have 16 or fewer: the
+    // four-wave kernel takes those too (as 128-row blocks), which saves the
+    // streaming launch (about 4 us when it finds no work).
+    const int smax = R >= 64 * p.experts ? 0 : (p.stream_max_m < 16 ? p.stream_max_m : 16);
     const int klen = p.k / p.splits;
     for (int s = 0; s < p.splits; ++s) {
         const Split sp{s * klen, klen, s > 0};
