@@ -58,6 +58,29 @@ typedef enum {
 
 typedef struct bi_gemm *bi_gemm_t;
 
+/*
+ * Dense kernels a tiling entry may name.  All of them realise the same tree;
+ * the entry only moves work between them (Detent, §3: a knob of the
+ * selection is fixed per deployment, never read from the batch).
+ */
+typedef enum {
+    BI_KERNEL_STREAM_MB1 = 0,     /* weight streamer, 16 x rows per m-block      */
+    BI_KERNEL_STREAM_MB2 = 1,     /* weight streamer, 32 x rows per m-block      */
+    BI_KERNEL_STREAM_MB4 = 2,     /* weight streamer, 64 x rows per m-block      */
+    BI_KERNEL_TILED_64X32 = 3,    /* LDS-pipelined tiles: x rows x W rows        */
+    BI_KERNEL_TILED_64X64 = 4,
+    BI_KERNEL_TILED_128X64 = 5,
+    BI_KERNEL_TILED_128X64_DEEP = 6,
+    BI_KERNEL_TILED_128X128 = 7,
+    BI_KERNEL_TILED_128X128_DEEP = 8,
+    BI_KERNEL_TILED4_128X256 = 9, /* four waves, accumulators in AGPRs           */
+    BI_KERNEL_TILED4_256X256 = 10,
+    BI_KERNEL_COUNT = 11
+} bi_kernel_kind_t;
+
+/* Most entries of a pin's tiling list. */
+#define BI_MAX_TILINGS 12
+
 /* Tree and tiling a handle runs with (introspection for tests and benches). */
 typedef struct bi_pin_info {
     int32_t n, k;                 /* layer shape                                 */
@@ -71,13 +94,43 @@ typedef struct bi_pin_info {
                                      weight-streaming kernel runs                */
     int32_t from_table;           /* 1: pin read from the pin table; 0: default  */
     int32_t table_version;        /* version line of the pin table (0: none)     */
+    int32_t tilings;              /* entries used below; 0: the built-in rule
+                                     (streaming up to stream_max_m rows, then
+                                     the largest tile that gives every CU one) */
+    int32_t tile_m_max[BI_MAX_TILINGS];  /* ascending row bounds: entry i serves
+                                     tile_m_max[i-1] < M <= tile_m_max[i]; the
+                                     last entry is INT32_MAX (every larger M)   */
+    int32_t tile_kernel[BI_MAX_TILINGS]; /* bi_kernel_kind_t of each entry      */
 } bi_pin_info;
+
+/*
+ * Identifier of the tree this library realises (a static string without
+ * spaces): the MFMA instruction, the k-to-slot map, the split structure and
+ * the fold order.  A pin table names the tree it was tuned for on its `tree`
+ * line, and a table naming another tree is rejected: the pins are a cached
+ * solve that is only valid for the inputs it was computed from (Detent,
+ * §4.1: the solve is keyed by a hash of everything that can change it).
+ */
+const char *bi_gemm_tree_id(void);
+
+/* Table name of a dense kernel kind ("stream_mb1", "tiled4_256x256", ...;
+ * "" for an unknown kind). */
+const char *bi_gemm_kernel_kind_name(int kind);
 
 /*
  * Load the pin table (text file; see the package's pins/ directory) used by
  * later create calls.  Passing NULL clears the table.  The environment
  * variable BI_GEMM_PINS names a table that is loaded on first use when this
- * is never called.  Not thread-safe with concurrent create calls.
+ * is never called; if that table cannot be read or parsed, every later
+ * create fails with the table's status (BI_ERR_INVALID_ARGUMENT or
+ * BI_ERR_BAD_PIN_TABLE) and the parse error, until a table is loaded here:
+ * a named table is never silently replaced by the default tree.  Not
+ * thread-safe with concurrent create calls.
+ * Format: a `version V` line (V > 0), a `tree ID` line equal to
+ * bi_gemm_tree_id(), then one line per layer shape,
+ *   arch N K splits stream_max_m [M:kind,M:kind,...,*:kind]
+ * where the optional last field is the tiling list (kinds by their
+ * bi_gemm_kernel_kind_name, bounds ascending, the last `*`).
  * Returns BI_OK, BI_ERR_INVALID_ARGUMENT (unreadable file) or
  * BI_ERR_BAD_PIN_TABLE (with the offending line in bi_last_error()).
  */
@@ -112,10 +165,13 @@ bi_status_t bi_gemm_create(int N, int K, const void *W, bi_gemm_t *out);
  * Create a dense handle with an explicit pin instead of the table's.  For the
  * offline tuner, which measures each legal candidate by swapping the pin's
  * constants (Detent, §6 "Search": a repin regenerates the selector without
- * solving again), and for tests that force a kernel path.  Only pin->splits
- * and pin->stream_max_m are read; the pin must be legal for (N, K)
- * (1 <= splits <= 16, K % (64 * splits) == 0, 0 <= stream_max_m <= 4096),
- * else BI_ERR_INVALID_ARGUMENT.  Otherwise as bi_gemm_create.
+ * solving again), and for tests that force a kernel path.  Only
+ * pin->splits, pin->stream_max_m and the tiling list (pin->tilings,
+ * tile_m_max, tile_kernel) are read; the pin must be legal for (N, K)
+ * (1 <= splits <= 16, K % (64 * splits) == 0, 0 <= stream_max_m <= 4096;
+ * 0 <= tilings <= BI_MAX_TILINGS, bounds ascending and positive, the last
+ * INT32_MAX, every kernel a bi_kernel_kind_t), else
+ * BI_ERR_INVALID_ARGUMENT.  Otherwise as bi_gemm_create.
  */
 bi_status_t bi_gemm_create_pinned(int N, int K, const void *W, const bi_pin_info *pin,
                                   bi_gemm_t *out);
@@ -184,8 +240,11 @@ bi_status_t bi_gemm_get_pin(bi_gemm_t h, bi_pin_info *out);
 /*
  * Name of the kernel a run with M rows launches on this handle, e.g.
  * "bigemm_tiled<256x256>" (a static string; "" for an invalid handle or
- * M <= 0).  For benches and tests: it launches nothing.  Every name realises
- * the same tree; the choice only moves work.
+ * M <= 0).  For a grouped handle M is the total row count R, and the name
+ * lists the launches a run with R rows makes, e.g.
+ * "bigemm_stream_grouped+bigemm_tiled4_grouped".  For benches and tests: it
+ * launches nothing.  Every name realises the same tree; the choice only
+ * moves work.
  */
 const char *bi_gemm_kernel_name(bi_gemm_t h, int M);
 

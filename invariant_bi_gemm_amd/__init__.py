@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     STATUS,
     STATUS_CODE,
     BiGemmError,
+    KERNEL_KINDS,
     BiPinInfo,
     DecodeAttention,
     Gemm,

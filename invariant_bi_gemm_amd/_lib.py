@@ -30,13 +30,34 @@ STATUS = {
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 
+MAX_TILINGS = 12  # BI_MAX_TILINGS
+INT32_MAX = 2 ** 31 - 1
+
+# bi_kernel_kind_t, by index; the names are the pin table's
+KERNEL_KINDS = ("stream_mb1", "stream_mb2", "stream_mb4", "tiled_64x32", "tiled_64x64", "tiled_128x64",
+                "tiled_128x64_deep", "tiled_128x128", "tiled_128x128_deep", "tiled4_128x256", "tiled4_256x256")
+
+
 class BiPinInfo(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "n", "k", "experts", "mfma_m", "mfma_n", "mfma_k", "k_map", "splits", "split_len",
-        "fold", "stream_max_m", "from_table", "table_version")]
+        "fold", "stream_max_m", "from_table", "table_version", "tilings")] + [
+        ("tile_m_max", ctypes.c_int32 * MAX_TILINGS), ("tile_kernel", ctypes.c_int32 * MAX_TILINGS)]
 
     def as_dict(self):
-        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+        d = {name: int(getattr(self, name)) for name, _ in self._fields_[:-2]}
+        d["tiling"] = [(int(self.tile_m_max[i]), KERNEL_KINDS[self.tile_kernel[i]]) for i in range(self.tilings)]
+        return d
+
+    def set_tiling(self, tiling):
+        """tiling: [(m_max, kind name or index), ...], the last m_max None or
+        INT32_MAX (every larger M)."""
+        if len(tiling) > MAX_TILINGS:
+            raise ValueError("at most %d tiling entries" % MAX_TILINGS)
+        self.tilings = len(tiling)
+        for i, (m, kind) in enumerate(tiling):
+            self.tile_m_max[i] = INT32_MAX if m is None else int(m)
+            self.tile_kernel[i] = KERNEL_KINDS.index(kind) if isinstance(kind, str) else int(kind)
 
 
 class BiGemmError(RuntimeError):
@@ -56,6 +77,8 @@ def _declare(lib):
     S = ctypes.c_int  # bi_status_t
     sig = {
         "bi_gemm_load_pins": ([ctypes.c_char_p], S),
+        "bi_gemm_tree_id": ([], ctypes.c_char_p),
+        "bi_gemm_kernel_kind_name": ([I], ctypes.c_char_p),
         "bi_gemm_set_strict": ([I], None),
         "bi_gemm_create": ([I, I, P, ctypes.POINTER(P)], S),
         "bi_gemm_create_pinned": ([I, I, P, ctypes.POINTER(BiPinInfo), ctypes.POINTER(P)], S),
@@ -143,8 +166,8 @@ class Gemm:
 
     ``W`` is a contiguous bf16 [N, K] CUDA tensor.  The C library packs its
     own copy at create, so W may be freed or changed afterwards.  ``pin``
-    (optional) is a dict
-    with ``splits`` and ``stream_max_m`` to override the pin table.
+    (optional) is a dict with ``splits``, ``stream_max_m`` and ``tiling``
+    ([(m_max, kind), ...], the last m_max None) to override the pin table.
     """
 
     def __init__(self, W, pin: dict | None = None):
@@ -162,6 +185,7 @@ class Gemm:
                 p = BiPinInfo()
                 p.splits = int(pin.get("splits", 1))
                 p.stream_max_m = int(pin.get("stream_max_m", 16))
+                p.set_tiling(pin.get("tiling", []))
                 st = lib.bi_gemm_create_pinned(self.n, self.k, ctypes.c_void_p(W.data_ptr()),
                                                ctypes.byref(p), ctypes.byref(h))
         check(st)

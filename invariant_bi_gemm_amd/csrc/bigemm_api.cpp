@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cerrno>
+#include <climits>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -38,9 +39,22 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // ---- pin table -------------------------------------------------------------
 
+// The tree this library realises, as a pin table names it.  Change the
+// last component whenever a kernel change could change any output bit
+// (instruction, k-to-slot map, split structure, fold order): tables tuned
+// for the old tree are then rejected instead of read.
+constexpr const char* kTreeId = "mfma_f32_16x16x32_bf16.kmap_g8.contiguous_splits.left_fold.t1";
+
+struct Tiling {
+    int count = 0;
+    int m_max[BI_MAX_TILINGS];
+    int kernel[BI_MAX_TILINGS];
+};
+
 struct PinRow {
     std::string arch;
     int n, k, splits, stream_max_m;
+    Tiling tiling;
 };
 
 struct PinTable {
@@ -51,6 +65,10 @@ struct PinTable {
 std::mutex g_pin_mu;
 PinTable g_pins;
 bool g_pins_env_checked = false;
+// a BI_GEMM_PINS table that failed to load: its status and message, returned
+// by every create until bi_gemm_load_pins replaces it
+bi_status_t g_pins_env_status = BI_OK;
+std::string g_pins_env_error;
 int g_strict = -1;  // -1: read BI_GEMM_STRICT on first use
 
 // The default tiling when the table has no entry: the streaming kernel for
@@ -77,6 +95,79 @@ bool pin_legal(int N, int K, int splits, int stream_max_m, std::string* why)
     return true;
 }
 
+// A tiling list is legal when its bounds ascend, are positive, end with
+// INT32_MAX and every kernel is a known kind.
+bool tiling_legal(int count, const int* m_max, const int* kernel, std::string* why)
+{
+    if (count < 0 || count > BI_MAX_TILINGS) {
+        *why = "a tiling list has 0.." + std::to_string(BI_MAX_TILINGS) + " entries";
+        return false;
+    }
+    for (int i = 0; i < count; ++i) {
+        if (kernel[i] < 0 || kernel[i] >= BI_KERNEL_COUNT) {
+            *why = "unknown kernel kind " + std::to_string(kernel[i]);
+            return false;
+        }
+        if (m_max[i] < 1 || (i > 0 && m_max[i] <= m_max[i - 1])) {
+            *why = "tiling bounds must be positive and ascending";
+            return false;
+        }
+    }
+    if (count > 0 && m_max[count - 1] != INT32_MAX) {
+        *why = "the last tiling entry must cover every larger M";
+        return false;
+    }
+    return true;
+}
+
+// "M:kind,M:kind,...,*:kind" -> a tiling list
+bool parse_tiling(const char* text, Tiling* t, std::string* why)
+{
+    t->count = 0;
+    std::string item;
+    const std::string all(text);
+    size_t pos = 0;
+    while (pos <= all.size()) {
+        const size_t comma = all.find(',', pos);
+        item = all.substr(pos, comma == std::string::npos ? std::string::npos : comma - pos);
+        pos = comma == std::string::npos ? all.size() + 1 : comma + 1;
+        const size_t colon = item.find(':');
+        if (colon == std::string::npos || colon == 0) {
+            *why = "tiling entries are M:kind";
+            return false;
+        }
+        if (t->count == BI_MAX_TILINGS) {
+            *why = "too many tiling entries";
+            return false;
+        }
+        const std::string m = item.substr(0, colon), kind = item.substr(colon + 1);
+        int bound;
+        if (m == "*") {
+            bound = INT32_MAX;
+        } else {
+            char* end = nullptr;
+            const long v = std::strtol(m.c_str(), &end, 10);
+            if (!end || *end || v < 1 || v >= INT32_MAX) {
+                *why = "bad tiling bound '" + m + "'";
+                return false;
+            }
+            bound = (int)v;
+        }
+        int k = -1;
+        for (int c = 0; c < BI_KERNEL_COUNT; ++c)
+            if (kind == bigemm::kernel_kind_name(c))
+                k = c;
+        if (k < 0) {
+            *why = "unknown kernel kind '" + kind + "'";
+            return false;
+        }
+        t->m_max[t->count] = bound;
+        t->kernel[t->count] = k;
+        ++t->count;
+    }
+    return tiling_legal(t->count, t->m_max, t->kernel, why);
+}
+
 bi_status_t parse_pins(const char* path, PinTable* out)
 {
     FILE* f = std::fopen(path, "r");
@@ -84,8 +175,9 @@ bi_status_t parse_pins(const char* path, PinTable* out)
         return fail(BI_ERR_INVALID_ARGUMENT, std::string("cannot open pin table ") + path + ": " +
                                                  std::strerror(errno));
     PinTable t;
-    char line[512];
+    char line[640];
     int lineno = 0;
+    bool tree_seen = false;
     bi_status_t st = BI_OK;
     while (std::fgets(line, sizeof line, f)) {
         ++lineno;
@@ -95,6 +187,7 @@ bi_status_t parse_pins(const char* path, PinTable* out)
         char a[64];
         int n, k, s, sm, v;
         char extra[8];
+        char tiles[400];
         if (std::sscanf(line, " %63s", a) != 1)
             continue;  // blank
         if (std::strcmp(a, "version") == 0) {
@@ -105,9 +198,24 @@ bi_status_t parse_pins(const char* path, PinTable* out)
             t.version = v;
             continue;
         }
-        if (std::sscanf(line, " %63s %d %d %d %d %7s", a, &n, &k, &s, &sm, extra) != 5) {
+        if (std::strcmp(a, "tree") == 0) {
+            char id[200];
+            if (std::sscanf(line, " tree %199s %7s", id, extra) != 1) {
+                st = fail(BI_ERR_BAD_PIN_TABLE, "pin table line " + std::to_string(lineno) + ": bad tree line");
+                break;
+            }
+            if (std::strcmp(id, kTreeId) != 0) {
+                st = fail(BI_ERR_BAD_PIN_TABLE, "pin table line " + std::to_string(lineno) + ": the table was tuned for tree " +
+                                                    id + ", this library realises " + kTreeId);
+                break;
+            }
+            tree_seen = true;
+            continue;
+        }
+        const int got = std::sscanf(line, " %63s %d %d %d %d %399s %7s", a, &n, &k, &s, &sm, tiles, extra);
+        if (got != 5 && got != 6) {
             st = fail(BI_ERR_BAD_PIN_TABLE, "pin table line " + std::to_string(lineno) +
-                                                ": expected 'arch N K splits stream_max_m'");
+                                                ": expected 'arch N K splits stream_max_m [tilings]'");
             break;
         }
         std::string why;
@@ -117,6 +225,11 @@ bi_status_t parse_pins(const char* path, PinTable* out)
                                                 ": illegal pin " + (why.empty() ? "shape" : why));
             break;
         }
+        Tiling tiling;
+        if (got == 6 && !parse_tiling(tiles, &tiling, &why)) {
+            st = fail(BI_ERR_BAD_PIN_TABLE, "pin table line " + std::to_string(lineno) + ": " + why);
+            break;
+        }
         for (const PinRow& r : t.rows)
             if (r.arch == a && r.n == n && r.k == k) {
                 st = fail(BI_ERR_BAD_PIN_TABLE, "pin table line " + std::to_string(lineno) + ": duplicate shape");
@@ -124,11 +237,14 @@ bi_status_t parse_pins(const char* path, PinTable* out)
             }
         if (st != BI_OK)
             break;
-        t.rows.push_back(PinRow{a, n, k, s, sm});
+        t.rows.push_back(PinRow{a, n, k, s, sm, tiling});
     }
     std::fclose(f);
     if (st == BI_OK && t.version == 0)
         st = fail(BI_ERR_BAD_PIN_TABLE, "pin table has no version line");
+    if (st == BI_OK && !tree_seen)
+        st = fail(BI_ERR_BAD_PIN_TABLE, std::string("pin table has no tree line (this library realises ") +
+                                            kTreeId + ")");
     if (st == BI_OK)
         *out = std::move(t);
     return st;
@@ -141,8 +257,13 @@ void check_env_locked()
         const char* p = std::getenv("BI_GEMM_PINS");
         if (p && *p) {
             PinTable t;
-            if (parse_pins(p, &t) == BI_OK)
+            const bi_status_t st = parse_pins(p, &t);
+            if (st == BI_OK) {
                 g_pins = std::move(t);
+            } else {
+                g_pins_env_status = st;
+                g_pins_env_error = std::string("BI_GEMM_PINS=") + p + ": " + g_last_error;
+            }
         }
     }
     if (g_strict < 0) {
@@ -237,12 +358,28 @@ bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info*
 
     // the pin: forced (tuner), table, or default
     int splits = 1, stream_max_m = kDefaultStreamMaxM, from_table = 0, version = 0;
+    Tiling tiling;
     if (forced) {
         std::string why;
-        if (!pin_legal(N, K, forced->splits, forced->stream_max_m, &why))
+        if (!pin_legal(N, K, forced->splits, forced->stream_max_m, &why) ||
+            !tiling_legal(forced->tilings, forced->tile_m_max, forced->tile_kernel, &why))
             return fail(BI_ERR_INVALID_ARGUMENT, "illegal pin: " + why);
         splits = forced->splits;
         stream_max_m = forced->stream_max_m;
+        tiling.count = forced->tilings;
+        for (int i = 0; i < tiling.count; ++i) {
+            tiling.m_max[i] = forced->tile_m_max[i];
+            tiling.kernel[i] = forced->tile_kernel[i];
+        }
+    }
+
+    if (!forced) {
+        // a table named by BI_GEMM_PINS that failed to load stops every
+        // create that would read it, before any HIP call
+        std::lock_guard<std::mutex> g(g_pin_mu);
+        check_env_locked();
+        if (g_pins_env_status != BI_OK)
+            return fail(g_pins_env_status, g_pins_env_error);
     }
 
     int dev;
@@ -256,7 +393,8 @@ bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info*
 
     if (!forced) {
         std::lock_guard<std::mutex> g(g_pin_mu);
-        check_env_locked();
+        if (g_pins_env_status != BI_OK)
+            return fail(g_pins_env_status, g_pins_env_error);
         const PinRow* row = nullptr;
         for (const PinRow& r : g_pins.rows)
             if (r.n == N && r.k == K && info.arch.compare(0, r.arch.size(), r.arch) == 0)
@@ -264,6 +402,7 @@ bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info*
         if (row) {
             splits = row->splits;
             stream_max_m = row->stream_max_m;
+            tiling = row->tiling;
             from_table = 1;
             version = g_pins.version;
         } else if (g_strict) {
@@ -307,6 +446,12 @@ bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info*
     h->plan.splits = splits;
     h->plan.stream_max_m = stream_max_m;
     h->plan.num_cus = info.num_cus;
+    // a grouped handle always uses the built-in split between its kernels
+    h->plan.tilings = E > 0 ? 0 : tiling.count;
+    for (int i = 0; i < h->plan.tilings; ++i) {
+        h->plan.tile_m_max[i] = tiling.m_max[i];
+        h->plan.tile_kernel[i] = tiling.kernel[i];
+    }
     bi_pin_info& p = h->pin;
     std::memset(&p, 0, sizeof p);
     p.n = N;
@@ -322,6 +467,11 @@ bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info*
     p.stream_max_m = stream_max_m;
     p.from_table = from_table;
     p.table_version = version;
+    p.tilings = h->plan.tilings;
+    for (int i = 0; i < p.tilings; ++i) {
+        p.tile_m_max[i] = h->plan.tile_m_max[i];
+        p.tile_kernel[i] = h->plan.tile_kernel[i];
+    }
     try {
         std::lock_guard<std::mutex> g(g_live_mu);
         g_live.insert(h);
@@ -369,18 +519,25 @@ bi_status_t api_device(int* dev, int* num_cus)
 
 extern "C" {
 
+const char* bi_gemm_tree_id(void) { return kTreeId; }
+
+const char* bi_gemm_kernel_kind_name(int kind) { return bigemm::kernel_kind_name(kind); }
+
 bi_status_t bi_gemm_load_pins(const char* path)
 {
     std::lock_guard<std::mutex> g(g_pin_mu);
     g_pins_env_checked = true;
     if (!path) {
         g_pins = PinTable();
+        g_pins_env_status = BI_OK;
         return BI_OK;
     }
     PinTable t;
     bi_status_t st = parse_pins(path, &t);
-    if (st == BI_OK)
+    if (st == BI_OK) {
         g_pins = std::move(t);
+        g_pins_env_status = BI_OK;
+    }
     return st;
 }
 
@@ -540,7 +697,7 @@ const char* bi_gemm_kernel_name(bi_gemm_t hh, int M)
     if (!h || M <= 0)
         return "";
     if (h->plan.experts != 0)
-        return "bigemm_stream_grouped+bigemm_tiled_grouped<128x128>";
+        return bigemm::grouped_kernel_name(h->plan, M);
     return bigemm::dense_kernel_name(bigemm::choose_dense(h->plan, M));
 }
 

@@ -32,16 +32,33 @@ struct Plan {
     int stream_max_m;      // rows per expert/call at or below which the
                            // weight-streaming kernel runs
     int num_cus;           // compute units of the bound device
+    int tilings;           // dense tiling list from the pin (0: built-in rule)
+    int tile_m_max[BI_MAX_TILINGS];
+    int tile_kernel[BI_MAX_TILINGS];
 };
 
 // The dense kernels `run` may launch; M picks one, the tree is the same.
+// The values are the public bi_kernel_kind_t.
 enum class DenseKernel {
-    kStream16, kStream32, kStream64,
-    kTiled64x32, kTiled64, kTiled128x64, kTiled128x64Deep, kTiled128, kTiled128Deep, kTiled128x256,
-    kTiled256
+    kStream16 = BI_KERNEL_STREAM_MB1,
+    kStream32 = BI_KERNEL_STREAM_MB2,
+    kStream64 = BI_KERNEL_STREAM_MB4,
+    kTiled64x32 = BI_KERNEL_TILED_64X32,
+    kTiled64 = BI_KERNEL_TILED_64X64,
+    kTiled128x64 = BI_KERNEL_TILED_128X64,
+    kTiled128x64Deep = BI_KERNEL_TILED_128X64_DEEP,
+    kTiled128 = BI_KERNEL_TILED_128X128,
+    kTiled128Deep = BI_KERNEL_TILED_128X128_DEEP,
+    kTiled128x256 = BI_KERNEL_TILED4_128X256,
+    kTiled256 = BI_KERNEL_TILED4_256X256,
 };
 DenseKernel choose_dense(const Plan& p, int M);
 const char* dense_kernel_name(DenseKernel k);
+// Table name of a kind ("" when unknown).
+const char* kernel_kind_name(int kind);
+// The launches a grouped call with R rows makes, e.g.
+// "bigemm_stream_grouped+bigemm_tiled4_grouped".
+const char* grouped_kernel_name(const Plan& p, int R);
 
 // Host helpers the MoE layer's API shares with the GEMM API
 // (bigemm_api.cpp): record the calling thread's bi_last_error() and return

@@ -1258,6 +1258,10 @@ hipError_t pack_weights(const void* W, void* packed, int E, int N, int K, hipStr
 
 DenseKernel choose_dense(const Plan& p, int M)
 {
+    // the pin's tiling list, when it has one: the entry whose row range holds M
+    for (int i = 0; i < p.tilings; ++i)
+        if (M <= p.tile_m_max[i])
+            return static_cast<DenseKernel>(p.tile_kernel[i]);
     if (M <= p.stream_max_m) {
         if (M <= 16)
             return DenseKernel::kStream16;
@@ -1273,6 +1277,24 @@ DenseKernel choose_dense(const Plan& p, int M)
             return blocks <= p.num_cus ? t.deep : t.kind;
     }
     return DenseKernel::kTiled64x32;
+}
+
+const char* kernel_kind_name(int kind)
+{
+    switch (kind) {
+    case BI_KERNEL_STREAM_MB1: return "stream_mb1";
+    case BI_KERNEL_STREAM_MB2: return "stream_mb2";
+    case BI_KERNEL_STREAM_MB4: return "stream_mb4";
+    case BI_KERNEL_TILED_64X32: return "tiled_64x32";
+    case BI_KERNEL_TILED_64X64: return "tiled_64x64";
+    case BI_KERNEL_TILED_128X64: return "tiled_128x64";
+    case BI_KERNEL_TILED_128X64_DEEP: return "tiled_128x64_deep";
+    case BI_KERNEL_TILED_128X128: return "tiled_128x128";
+    case BI_KERNEL_TILED_128X128_DEEP: return "tiled_128x128_deep";
+    case BI_KERNEL_TILED4_128X256: return "tiled4_128x256";
+    case BI_KERNEL_TILED4_256X256: return "tiled4_256x256";
+    }
+    return "";
 }
 
 const char* dense_kernel_name(DenseKernel k)
@@ -1346,17 +1368,49 @@ hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, floa
     return hipSuccess;
 }
 
+namespace {
+
+// How a grouped call with R rows splits its experts between the kernels,
+// decided on the host from R and E alone.  Experts with 1..smax rows go to
+// the streaming kernel; the others to the four-wave kernel when the experts
+// average 16 rows or more (big), else to the tiled kernel.  All realise the
+// same tree, so the split points only move work, never bits.  When the
+// experts average 64 rows or more, few have 16 or fewer: the four-wave
+// kernel takes those too (as 128-row blocks), which saves the streaming
+// launch (about 4 us when it finds no work).
+struct GroupedSplit {
+    int smax;  // rows at or below which an expert streams (0: no streaming launch)
+    bool big;  // the four-wave kernel takes every other expert
+    bool tiled_launch;  // the tiled kernel is launched (it returns at once when R <= smax)
+};
+
+GroupedSplit grouped_split(const Plan& p, int R)
+{
+    GroupedSplit g;
+    g.smax = R >= 64 * p.experts ? 0 : (p.stream_max_m < 16 ? p.stream_max_m : 16);
+    g.big = R >= 128 && R >= 16 * p.experts;
+    g.tiled_launch = !g.big && R > g.smax;
+    return g;
+}
+
+}  // namespace
+
+const char* grouped_kernel_name(const Plan& p, int R)
+{
+    const GroupedSplit g = grouped_split(p, R);
+    if (g.smax > 0) {
+        if (g.big)
+            return "bigemm_stream_grouped+bigemm_tiled4_grouped";
+        return g.tiled_launch ? "bigemm_stream_grouped+bigemm_tiled_grouped<128x128>" : "bigemm_stream_grouped";
+    }
+    return g.big ? "bigemm_tiled4_grouped" : "bigemm_tiled_grouped<128x128>";
+}
+
 hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int32_t* offsets,
                           int R, float* y, const int32_t* xidx, int xn, hipStream_t stream)
 {
-    // Experts with 1..smax rows go to the streaming kernel; the others to
-    // the four-wave kernel when the experts average 16 rows or more, else to
-    // the tiled kernel.  All realise the same tree, so the split points only
-    // move work, never bits.
-    // When the experts average 64 rows or more, few have 16 or fewer: the
-    // four-wave kernel takes those too (as 128-row blocks), which saves the
-    // streaming launch (about 4 us when it finds no work).
-    const int smax = R >= 64 * p.experts ? 0 : (p.stream_max_m < 16 ? p.stream_max_m : 16);
+    const GroupedSplit g = grouped_split(p, R);
+    const int smax = g.smax;
     const int klen = p.k / p.splits;
     for (int s = 0; s < p.splits; ++s) {
         const Split sp{s * klen, klen, s > 0};
@@ -1377,7 +1431,7 @@ hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int
         // average 16 rows or more; below that, most experts stream and the
         // few others fill a 128-row block poorly, so the tiled kernel's
         // 128x128 tiles serve them
-        const int big = (R >= 128 && R >= 16 * p.experts) ? 256 : 0;
+        const int big = g.big ? 256 : 0;
         if (big)  // every expert above the streaming threshold, whole
             err = run_tiled4_grouped(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, xidx, xn, stream);
         else

@@ -1,19 +1,29 @@
 """Offline pin tuner: choose one layer's pin from its shape and a workload profile.
 
 The pin of a layer (N, K) is its reduction tree -- the number S of contiguous
-equal K splits -- plus a tiling knob, the row count at or below which calls
-run the weight-streaming kernel.  Both are fixed before deployment and never
-read the batch (Detent, §3: pins and knobs form a commitment tuple fixed for
-a workload; §6: the tuner picks it per workload).
+equal K splits -- plus its tiling: which dense kernel (output block shape,
+streaming or tiled) serves each range of row counts M.  Both are fixed before
+deployment and never read the batch (Detent, §3: pins and knobs form a
+commitment tuple fixed for a workload; §6: the tuner picks it per workload).
+The tiling only moves work between kernels that realise the same tree, so it
+never changes an output bit; S does.
 
-Cost model (Detent, §6 eq. 3, restricted to one kernel family): a workload
-profile W = {(M, n)} lists the row counts its calls have and how often; the
-cost of a legal assignment a is T(a) = sum over W of n * t(M, a), with t
-measured on the device; the tuner returns argmin T.  Candidates are legal by
-construction (S divides K into whole 64-wide stages; the library checks it
-again); each is measured by creating a handle with the pin swapped in
-(Detent, §6 "Search": a repin swaps the constants without solving again).
-The grids here are small, so the search is exhaustive.
+Cost model (Detent, §6 eq. 3): a workload profile W = {(M, n)} lists the row
+counts its calls have and how often; the cost of a legal assignment a is
+T(a) = sum over W of n * t(M, a), with t measured on the device; the tuner
+returns argmin T.  An assignment is a tree S and a kernel per profile M.
+Given S, the kernels of different M do not interact, so the argmin picks the
+fastest kernel at each M, and the tree with the lowest resulting total.
+Candidates are legal by construction (S divides K into whole 64-wide stages;
+the library checks it again); each is measured by creating a handle with
+the pin swapped in (Detent, §6 "Search": a repin swaps the constants
+without solving again).  The grids are small, so the search is exhaustive,
+except that the weight streamers are not tried above 256 rows (they re-read
+W once per 16 rows per m-block there) -- a measured family of the pages is
+likewise a handful of candidates (Detent, §6 Fig. 6).
+
+Between two profile points the tiling switches at their geometric mean; the
+last kernel serves every larger M.
 
 Usage:
     python -m invariant_bi_gemm_amd.tuner --shape 4096x14336 \
@@ -21,18 +31,24 @@ Usage:
         --table invariant_bi_gemm_amd/pins/gfx950.txt --write
 
 The table keeps one line per (arch, N, K); writing replaces the shape's line,
-keeps the others and bumps the version (a new table version may give
-different bits, as a different commitment tuple does).
+keeps the others, bumps the version (a new table version may give different
+bits, as a different commitment tuple does) and names the library's tree.
 """
 from __future__ import annotations
 
 import argparse
+import math
 import os
 import sys
 
 SPLIT_CHOICES = (1, 2, 4, 7, 8, 14, 16)
-STREAM_CHOICES = (0, 16, 32, 64)
 MAX_SPLITS = 16
+STREAM_KINDS = ("stream_mb1", "stream_mb2", "stream_mb4")
+KERNEL_KINDS = ("stream_mb1", "stream_mb2", "stream_mb4", "tiled_64x32", "tiled_64x64", "tiled_128x64",
+                "tiled_128x64_deep", "tiled_128x128", "tiled_128x128_deep", "tiled4_128x256", "tiled4_256x256")
+STREAM_LIMIT = 256  # streamers are candidates at M <= this
+MAX_TILINGS = 12
+INT32_MAX = 2 ** 31 - 1
 
 
 def parse_profile(text: str):
@@ -61,42 +77,94 @@ def legal_splits(k: int, choices=SPLIT_CHOICES):
     return [s for s in choices if 1 <= s <= MAX_SPLITS and k % (64 * s) == 0]
 
 
-def candidates(n: int, k: int, profile, split_choices=SPLIT_CHOICES, stream_choices=STREAM_CHOICES):
-    """All legal (splits, stream_max_m) pairs; stream thresholds above the
-    profile's largest M are equivalent to it and dropped."""
-    mmax = max(m for m, _ in profile)
-    sm = sorted({min(v, mmax) for v in stream_choices})
-    return [(s, v) for s in legal_splits(k, split_choices) for v in sm]
+def kernel_candidates(m: int, kinds=KERNEL_KINDS):
+    """Kernel kinds tried at M rows."""
+    return [kd for kd in kinds if m <= STREAM_LIMIT or kd not in STREAM_KINDS]
 
 
 def cost(profile, timing):
-    """Detent eq. 3 for one family: sum of count * time over the profile."""
+    """Detent eq. 3: sum of count * time over the profile."""
     return sum(n * timing[m] for m, n in profile)
 
 
-def choose(profile, measure, cands):
-    """argmin over candidates of the profile cost; `measure(cand)` returns
-    {M: seconds}.  Ties go to the earlier candidate (fewer splits first)."""
-    best = None
+def choose(profile, measure, splits, kinds=KERNEL_KINDS):
+    """argmin over trees S and per-M kernels of the profile cost.
+
+    ``measure(s, kind)`` returns {M: seconds} for the profile's M (only the
+    M where ``kind`` is a candidate are read).  Returns (S, {M: kind},
+    {M: seconds}, report) with report = [(S, total, {M: (kind, seconds)})].
+    Ties go to the earlier candidate (fewer splits, earlier kind)."""
     report = []
-    for c in cands:
-        t = measure(c)
-        total = cost(profile, t)
-        report.append((c, total, t))
+    best = None
+    for s in splits:
+        per_m = {}
+        for kd in kinds:
+            t = measure(s, kd)
+            for m, _ in profile:
+                if kd in kernel_candidates(m, kinds) and (m not in per_m or t[m] < per_m[m][1]):
+                    per_m[m] = (kd, t[m])
+        total = cost(profile, {m: v[1] for m, v in per_m.items()})
+        report.append((s, total, per_m))
         if best is None or total < best[1]:
-            best = (c, total)
-    return best[0], report
+            best = (s, total, per_m)
+    s, _, per_m = best
+    return s, {m: v[0] for m, v in per_m.items()}, {m: v[1] for m, v in per_m.items()}, report
+
+
+def tiling_from_choice(choice):
+    """{M: kind} at the profile points -> [(m_max, kind)], the switch between
+    neighbouring points at their geometric mean, equal neighbours merged, the
+    last bound None (every larger M)."""
+    ms = sorted(choice)
+    out = []
+    for i, m in enumerate(ms):
+        bound = None if i + 1 == len(ms) else int(math.floor(math.sqrt(m * ms[i + 1])))
+        if out and out[-1][1] == choice[m]:
+            out[-1] = (bound, choice[m])
+        else:
+            out.append((bound, choice[m]))
+    if len(out) > MAX_TILINGS:
+        raise ValueError("the tiling needs %d entries, at most %d fit" % (len(out), MAX_TILINGS))
+    return out
+
+
+def stream_threshold(tiling, default=16):
+    """The largest M the tiling streams (grouped handles stream experts up to
+    it); `default` when it streams nothing."""
+    last = 0
+    for bound, kind in tiling:
+        if kind in STREAM_KINDS:
+            last = bound if bound is not None else 4096
+    return min(last, 4096) if last else default
+
+
+def format_tiling(tiling):
+    return ",".join("%s:%s" % ("*" if b is None else b, kd) for b, kd in tiling)
+
+
+def parse_tiling(text: str):
+    out = []
+    for item in text.split(","):
+        b, _, kd = item.partition(":")
+        if kd not in KERNEL_KINDS:
+            raise ValueError("unknown kernel kind %r" % kd)
+        out.append((None if b == "*" else int(b), kd))
+    bounds = [b for b, _ in out[:-1]]
+    if not out or out[-1][0] is not None or bounds != sorted(set(bounds)) or any(b < 1 for b in bounds):
+        raise ValueError("tiling bounds must ascend and end with '*': %r" % text)
+    return out
 
 
 # --- pin table ---------------------------------------------------------------
 
 def read_table(path: str):
-    """-> (version, header comment lines, {(arch, N, K): (splits, stream_max_m)})."""
+    """-> (version, tree, header comment lines, {(arch, N, K): (splits, stream_max_m, tiling)})."""
     version = 0
+    tree = None
     header = []
     rows = {}
     if not os.path.exists(path):
-        return version, header, rows
+        return version, tree, header, rows
     for line in open(path):
         raw = line.rstrip("\n")
         body = raw.split("#", 1)[0].split()
@@ -107,34 +175,44 @@ def read_table(path: str):
         if body[0] == "version":
             version = int(body[1])
             continue
+        if body[0] == "tree":
+            tree = body[1]
+            continue
         arch, n, k, s, sm = body[0], int(body[1]), int(body[2]), int(body[3]), int(body[4])
-        rows[(arch, n, k)] = (s, sm)
-    return version, header, rows
+        tiling = parse_tiling(body[5]) if len(body) > 5 else []
+        rows[(arch, n, k)] = (s, sm, tiling)
+    return version, tree, header, rows
 
 
-def write_table(path: str, version: int, header, rows):
-    lines = list(header) + ["version %d" % version]
+def write_table(path: str, version: int, tree: str, header, rows):
+    lines = list(header) + ["version %d" % version, "tree %s" % tree]
     for (arch, n, k) in sorted(rows):
-        s, sm = rows[(arch, n, k)]
+        s, sm, tiling = rows[(arch, n, k)]
         if not (1 <= s <= MAX_SPLITS and k % (64 * s) == 0 and n % 16 == 0 and 0 <= sm <= 4096):
             raise ValueError("illegal pin for %s N=%d K=%d: S=%d stream_max_m=%d" % (arch, n, k, s, sm))
-        lines.append("%s %d %d %d %d" % (arch, n, k, s, sm))
+        line = "%s %d %d %d %d" % (arch, n, k, s, sm)
+        if tiling:
+            parse_tiling(format_tiling(tiling))  # validates
+            line += " " + format_tiling(tiling)
+        lines.append(line)
     tmp = path + ".tmp%d" % os.getpid()
     with open(tmp, "w") as f:
         f.write("\n".join(lines) + "\n")
     os.replace(tmp, path)
 
 
-def update_table(path: str, arch: str, n: int, k: int, pin):
-    version, header, rows = read_table(path)
-    rows[(arch, n, k)] = (int(pin[0]), int(pin[1]))
-    write_table(path, version + 1, header, rows)
+def update_table(path: str, arch: str, n: int, k: int, pin, tree: str):
+    """pin = (splits, stream_max_m, tiling)."""
+    version, _, header, rows = read_table(path)
+    rows[(arch, n, k)] = (int(pin[0]), int(pin[1]), list(pin[2]))
+    write_table(path, version + 1, tree, header, rows)
 
 
 # --- measurement on the device ------------------------------------------------
 
 def device_measure(n: int, k: int, profile, reps: int = 20, rotate_bytes: float = 2 ** 30):
-    """A `measure` function timing bi_gemm_run with HIP events on cuda:0.
+    """A `measure(s, kind)` function timing bi_gemm_run with HIP events on
+    cuda:0, the kernel forced by a one-entry tiling list.
 
     Weights rotate over copies totalling `rotate_bytes` so that the Infinity
     Cache does not serve them to small-M calls.
@@ -151,11 +229,13 @@ def device_measure(n: int, k: int, profile, reps: int = 20, rotate_bytes: float 
     x = torch.randn(mmax, k, device="cuda:0").to(torch.bfloat16)
     ys = {m: torch.empty(m, n, device="cuda:0") for m, _ in profile}
 
-    def measure(cand):
-        s, sm = cand
-        hs = [_lib.Gemm(w, pin={"splits": s, "stream_max_m": sm}) for w in ws]
+    def measure(s, kind):
+        hs = [_lib.Gemm(w, pin={"splits": s, "stream_max_m": 0, "tiling": [(None, kind)]}) for w in ws]
         out = {}
         for m, _ in profile:
+            if kind not in kernel_candidates(m):
+                out[m] = float("inf")
+                continue
             for i in range(3):
                 hs[i % copies](x[:m], out=ys[m])
             torch.cuda.synchronize()
@@ -182,21 +262,30 @@ def main(argv=None):
     ap.add_argument("--table", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "pins", "gfx950.txt"))
     ap.add_argument("--write", action="store_true", help="write the chosen pin into the table")
     ap.add_argument("--splits", default=",".join(map(str, SPLIT_CHOICES)))
-    ap.add_argument("--stream", default=",".join(map(str, STREAM_CHOICES)))
+    ap.add_argument("--kinds", default=",".join(KERNEL_KINDS))
     ap.add_argument("--reps", type=int, default=20)
     args = ap.parse_args(argv)
     n, k = (int(v) for v in args.shape.lower().split("x"))
     profile = parse_profile(args.profile)
-    cands = candidates(n, k, profile, tuple(int(v) for v in args.splits.split(",")),
-                       tuple(int(v) for v in args.stream.split(",")))
+    kinds = tuple(v for v in args.kinds.split(",") if v)
+    for kd in kinds:
+        if kd not in KERNEL_KINDS:
+            raise SystemExit("unknown kernel kind %r" % kd)
+    splits = legal_splits(k, tuple(int(v) for v in args.splits.split(",")))
     measure = device_measure(n, k, profile, reps=args.reps)
-    best, report = choose(profile, measure, cands)
-    for (s, sm), total, t in report:
-        print("S=%-2d stream_max_m=%-4d cost %.1f us  %s" % (
-            s, sm, total * 1e6, " ".join("%d:%.1f" % (m, v * 1e6) for m, v in sorted(t.items()))), flush=True)
-    print("chosen: N=%d K=%d splits=%d stream_max_m=%d" % (n, k, best[0], best[1]), flush=True)
+    s, choice, times, report = choose(profile, measure, splits, kinds)
+    for s_, total, per_m in report:
+        print("S=%-2d cost %.1f us  %s" % (s_, total * 1e6, " ".join(
+            "%d:%s:%.1f" % (m, kd, t * 1e6) for m, (kd, t) in sorted(per_m.items()))), flush=True)
+    tiling = tiling_from_choice(choice)
+    smax = stream_threshold(tiling)
+    print("chosen: N=%d K=%d splits=%d stream_max_m=%d tiling=%s" % (n, k, s, smax, format_tiling(tiling)),
+          flush=True)
     if args.write:
-        update_table(args.table, args.arch, n, k, best)
+        from . import _lib
+
+        tree = _lib.load().bi_gemm_tree_id().decode()
+        update_table(args.table, args.arch, n, k, (s, smax, tiling), tree)
         print("wrote", args.table)
     return 0
 

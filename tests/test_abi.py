@@ -123,9 +123,9 @@ def test_pin_table_parses(lib):
     assert lib.bi_gemm_load_pins(bg.PIN_TABLE.encode()) == 0
 
 
-def test_pin_table_entries_legal():
+def test_pin_table_entries_legal(lib):
     rows = []
-    version = None
+    version = tree = None
     for line in open(bg.PIN_TABLE):
         line = line.split("#", 1)[0].split()
         if not line:
@@ -133,32 +133,119 @@ def test_pin_table_entries_legal():
         if line[0] == "version":
             version = int(line[1])
             continue
-        arch, n, k, s, smax = line[0], *map(int, line[1:])
+        if line[0] == "tree":
+            tree = line[1]
+            continue
+        arch, n, k, s, smax = line[0], *map(int, line[1:5])
         rows.append((arch, n, k))
         assert arch == "gfx950"
         assert n % 16 == 0 and k % 64 == 0
         assert 1 <= s <= 16 and k % (64 * s) == 0
         assert 0 <= smax <= 4096
+        if len(line) > 5:
+            entries = [e.split(":") for e in line[5].split(",")]
+            assert entries[-1][0] == "*"
+            bounds = [int(b) for b, _ in entries[:-1]]
+            assert bounds == sorted(set(bounds))
+            assert all(kd in bg.KERNEL_KINDS for _, kd in entries)
     assert version and version > 0
+    assert tree == lib.bi_gemm_tree_id().decode()
     assert len(rows) == len(set(rows))
     # every shape the workloads use has a pin
     for shape in ((128, 2048), (256, 512), (4096, 14336), (28672, 4096), (8192, 3584), (1536, 2048), (2048, 768)):
         assert ("gfx950",) + shape in rows
 
 
+def _head(lib):
+    return "version 1\ntree %s\n" % lib.bi_gemm_tree_id().decode()
+
+
 @pytest.mark.parametrize("body", [
-    "gfx950 256 512 1 16\n",                                # no version
-    "version 1\ngfx950 256 512 3 16\n",                     # 512 is not 3 equal 64-multiples
-    "version 1\ngfx950 256 512 32 16\n",                    # more than 16 splits
-    "version 1\ngfx950 256 500 1 16\n",                     # K not a multiple of 64
-    "version 1\ngfx950 256 512 1 16\ngfx950 256 512 1 8\n",  # duplicate shape
-    "version 1\ngfx950 256 512 1\n",                        # missing field
+    "TREE\ngfx950 256 512 1 16\n",                          # no version
+    "version 1\ngfx950 256 512 1 16\n",                     # no tree line
+    "version 1\ntree mfma_f32_32x32x16_bf16.other\ngfx950 256 512 1 16\n",  # tuned for another tree
+    "HEAD gfx950 256 512 3 16\n",                           # 512 is not 3 equal 64-multiples
+    "HEAD gfx950 256 512 32 16\n",                          # more than 16 splits
+    "HEAD gfx950 256 500 1 16\n",                           # K not a multiple of 64
+    "HEAD gfx950 256 512 1 16\ngfx950 256 512 1 8\n",       # duplicate shape
+    "HEAD gfx950 256 512 1\n",                              # missing field
+    "HEAD gfx950 256 512 1 16 64:tiled_64x64\n",            # tiling without '*'
+    "HEAD gfx950 256 512 1 16 64:tiled_64x64,32:tiled_64x32,*:tiled4_256x256\n",  # bounds not ascending
+    "HEAD gfx950 256 512 1 16 64:tiled_96x96,*:tiled4_256x256\n",                 # unknown kind
+    "HEAD gfx950 256 512 1 16 0:stream_mb1,*:tiled4_256x256\n",                   # bound below 1
+    "HEAD gfx950 256 512 1 16 *:tiled4_256x256 extra\n",    # trailing field
     "version x\n",
 ])
 def test_bad_pin_tables_rejected(lib, tmp_path, body):
+    body = body.replace("TREE\n", "tree %s\n" % lib.bi_gemm_tree_id().decode()).replace("HEAD ", _head(lib))
     assert lib.bi_gemm_load_pins(_table(tmp_path, body)) == BAD_TABLE
     assert "pin table" in lib.bi_last_error().decode()
     assert lib.bi_gemm_load_pins(bg.PIN_TABLE.encode()) == 0
+
+
+def test_tiled_pin_table_accepted(lib, tmp_path):
+    body = _head(lib) + "gfx950 256 512 1 16 16:stream_mb1,100:tiled_64x32,*:tiled4_256x256\n"
+    assert lib.bi_gemm_load_pins(_table(tmp_path, body)) == 0, lib.bi_last_error()
+    assert lib.bi_gemm_load_pins(bg.PIN_TABLE.encode()) == 0
+
+
+def test_kernel_kind_names(lib):
+    for i, name in enumerate(bg.KERNEL_KINDS):
+        assert lib.bi_gemm_kernel_kind_name(i).decode() == name
+    assert lib.bi_gemm_kernel_kind_name(len(bg.KERNEL_KINDS)).decode() == ""
+    assert lib.bi_gemm_kernel_kind_name(-1).decode() == ""
+
+
+def test_create_pinned_rejects_illegal_tilings(lib):
+    h = ctypes.c_void_p()
+    for tiling in ([(64, "tiled_64x64")],                                   # last bound not 'every M'
+                   [(64, "tiled_64x64"), (32, "tiled_64x32"), (None, "tiled4_256x256")],
+                   [(0, "stream_mb1"), (None, "tiled4_256x256")],
+                   [(None, 11)], [(None, -1)]):
+        p = BiPinInfo()
+        p.splits, p.stream_max_m = 1, 16
+        p.set_tiling(tiling)
+        assert lib.bi_gemm_create_pinned(256, 512, ctypes.c_void_p(4096), ctypes.byref(p), ctypes.byref(h)) == INV
+    p = BiPinInfo()
+    p.splits, p.stream_max_m, p.tilings = 1, 16, 13
+    assert lib.bi_gemm_create_pinned(256, 512, ctypes.c_void_p(4096), ctypes.byref(p), ctypes.byref(h)) == INV
+
+
+_ENV_PROBE = '''
+import ctypes, sys
+sys.path.insert(0, %r)
+import invariant_bi_gemm_amd._lib as L
+lib = L._declare(ctypes.CDLL(L.LIB_PATH))
+h = ctypes.c_void_p()
+st = lib.bi_gemm_create(256, 512, ctypes.c_void_p(4096), ctypes.byref(h))
+print(st, lib.bi_last_error().decode())
+st2 = lib.bi_gemm_load_pins(L.PIN_TABLE.encode())
+print(st2)
+'''
+
+
+@pytest.mark.parametrize("body,want", [
+    ("version 1\ngfx950 256 512 1 16\n", BAD_TABLE),  # malformed (no tree line)
+    (None, INV),                                      # missing file
+])
+def test_env_pin_table_failure_stops_create(lib, tmp_path, body, want):
+    """A BI_GEMM_PINS table that does not load makes create fail with its
+    error (before any HIP call) instead of using the default tree."""
+    import subprocess
+    import sys
+
+    path = str(tmp_path / "env_pins.txt")
+    if body is not None:
+        open(path, "w").write(body)
+    env = dict(os.environ, BI_GEMM_PINS=path)
+    out = subprocess.run([sys.executable, "-c", _ENV_PROBE % ROOT], env=env, capture_output=True, text=True,
+                         timeout=120)
+    assert out.returncode == 0, out.stderr
+    first, second = out.stdout.strip().splitlines()
+    st, msg = first.split(" ", 1)
+    assert int(st) == want, out.stdout
+    assert "BI_GEMM_PINS" in msg and path in msg
+    assert int(second) == 0
 
 
 def test_missing_pin_table(lib):

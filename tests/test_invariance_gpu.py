@@ -203,3 +203,21 @@ def test_every_kernel_configuration(gpu):
         assert_bits_equal(bits32(got), np.stack([ref[int(r)] for r in rows]), "%s M=%d" % (g.kernel_name(m), m))
         yr, a = oracle.gemm_f64(x[:m], w, rows=rows)
         assert_parity(got.cpu().numpy(), yr, a, "%s M=%d" % (g.kernel_name(m), m))
+
+
+def test_every_kernel_kind_forced_by_tiling(gpu):
+    """Each dense kernel kind, forced for every M by a one-entry tiling list
+    (the tuner's way of measuring it), gives every row the bits of the same
+    row computed alone by the default pin."""
+    n, k = 1024, 1024
+    w = synth.normal_bf16(160, (n, k), 0.02)
+    ms = [1, 5, 40, 130]
+    x = synth.normal_bf16(161, (max(ms), k))
+    wd, xd = to_dev(w), to_dev(x)
+    ref = singles(gpu.Gemm(wd), xd, np.arange(max(ms)))
+    for kind in gpu.KERNEL_KINDS:
+        g = gpu.Gemm(wd, pin={"splits": 1, "stream_max_m": 0, "tiling": [(None, kind)]})
+        assert g.pin["tiling"] == [(2 ** 31 - 1, kind)]
+        for m in ms:
+            assert_bits_equal(bits32(g(xd[:m])), ref[:m], "%s M=%d" % (kind, m))
+        g.close()

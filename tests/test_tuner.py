@@ -26,66 +26,93 @@ def test_legal_splits():
             assert k % (64 * s) == 0
 
 
-def test_candidates_drop_equivalent_thresholds():
-    prof = [(1, 1), (8, 1)]
-    c = tuner.candidates(256, 512, prof)
-    assert (1, 8) in c and (1, 16) not in c and (1, 0) in c
-    assert len(c) == len(set(c))
+def test_kernel_candidates():
+    assert tuner.kernel_candidates(1) == list(tuner.KERNEL_KINDS)
+    assert tuner.kernel_candidates(256) == list(tuner.KERNEL_KINDS)
+    big = tuner.kernel_candidates(257)
+    assert not any(k in tuner.STREAM_KINDS for k in big) and "tiled4_256x256" in big
 
 
 def test_cost_and_choose():
     prof = [(1, 10), (4096, 1)]
-    # synthetic timings: S = 2 is faster for M = 1 but slower at 4096
+    # synthetic timings per (S, kind): S = 2 is faster at M = 1 but slower at 4096
     table = {
-        (1, 16): {1: 20e-6, 4096: 400e-6},
-        (2, 16): {1: 15e-6, 4096: 460e-6},
-        (1, 0): {1: 60e-6, 4096: 400e-6},
+        (1, "stream_mb1"): {1: 20e-6, 4096: float("inf")},
+        (1, "tiled4_256x256"): {1: 60e-6, 4096: 400e-6},
+        (2, "stream_mb1"): {1: 15e-6, 4096: float("inf")},
+        (2, "tiled4_256x256"): {1: 70e-6, 4096: 460e-6},
     }
-    best, report = tuner.choose(prof, lambda c: table[c], list(table))
-    assert tuner.cost(prof, table[(1, 16)]) == pytest.approx(600e-6)
-    assert tuner.cost(prof, table[(2, 16)]) == pytest.approx(610e-6)
-    assert best == (1, 16)
-    assert len(report) == 3
-    # heavier decode weight flips the choice
+    kinds = ("stream_mb1", "tiled4_256x256")
+    s, choice, times, report = tuner.choose(prof, lambda s_, kd: table[(s_, kd)], [1, 2], kinds)
+    assert s == 1 and choice == {1: "stream_mb1", 4096: "tiled4_256x256"}
+    assert tuner.cost(prof, times) == pytest.approx(600e-6)
+    assert [r[0] for r in report] == [1, 2]
+    assert report[1][1] == pytest.approx(610e-6)
+    # heavier decode weight flips the tree
     prof2 = [(1, 100), (4096, 1)]
-    best2, _ = tuner.choose(prof2, lambda c: table[c], list(table))
-    assert best2 == (2, 16)
+    s2, _, _, _ = tuner.choose(prof2, lambda s_, kd: table[(s_, kd)], [1, 2], kinds)
+    assert s2 == 2
+
+
+def test_tiling_from_choice():
+    choice = {1: "stream_mb1", 16: "stream_mb1", 64: "stream_mb4", 256: "tiled_64x64", 4096: "tiled4_256x256",
+              8192: "tiled4_256x256"}
+    t = tuner.tiling_from_choice(choice)
+    # switches at the geometric means sqrt(16*64) = 32, sqrt(64*256) = 128, sqrt(256*4096) = 1024
+    assert t == [(32, "stream_mb1"), (128, "stream_mb4"), (1024, "tiled_64x64"), (None, "tiled4_256x256")]
+    assert tuner.stream_threshold(t) == 128
+    assert tuner.stream_threshold([(None, "tiled_64x64")]) == 16
+    assert tuner.parse_tiling(tuner.format_tiling(t)) == t
+    for bad in ("64:tiled_64x64", "64:tiled_64x64,32:tiled_64x32,*:tiled4_256x256", "*:nope"):
+        with pytest.raises(ValueError):
+            tuner.parse_tiling(bad)
 
 
 def test_table_round_trip_and_c_parser(tmp_path):
     path = str(tmp_path / "pins.txt")
     with open(bg.PIN_TABLE) as f:
         open(path, "w").write(f.read())
-    v0, header, rows = tuner.read_table(path)
+    lib = bg.load()
+    tree = lib.bi_gemm_tree_id().decode()
+    v0, tree0, header, rows = tuner.read_table(path)
+    assert tree0 == tree
     assert rows[("gfx950", 4096, 14336)][0] >= 1 and header
-    tuner.update_table(path, "gfx950", 4096, 14336, (2, 32))
-    v1, header1, rows1 = tuner.read_table(path)
-    assert v1 == v0 + 1 and rows1[("gfx950", 4096, 14336)] == (2, 32) and header1 == header
+    tiling = [(32, "stream_mb1"), (128, "stream_mb4"), (None, "tiled4_256x256")]
+    tuner.update_table(path, "gfx950", 4096, 14336, (2, 128, tiling), tree)
+    v1, tree1, header1, rows1 = tuner.read_table(path)
+    assert v1 == v0 + 1 and tree1 == tree and header1 == header
+    assert rows1[("gfx950", 4096, 14336)] == (2, 128, tiling)
     assert {kk: vv for kk, vv in rows1.items() if kk != ("gfx950", 4096, 14336)} == \
            {kk: vv for kk, vv in rows.items() if kk != ("gfx950", 4096, 14336)}
-    lib = bg.load()
     try:
         assert lib.bi_gemm_load_pins(path.encode()) == 0, lib.bi_last_error()
     finally:
         assert lib.bi_gemm_load_pins(bg.PIN_TABLE.encode()) == 0
     with pytest.raises(ValueError):
-        tuner.update_table(path, "gfx950", 256, 512, (3, 16))  # 512 is not 3 equal parts
+        tuner.update_table(path, "gfx950", 256, 512, (3, 16, []), tree)  # 512 is not 3 equal parts
 
 
 @pytest.mark.gpu
 def test_tuner_on_device(gpu):
     """The tuner measures every legal candidate for a small layer and returns
     one of them; the chosen pin creates a working handle."""
-    prof = tuner.parse_profile("1:4,24:1,200:1")
-    cands = tuner.candidates(256, 512, prof, split_choices=(1, 2, 8), stream_choices=(0, 16))
+    prof = tuner.parse_profile("1:4,24:1,200:1,300:1")
+    kinds = ("stream_mb1", "stream_mb2", "tiled_64x32", "tiled4_128x256")
     measure = tuner.device_measure(256, 512, prof, reps=3, rotate_bytes=0)
-    best, report = tuner.choose(prof, measure, cands)
-    assert best in cands and len(report) == len(cands)
-    for _, total, t in report:
-        assert total > 0 and set(t) == {1, 24, 200}
+    s, choice, times, report = tuner.choose(prof, measure, [1, 2, 8], kinds)
+    assert s in (1, 2, 8) and len(report) == 3
+    assert set(choice) == {1, 24, 200, 300} and choice[300] not in tuner.STREAM_KINDS
+    for _, total, per_m in report:
+        assert 0 < total < float("inf") and set(per_m) == {1, 24, 200, 300}
+    tiling = tuner.tiling_from_choice(choice)
     import torch
 
     w = (torch.randn(256, 512, device="cuda:0") * 0.02).to(torch.bfloat16)
-    g = gpu.Gemm(w, pin={"splits": best[0], "stream_max_m": best[1]})
+    g = gpu.Gemm(w, pin={"splits": s, "stream_max_m": tuner.stream_threshold(tiling), "tiling": tiling})
+    assert g.pin["tiling"] == [(tuner.INT32_MAX if b is None else b, kd) for b, kd in tiling]
+    for m in (1, 24, 200, 300):
+        want = {"stream_mb1": "bigemm_stream<mb=1>", "stream_mb2": "bigemm_stream<mb=2>",
+                "tiled_64x32": "bigemm_tiled<64x32>", "tiled4_128x256": "bigemm_tiled<128x256>"}[choice[m]]
+        assert g.kernel_name(m) == want
     y = g(torch.randn(5, 512, device="cuda:0").to(torch.bfloat16))
     assert torch.isfinite(y).all()
