@@ -142,34 +142,37 @@ def _time_calls(fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+SPLITK_CHOICES = (1, 2, 4, 8)
+
+
 def invariance_cost(bg, ws, xd, ms, n, k, reps=10):
     """Cost of invariance: the pinned call at each M against the fastest
-    choice a batch-dependent selector could make at that M among the same
-    kernels (any split count, any streaming threshold), and hipBLASLt
-    (torch.matmul, bf16 output) as context, with whether its rows keep their
-    bits across M."""
-    import numpy as np
+    NON-invariant GEMM this library can run for that M -- any of its kernel
+    kinds with 1, 2, 4 or 8 concurrent K splits (bi_gemm_run_splitk), the
+    fastest chosen per M as a batch-dependent selector would (LLM-42 notes,
+    §2.3 Fig. 4a: the vendor GEMM adapts tile and split-K to the shape).  Both
+    timed back to back with weights rotating over the same copies.  hipBLASLt
+    (torch.matmul, bf16 output: half the output bytes) is context, with
+    whether its rows keep their bits across M."""
     import torch
 
-    import invariant_bi_gemm_amd.tuner as tuner
-
     copies = len(ws)
-    splits = [s for s in (1, 2, 4) if s in tuner.legal_splits(k)]
-    cands = [(s_, sm) for s_ in splits for sm in (0, 16, 64)]
     ys = {m: torch.empty((m, n), dtype=torch.float32, device="cuda:0") for m in ms}
-    # the pinned handles, timed the same way as the alternatives
     pinned_hs = [bg.Gemm(w) for w in ws]
     pinned = {m: _time_calls(lambda i: pinned_hs[i % copies](xd[:m], out=ys[m]), reps) for m in ms}
-    best = {m: (pinned[m], tuple(pinned_hs[0].pin[f] for f in ("splits", "stream_max_m"))) for m in ms}
-    for s_, sm in cands:
-        hs = [bg.Gemm(w, pin={"splits": s_, "stream_max_m": sm}) for w in ws]
-        for m in ms:
-            t = _time_calls(lambda i: hs[i % copies](xd[:m], out=ys[m]), reps)
-            if t < best[m][0]:
-                best[m] = (t, (s_, sm))
-        for h in hs:
-            h.close()
-    pinned_ms = pinned
+    splits = [p for p in SPLITK_CHOICES if k % (64 * p) == 0]
+    best = {}
+    for m in ms:
+        wsp = torch.empty(max(splits) * m * n, dtype=torch.float32, device="cuda:0")
+        for kind in bg.KERNEL_KINDS:
+            if kind.startswith("stream") and m > 256:
+                continue
+            for p_ in splits:
+                t = _time_calls(lambda i: pinned_hs[i % copies].run_splitk(xd[:m], kind, p_, out=ys[m],
+                                                                            workspace=wsp), reps)
+                if m not in best or t < best[m][0]:
+                    best[m] = (t, kind, p_)
+        del wsp
     rows = []
     tot_pin = tot_best = tot_blas = 0.0
     wts = [w.t() for w in ws]
@@ -178,21 +181,98 @@ def invariance_cost(bg, ws, xd, ms, n, k, reps=10):
     for m in ms:
         tb = _time_calls(lambda i: torch.matmul(xd[:m], wts[i % copies]), reps)
         same = bool(torch.equal(torch.matmul(xd[:m], wts[0])[:1].view(torch.int16), ref_row))
-        tot_pin += pinned_ms[m]
+        tot_pin += pinned[m]
         tot_best += best[m][0]
         tot_blas += tb
-        rows.append({"M": m, "pinned_us": round(pinned_ms[m] * 1e3, 2),
-                     "best_per_M_us": round(best[m][0] * 1e3, 2),
-                     "best_choice": list(best[m][1]) if best[m][1] else None,
+        rows.append({"M": m, "pinned_us": round(pinned[m] * 1e3, 2),
+                     "noninvariant_us": round(best[m][0] * 1e3, 2),
+                     "noninvariant_choice": {"kernel": best[m][1], "concurrent_splits": best[m][2]},
+                     "invariant_over_noninvariant": round(pinned[m] / best[m][0], 3),
                      "hipblaslt_bf16out_us": round(tb * 1e3, 2),
                      "hipblaslt_row0_same_bits_as_M1": same})
-    return {"what": "pinned tree vs the fastest per-M choice of split count and kernel "
-                    "(a batch-dependent selector) over the same kernels, both timed back to back "
-                    "with rotated weights; hipBLASLt (torch.matmul, bf16 output) as context",
-            "ratio_pinned_over_best_per_M": round(tot_pin / tot_best, 4),
+    return {"what": "pinned (batch-invariant) call vs the fastest non-invariant GEMM of this library at each M "
+                    "(any kernel kind, 1/2/4/8 concurrent K splits, chosen per M), both timed back to back "
+                    "with rotated weights, fp32 output; hipBLASLt (torch.matmul, bf16 output) as context",
+            "ratio_invariant_over_noninvariant_sweep": round(tot_pin / tot_best, 4),
             "pinned_sweep_ms": round(tot_pin, 4),
-            "hipblaslt_sweep_ms": round(tot_blas, 4),
+            "noninvariant_sweep_ms": round(tot_best, 4),
+            "hipblaslt_bf16out_sweep_ms": round(tot_blas, 4),
             "per_m": rows}
+
+
+class ClockSampler:
+    """The GPU's graphics clock sampled from a host thread while work runs
+    (amdsmi GPU metrics, read only); `mean_ghz` is None when the metrics are
+    not readable."""
+
+    KEYS = ("current_gfxclk", "average_gfxclk_frequency")
+
+    def __init__(self, period_s=0.002):
+        import threading
+
+        self.samples = []
+        self.source = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._period = period_s
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()
+        except Exception as e:  # noqa: BLE001 (metrics are optional)
+            self._amdsmi = None
+            self.error = "%s: %s" % (type(e).__name__, e)
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+        for key in self.KEYS:
+            v = m.get(key)
+            if isinstance(v, (list, tuple)):
+                v = [u for u in v if isinstance(u, (int, float)) and 0 < u < 10000]
+                v = sum(v) / len(v) if v else None
+            if isinstance(v, (int, float)) and 0 < v < 10000:
+                self.source = "amdsmi gpu_metrics %s" % key
+                return float(v)
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v:
+                    self.samples.append(v)
+            except Exception:  # noqa: BLE001
+                pass
+            self._stop.wait(self._period)
+
+    def __enter__(self):
+        import threading
+
+        if self._amdsmi is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        if self._amdsmi is not None:
+            try:
+                self._amdsmi.amdsmi_shut_down()
+            except Exception:  # noqa: BLE001
+                pass
+
+    @property
+    def mean_ghz(self):
+        return sum(self.samples) / len(self.samples) / 1000.0 if self.samples else None
+
+
+# MI355X's peak engine clock: the nominal bf16 peak is quoted at it
+PEAK_CLOCK_GHZ = 2.4
 
 
 def run_moe(args, bg):
@@ -888,13 +968,15 @@ def main(argv=None):
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record()
-    for s in range(args.steps):
-        step(ev[s])
-    t_end.record()
-    torch.cuda.synchronize()
+    with ClockSampler() as clock:
+        t_start.record()
+        for s in range(args.steps):
+            step(ev[s])
+        t_end.record()
+        torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    per_call_ms = {m: float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
+    # per call: the median over the timed steps of its launch's event pair
+    per_call_ms = {m: float(np.median([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
                    for j, m in enumerate(ms)}
 
     step_flops = sum(flops.values())
@@ -922,6 +1004,15 @@ def main(argv=None):
     roof["kernel"] = dom
     roof["launches_per_step"] = d["launches"]
     roof["avg_launch_us"] = d["ms"] * 1e3 / d["launches"]
+    roof["launch_us_statistic"] = "median over the timed steps, per launch"
+    # the MFMA peak scales with the engine clock: the same fraction against
+    # the peak at the clock sampled during the timed region
+    roof["sustained_clock_ghz"] = round(clock.mean_ghz, 3) if clock.mean_ghz else None
+    roof["clock_source"] = clock.source if clock.mean_ghz else getattr(clock, "error", "no samples")
+    if clock.mean_ghz and roof["bound"] == "mfma":
+        peak_at_clock = PEAK_BF16_TFLOPS * clock.mean_ghz / PEAK_CLOCK_GHZ
+        roof["peak_at_sustained_clock"] = round(peak_at_clock, 1)
+        roof["frac_at_sustained_clock"] = roof["achieved"] / peak_at_clock
 
     per_m = []
     for m in ms:

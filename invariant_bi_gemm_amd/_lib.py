@@ -14,7 +14,9 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libbigemm.so")
+# BI_GEMM_LIB may name another build of the same library (the CPU tests'
+# AddressSanitizer copy); there is no other implementation to fall back to
+LIB_PATH = os.environ.get("BI_GEMM_LIB") or os.path.join(HERE, "libbigemm.so")
 PIN_TABLE = os.path.join(HERE, "pins", "gfx950.txt")
 
 STATUS = {
@@ -83,6 +85,7 @@ def _declare(lib):
         "bi_gemm_create": ([I, I, P, ctypes.POINTER(P)], S),
         "bi_gemm_create_pinned": ([I, I, P, ctypes.POINTER(BiPinInfo), ctypes.POINTER(P)], S),
         "bi_gemm_run": ([P, P, I, P, P], S),
+        "bi_gemm_run_splitk": ([P, P, I, P, I, I, P, P], S),
         "bi_grouped_gemm_create": ([I, I, I, P, ctypes.POINTER(P)], S),
         "bi_grouped_gemm_run": ([P, P, P, I, P, P], S),
         "bi_gemm_destroy": ([P], None),
@@ -221,6 +224,30 @@ class Gemm:
         """Raw call: device pointers and the row count, as the C ABI takes them."""
         check(self._lib.bi_gemm_run(self._h, ctypes.c_void_p(x_ptr), int(m), ctypes.c_void_p(y_ptr),
                                     _stream_ptr(stream)))
+
+    def run_splitk(self, x, kind, splits, out=None, workspace=None, stream=None):
+        """The NON-invariant comparison GEMM (include/bi_gemm_ref.h): kernel
+        ``kind`` (a name of KERNEL_KINDS or its index) over ``splits``
+        concurrent K splits.  ``workspace``: fp32 with at least
+        (splits-1)*M*N elements (allocated here when None)."""
+        import torch
+
+        _need(x, torch.bfloat16, 2, "x")
+        if x.shape[1] != self.k:
+            raise ValueError("x has K=%d, the layer has K=%d" % (x.shape[1], self.k))
+        m = int(x.shape[0])
+        if out is None:
+            out = torch.empty((m, self.n), dtype=torch.float32, device=x.device)
+        if workspace is None and splits > 1:
+            workspace = torch.empty((splits - 1) * m * self.n, dtype=torch.float32, device=x.device)
+        if workspace is not None and workspace.numel() < (splits - 1) * m * self.n:
+            raise ValueError("workspace too small")
+        k = KERNEL_KINDS.index(kind) if isinstance(kind, str) else int(kind)
+        check(self._lib.bi_gemm_run_splitk(self._h, ctypes.c_void_p(x.data_ptr()), m, ctypes.c_void_p(out.data_ptr()),
+                                           k, int(splits),
+                                           ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0),
+                                           _stream_ptr(stream)))
+        return out
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:

@@ -34,11 +34,29 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libbigemm.so (always recompiles)."""
+# AddressSanitizer on the host code only (argument checks, handles, the pin
+# table parser); the device code is built exactly as in the product library.
+ASAN_HOST_FLAGS = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer -shared-libsan".split()
+
+
+def asan_runtime() -> str:
+    """The sanitizer runtime hipcc links the host code against (to preload
+    into a Python process that loads the sanitized library)."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the host AddressSanitizer runtime was not found")
+    return path
+
+
+def build(verbose: bool = False, asan: bool = False, out: str | None = None, check_asm: bool = True) -> str:
+    """Compile every source into libbigemm.so (always recompiles), then check
+    the built code of the four-wave kernels (asm_check).  asan: a copy with
+    the host code under AddressSanitizer, at `out`, for the CPU ABI tests."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *srcs]
+    target = out or LIB
+    tmp = target + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, *(ASAN_HOST_FLAGS if asan else []), "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,9 +66,24 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
+    if check_asm and not asan:
+        from . import asm_check
+
+        problems = asm_check.problems(asm_check.assemble(target + ".s"))
+        os.remove(target + ".s")
+        if problems:
+            raise RuntimeError("the built four-wave kernels fail their code checks:\n  " + "\n  ".join(problems))
+        if verbose:
+            print("built-code checks of the four-wave kernels: ok")
+    return target
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if __package__ in (None, ""):
+        sys.path.insert(0, os.path.dirname(HERE))
+        from invariant_bi_gemm_amd import build as _self
+
+        print(_self.build(verbose=True))
+    else:
+        print(build(verbose=True))

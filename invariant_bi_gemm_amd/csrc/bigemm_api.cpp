@@ -20,6 +20,7 @@
 #include <unordered_set>
 #include <vector>
 
+#include "../../include/bi_gemm_ref.h"
 #include "bigemm_internal.h"
 
 namespace {
@@ -599,6 +600,46 @@ bi_status_t bi_gemm_run(bi_gemm_t hh, const void* x, int M, float* y, void* stre
     if (st != BI_OK)
         return st;
     hipError_t e = bigemm::launch_dense(h->plan, h->W, x, M, y, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(BI_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return BI_OK;
+}
+
+bi_status_t bi_gemm_run_splitk(bi_gemm_t hh, const void* x, int M, float* y, int kind, int splits, float* workspace,
+                               void* stream)
+{
+    bi_gemm* h = handle_of(hh);
+    if (!h)
+        return fail(BI_ERR_INVALID_ARGUMENT, "invalid handle");
+    if (h->plan.experts != 0)
+        return fail(BI_ERR_INVALID_ARGUMENT, "grouped handle passed to bi_gemm_run_splitk");
+    if (kind < 0 || kind >= BI_KERNEL_COUNT)
+        return fail(BI_ERR_INVALID_ARGUMENT, "unknown kernel kind");
+    if (splits < 1 || splits > bigemm::kMaxSplits || h->plan.k % (splits * bigemm::kKGranule) != 0)
+        return fail(BI_ERR_INVALID_ARGUMENT, "splits must be within 1..16 and cut K into equal multiples of 64");
+    if (M < 0)
+        return fail(BI_ERR_INVALID_ARGUMENT, "M must be >= 0");
+    if (M == 0)
+        return BI_OK;
+    if (!x || !y || (splits > 1 && !workspace))
+        return fail(BI_ERR_INVALID_ARGUMENT, "x, y or workspace is NULL");
+    if (!aligned16(x) || !aligned16(y) || (splits > 1 && !aligned16(workspace)))
+        return fail(BI_ERR_MISALIGNED, "x, y and workspace must be 16-byte aligned");
+    const long long wide = h->plan.n > h->plan.k ? h->plan.n : h->plan.k;
+    if ((long long)M * wide >= (1LL << 31))
+        return fail(BI_ERR_INVALID_ARGUMENT, "M*max(N,K) must be below 2^31");
+    if (splits > 1) {
+        const char* wb = reinterpret_cast<const char*>(workspace);
+        const char* yb = reinterpret_cast<const char*>(y);
+        const size_t ybytes = (size_t)M * h->plan.n * 4, wbytes = ybytes * (size_t)(splits - 1);
+        if (wb < yb + ybytes && yb < wb + wbytes)
+            return fail(BI_ERR_INVALID_ARGUMENT, "workspace must not overlap y");
+    }
+    bi_status_t st = check_run_device(h);
+    if (st != BI_OK)
+        return st;
+    hipError_t e = bigemm::launch_splitk(h->plan, kind, splits, h->W, x, M, y, workspace,
+                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(BI_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return BI_OK;

@@ -72,6 +72,10 @@ bi_status_t api_device(int* dev, int* num_cus);
 hipError_t pack_weights(const void* W, void* packed, int E, int N, int K, hipStream_t stream);
 hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, float* y,
                         hipStream_t stream);
+// Non-invariant comparison: kernel `kind` over `splits` concurrent K splits,
+// partials of splits 1.. in part ([splits-1][M][N] fp32), then added to y.
+hipError_t launch_splitk(const Plan& p, int kind, int splits, const void* W, const void* x, int M, float* y,
+                         float* part, hipStream_t stream);
 // xidx (optional): row i of the grouped x is row xidx[i] of x (xn rows).
 hipError_t launch_grouped(const Plan& p, const void* W, const void* x,
                           const int32_t* offsets, int R, float* y, const int32_t* xidx, int xn,

@@ -146,6 +146,25 @@ __device__ __forceinline__ void emit4(float* p, const f32x4& v, int fold)
     }
 }
 
+// Concurrent split-K for the non-invariant comparison path only
+// (bi_gemm_run_splitk): the kernels instantiated with kCmp = true run split
+// blockIdx.y of gridDim.y, each a chain over its own K range from +0; split 0
+// stores into y and split s > 0 into partial s - 1 of `part` ([splits-1][M][N]),
+// which splitk_reduce adds to y afterwards.  Where the splits fall follows
+// the caller's choice per M, so rows are not batch-invariant there.  The
+// product kernels are the kCmp = false instances and never take this path.
+template <bool kCmp>
+__device__ __forceinline__ float* cmp_split(Split& sp, float* y, float* part, int M, int N)
+{
+    if constexpr (kCmp) {
+        sp.k0 = (int)blockIdx.y * sp.klen;
+        sp.fold = 0;
+        if (blockIdx.y > 0)
+            return part + (size_t)(blockIdx.y - 1) * M * N;
+    }
+    return y;
+}
+
 // XOR swizzle of 16-byte chunk c of row r in an LDS tile whose rows hold kCh
 // chunks.  An MFMA fragment read has 16 lanes reading one chunk of 16
 // consecutive rows.  The XOR terms are the ones measured free of LDS bank
@@ -512,14 +531,15 @@ __device__ __forceinline__ void tile_of_block(int b, int nblocks, int tiles_m, i
     *tn = r / rows;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NS>
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool kCmp = false>
 __global__ void __launch_bounds__(WM * WN * 64)
     bigemm_tiled(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                  float* __restrict__ y, int M, int N, int K, Split sp, int tiles_m, int tiles_n,
-                 int group_m)
+                 int group_m, float* part)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     __shared__ uint4 lds[NS * C::kStageUnits];
+    y = cmp_split<kCmp>(sp, y, part, M, N);
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
     tiled_block<BM, BN, WM, WN, BK, NS>(lds, x, W, y, tm * BM, M, tn * BN, N, K, sp);
@@ -758,12 +778,13 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
 }
 
 // (32 XT) x 256 output blocks, one per workgroup.
-template <int XT>
+template <int XT, bool kCmp = false>
 __global__ void __launch_bounds__(256)
     bigemm_tiled4(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ y, int M,
-                   int N, int K, Split sp, int tiles_m, int tiles_n, int group_m)
+                   int N, int K, Split sp, int tiles_m, int tiles_n, int group_m, float* part)
 {
     __shared__ uint4 lds[3 * 256 * 8 + 2 * 32 * XT * 8];
+    y = cmp_split<kCmp>(sp, y, part, M, N);
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
     tiled4_block<XT>(lds, x, W, y, tm * 32 * XT, M, tn * 256, N, K, sp);
@@ -1054,13 +1075,14 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
     }
 }
 
-template <int MB, int XR, int BKS, int NP>
+template <int MB, int XR, int BKS, int NP, bool kCmp = false>
 __global__ void __launch_bounds__((MB + NP) * 64)
     bigemm_stream(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
-                  float* __restrict__ y, int M, int N, int K, Split sp)
+                  float* __restrict__ y, int M, int N, int K, Split sp, float* part)
 {
     using C = StreamCfg<MB, XR, BKS, NP>;
     __shared__ uint4 ring[C::NR * C::kStageUnits];
+    y = cmp_split<kCmp>(sp, y, part, M, N);
     const int tiles_n = N / 16;
     const int mblocks = (M + 16 * MB - 1) / (16 * MB);
     stream_body<MB, XR, BKS, NP>(ring, x, W, y, N, K, sp, tiles_n, mblocks * tiles_n, M, nullptr, nullptr);
@@ -1096,40 +1118,59 @@ __global__ void __launch_bounds__((MB + NP) * 64)
 // ---------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------
+// ysplits > 1 (comparison path only): the kCmp instance over a grid of
+// ysplits concurrent K splits, partials of splits 1.. into `part`.
 template <int BM, int BN, int WM, int WN, int BK, int NS>
 hipError_t run_tiled(const void* W, const void* x, int M, float* y, int N, int K, Split sp,
-                     hipStream_t stream)
+                     hipStream_t stream, int ysplits = 1, float* part = nullptr)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int nblocks = tiles_m * tiles_n;
-    hipLaunchKernelGGL((bigemm_tiled<BM, BN, WM, WN, BK, NS>), dim3(nblocks), dim3(C::kThreads),
-                       0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
-                       y, M, N, K, sp, tiles_m, tiles_n, 4);
+    if (ysplits > 1)
+        hipLaunchKernelGGL((bigemm_tiled<BM, BN, WM, WN, BK, NS, true>), dim3(nblocks, ysplits), dim3(C::kThreads),
+                           0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
+                           y, M, N, K, sp, tiles_m, tiles_n, 4, part);
+    else
+        hipLaunchKernelGGL((bigemm_tiled<BM, BN, WM, WN, BK, NS>), dim3(nblocks), dim3(C::kThreads),
+                           0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
+                           y, M, N, K, sp, tiles_m, tiles_n, 4, nullptr);
     return hipGetLastError();
 }
 
 template <int XT>
-hipError_t run_tiled4(const void* W, const void* x, int M, float* y, int N, int K, Split sp, hipStream_t stream)
+hipError_t run_tiled4(const void* W, const void* x, int M, float* y, int N, int K, Split sp, hipStream_t stream,
+                      int ysplits = 1, float* part = nullptr)
 {
     const int tiles_m = (M + 32 * XT - 1) / (32 * XT);
     const int tiles_n = (N + 255) / 256;
-    hipLaunchKernelGGL(bigemm_tiled4<XT>, dim3(tiles_m * tiles_n), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K, sp, tiles_m,
-                       tiles_n, 4);
+    if (ysplits > 1)
+        hipLaunchKernelGGL((bigemm_tiled4<XT, true>), dim3(tiles_m * tiles_n, ysplits), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K, sp,
+                           tiles_m, tiles_n, 4, part);
+    else
+        hipLaunchKernelGGL(bigemm_tiled4<XT>, dim3(tiles_m * tiles_n), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K, sp,
+                           tiles_m, tiles_n, 4, nullptr);
     return hipGetLastError();
 }
 
 template <int MB, int XR, int BKS, int NP>
 hipError_t run_stream(const void* W, const void* x, int M, float* y, int N, int K, Split sp,
-                      int num_cus, hipStream_t stream)
+                      int num_cus, hipStream_t stream, int ysplits = 1, float* part = nullptr)
 {
     using C = StreamCfg<MB, XR, BKS, NP>;
     const int items = ((M + 16 * MB - 1) / (16 * MB)) * (N / 16);
     const int grid = items < num_cus ? items : num_cus;
-    hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP>), dim3(grid), dim3(C::kThreads), 0, stream,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K, sp);
+    if (ysplits > 1)
+        hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP, true>), dim3(grid, ysplits), dim3(C::kThreads), 0,
+                           stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K,
+                           sp, part);
+    else
+        hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP>), dim3(grid), dim3(C::kThreads), 0, stream,
+                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K, sp,
+                           nullptr);
     return hipGetLastError();
 }
 
@@ -1138,17 +1179,39 @@ hipError_t run_stream(const void* W, const void* x, int M, float* y, int N, int 
 // 64-row load group of that stage width needs.
 template <int MB, int XR>
 hipError_t run_stream_k(const void* W, const void* x, int M, float* y, int N, int K, Split sp,
-                        int num_cus, hipStream_t stream)
+                        int num_cus, hipStream_t stream, int ysplits = 1, float* part = nullptr)
 {
     if constexpr (MB == 1) {
         if (sp.klen % 512 == 0)
-            return run_stream<MB, XR, 512, stream_producers<MB, 512>()>(W, x, M, y, N, K, sp, num_cus, stream);
+            return run_stream<MB, XR, 512, stream_producers<MB, 512>()>(W, x, M, y, N, K, sp, num_cus, stream,
+                                                                        ysplits, part);
     }
     if (sp.klen % 256 == 0)
-        return run_stream<MB, XR, 256, stream_producers<MB, 256>()>(W, x, M, y, N, K, sp, num_cus, stream);
+        return run_stream<MB, XR, 256, stream_producers<MB, 256>()>(W, x, M, y, N, K, sp, num_cus, stream, ysplits,
+                                                                    part);
     if (sp.klen % 128 == 0)
-        return run_stream<MB, (XR < 4 ? 4 : XR), 128, stream_producers<MB, 128>()>(W, x, M, y, N, K, sp, num_cus, stream);
-    return run_stream<MB, (XR < 8 ? 8 : XR), 64, stream_producers<MB, 64>()>(W, x, M, y, N, K, sp, num_cus, stream);
+        return run_stream<MB, (XR < 4 ? 4 : XR), 128, stream_producers<MB, 128>()>(W, x, M, y, N, K, sp, num_cus,
+                                                                                   stream, ysplits, part);
+    return run_stream<MB, (XR < 8 ? 8 : XR), 64, stream_producers<MB, 64>()>(W, x, M, y, N, K, sp, num_cus, stream,
+                                                                             ysplits, part);
+}
+
+// y += part[0] + part[1] + ... (in that order), 4 values per thread and step:
+// the comparison path's combine of its concurrent splits.
+__global__ void __launch_bounds__(256)
+    splitk_reduce(float4* __restrict__ y, const float4* __restrict__ part, long long n4, int parts)
+{
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
+        float4 v = y[i];
+        for (int s = 0; s < parts; ++s) {
+            const float4 q = part[(long long)s * n4 + i];
+            v.x += q.x;
+            v.y += q.y;
+            v.z += q.z;
+            v.w += q.w;
+        }
+        y[i] = v;
+    }
 }
 
 template <int MB, int XR, int BKS, int NP>
@@ -1318,39 +1381,39 @@ const char* dense_kernel_name(DenseKernel k)
 namespace {
 
 hipError_t launch_dense_split(const Plan& p, DenseKernel kind, const void* W, const void* x, int M,
-                              float* y, Split sp, hipStream_t stream)
+                              float* y, Split sp, hipStream_t stream, int ys = 1, float* part = nullptr)
 {
     switch (kind) {
     case DenseKernel::kStream16:
         if (M <= 2)
-            return run_stream_k<1, 2>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
+            return run_stream_k<1, 2>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ys, part);
         if (M <= 4)
-            return run_stream_k<1, 4>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
+            return run_stream_k<1, 4>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ys, part);
         if (M <= 8)
-            return run_stream_k<1, 8>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
-        return run_stream_k<1, 16>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
+            return run_stream_k<1, 8>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ys, part);
+        return run_stream_k<1, 16>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ys, part);
     case DenseKernel::kStream32:
-        return run_stream_k<2, 32>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
+        return run_stream_k<2, 32>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ys, part);
     case DenseKernel::kStream64:
-        return run_stream_k<4, 64>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream);
+        return run_stream_k<4, 64>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ys, part);
     case DenseKernel::kTiled256:
-        return run_tiled4<8>(W, x, M, y, p.n, p.k, sp, stream);
+        return run_tiled4<8>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
     case DenseKernel::kTiled128x256:
-        return run_tiled4<4>(W, x, M, y, p.n, p.k, sp, stream);
+        return run_tiled4<4>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
     case DenseKernel::kTiled128:
-        return run_tiled<128, 128, 2, 2, 64, 2>(W, x, M, y, p.n, p.k, sp, stream);
+        return run_tiled<128, 128, 2, 2, 64, 2>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
     case DenseKernel::kTiled128x64:
-        return run_tiled<128, 64, 2, 2, 64, 3>(W, x, M, y, p.n, p.k, sp, stream);
+        return run_tiled<128, 64, 2, 2, 64, 3>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
     case DenseKernel::kTiled128x64Deep:
-        return run_tiled<128, 64, 2, 2, 64, 6>(W, x, M, y, p.n, p.k, sp, stream);
+        return run_tiled<128, 64, 2, 2, 64, 6>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
     case DenseKernel::kTiled128Deep:
-        return run_tiled<128, 128, 2, 4, 64, 4>(W, x, M, y, p.n, p.k, sp, stream);
+        return run_tiled<128, 128, 2, 4, 64, 4>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
     case DenseKernel::kTiled64x32:
-        return run_tiled<64, 32, 2, 2, 64, 8>(W, x, M, y, p.n, p.k, sp, stream);
+        return run_tiled<64, 32, 2, 2, 64, 8>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
     case DenseKernel::kTiled64:
         break;
     }
-    return run_tiled<64, 64, 2, 2, 64, 4>(W, x, M, y, p.n, p.k, sp, stream);
+    return run_tiled<64, 64, 2, 2, 64, 4>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
 }
 
 }  // namespace
@@ -1404,6 +1467,20 @@ const char* grouped_kernel_name(const Plan& p, int R)
         return g.tiled_launch ? "bigemm_stream_grouped+bigemm_tiled_grouped<128x128>" : "bigemm_stream_grouped";
     }
     return g.big ? "bigemm_tiled4_grouped" : "bigemm_tiled_grouped<128x128>";
+}
+
+hipError_t launch_splitk(const Plan& p, int kind, int splits, const void* W, const void* x, int M, float* y,
+                         float* part, hipStream_t stream)
+{
+    const Split sp{0, p.k / splits, 0};
+    hipError_t e = launch_dense_split(p, static_cast<DenseKernel>(kind), W, x, M, y, sp, stream, splits, part);
+    if (e != hipSuccess || splits == 1)
+        return e;
+    const long long n4 = (long long)M * p.n / 4;
+    const long long blocks = (n4 + 255) / 256;
+    hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream,
+                       reinterpret_cast<float4*>(y), reinterpret_cast<const float4*>(part), n4, splits - 1);
+    return hipGetLastError();
 }
 
 hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int32_t* offsets,

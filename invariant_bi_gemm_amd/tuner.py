@@ -87,22 +87,47 @@ def cost(profile, timing):
     return sum(n * timing[m] for m, n in profile)
 
 
-def choose(profile, measure, splits, kinds=KERNEL_KINDS):
+TIE = 0.03  # kernels within 3% of the fastest count as equally fast
+
+
+def pick_kernels(times, kinds=KERNEL_KINDS, tie=TIE):
+    """{M: {kind: seconds}} -> {M: (kind, seconds)}, ascending in M: the
+    fastest kind, except that the kind of the previous M is kept while it is
+    within `tie` of the fastest (timings of equal kernels differ by noise,
+    which would otherwise cut the tiling into many small ranges); ties
+    between new kinds go to the earlier kind."""
+    out, prev = {}, None
+    for m in sorted(times):
+        cand = [(t, kinds.index(kd), kd) for kd, t in times[m].items() if kd in kernel_candidates(m, kinds)]
+        best_t = min(c[0] for c in cand)
+        if prev is not None and prev in times[m] and prev in kernel_candidates(m, kinds) and \
+                times[m][prev] <= best_t * (1 + tie):
+            out[m] = (prev, times[m][prev])
+        else:
+            t, _, kd = min(cand)
+            out[m] = (kd, t)
+        prev = out[m][0]
+    return out
+
+
+def choose(profile, measure, splits, kinds=KERNEL_KINDS, tie=TIE):
     """argmin over trees S and per-M kernels of the profile cost.
 
     ``measure(s, kind)`` returns {M: seconds} for the profile's M (only the
     M where ``kind`` is a candidate are read).  Returns (S, {M: kind},
     {M: seconds}, report) with report = [(S, total, {M: (kind, seconds)})].
-    Ties go to the earlier candidate (fewer splits, earlier kind)."""
+    Per S the kernels are those of pick_kernels; ties between trees go to
+    the earlier candidate (fewer splits)."""
     report = []
     best = None
     for s in splits:
-        per_m = {}
+        times = {m: {} for m, _ in profile}
         for kd in kinds:
             t = measure(s, kd)
             for m, _ in profile:
-                if kd in kernel_candidates(m, kinds) and (m not in per_m or t[m] < per_m[m][1]):
-                    per_m[m] = (kd, t[m])
+                if kd in kernel_candidates(m, kinds):
+                    times[m][kd] = t[m]
+        per_m = pick_kernels(times, kinds, tie)
         total = cost(profile, {m: v[1] for m, v in per_m.items()})
         report.append((s, total, per_m))
         if best is None or total < best[1]:

@@ -99,8 +99,8 @@ def test_grouped_uses_the_dense_split_tree(gpu, tmp_path):
 
     e, n, k = 8, 256, 1024
     table = tmp_path / "pins.txt"
-    table.write_text("version 7\ngfx950 %d %d 2 16\n" % (n, k))
     lib = bg.load()
+    table.write_text("version 7\ntree %s\ngfx950 %d %d 2 16\n" % (lib.bi_gemm_tree_id().decode(), n, k))
     assert lib.bi_gemm_load_pins(str(table).encode()) == 0
     try:
         w = synth.normal_bf16(220, (e, n, k), 0.02)
@@ -131,8 +131,8 @@ def test_grouped_big_blocks_use_the_dense_split_tree(gpu, tmp_path):
 
     e, n, k = 8, 256, 1024
     table = tmp_path / "pins.txt"
-    table.write_text("version 7\ngfx950 %d %d 2 16\n" % (n, k))
     lib = bg.load()
+    table.write_text("version 7\ntree %s\ngfx950 %d %d 2 16\n" % (lib.bi_gemm_tree_id().decode(), n, k))
     assert lib.bi_gemm_load_pins(str(table).encode()) == 0
     try:
         w = synth.normal_bf16(222, (e, n, k), 0.02)

@@ -54,6 +54,19 @@ def test_cost_and_choose():
     assert s2 == 2
 
 
+def test_pick_kernels_keeps_near_ties():
+    times = {1: {"stream_mb1": 10.0, "tiled_64x64": 9.9},   # within 3%: first seen order decides
+             2: {"stream_mb1": 10.1, "tiled_64x64": 10.0},  # previous kind within 3%: kept
+             3: {"stream_mb1": 12.0, "tiled_64x64": 10.0},  # previous kind 20% slower: switch
+             4: {"stream_mb1": 9.0, "tiled_64x64": 10.0}}   # tiled within... no: 11% slower, switch back
+    got = tuner.pick_kernels(times, ("stream_mb1", "tiled_64x64"))
+    assert got[1] == ("tiled_64x64", 9.9)
+    assert got[2][0] == "tiled_64x64" and got[3][0] == "tiled_64x64" and got[4][0] == "stream_mb1"
+    # exact ties go to the earlier kind
+    assert tuner.pick_kernels({5: {"tiled_64x64": 1.0, "stream_mb1": 1.0}},
+                              ("stream_mb1", "tiled_64x64"))[5][0] == "stream_mb1"
+
+
 def test_tiling_from_choice():
     choice = {1: "stream_mb1", 16: "stream_mb1", 64: "stream_mb4", 256: "tiled_64x64", 4096: "tiled4_256x256",
               8192: "tiled4_256x256"}
