@@ -698,9 +698,9 @@ def run_norm_gate_up(args, bg):
     t1.record()
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
-    norm_us = {m: 1e3 * float(np.mean([ev[s_][j][0].elapsed_time(ev[s_][j][1]) for s_ in range(args.steps)]))
+    norm_us = {m: 1e3 * float(np.median([ev[s_][j][0].elapsed_time(ev[s_][j][1]) for s_ in range(args.steps)]))
                for j, m in enumerate(ms)}
-    gemm_us = {m: 1e3 * float(np.mean([ev[s_][j][1].elapsed_time(ev[s_][j][2]) for s_ in range(args.steps)]))
+    gemm_us = {m: 1e3 * float(np.median([ev[s_][j][1].elapsed_time(ev[s_][j][2]) for s_ in range(args.steps)]))
                for j, m in enumerate(ms)}
     flops = {m: 2.0 * m * n * k for m in ms}
     norm_bytes = {m: 4.0 * m * k + 2.0 * k for m in ms}
@@ -719,6 +719,43 @@ def run_norm_gate_up(args, bg):
     roof.update({"traffic": None, "kernel": dom, "launches_per_step": launches, "avg_launch_us": us / launches})
     norm_total_us = sum(norm_us.values())
     norm_roof = _roof(0.0, sum(norm_bytes.values()), norm_total_us)
+
+    # A/B: the norm fused into the GEMM's prologue (bi_rmsnorm_gemm_run: an
+    # r-per-row pass, then the GEMM normalising its x tiles in LDS), same
+    # inputs and weight rotation, events around each call
+    rstd = torch.empty(mmax, dtype=torch.float32, device="cuda:0")
+
+    def fused_step(events=None):
+        for j, m in enumerate(ms):
+            h = hps[call_no[0] % copies]
+            call_no[0] += 1
+            if events is not None:
+                events[j][0].record()
+            st = lib.bi_rmsnorm_gemm_run(h, P(xraw), P(gain), ctypes.c_float(1e-5), m, P(rstd), P(ys[m]), stream)
+            if st != 0:
+                bg.check(st)
+            if events is not None:
+                events[j][1].record()
+
+    for _ in range(args.warmup):
+        fused_step()
+    torch.cuda.synchronize()
+    fev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in ms] for _ in range(args.steps)]
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for s_ in range(args.steps):
+        fused_step(fev[s_])
+    f1.record()
+    torch.cuda.synchronize()
+    fused_ms_per_step = f0.elapsed_time(f1) / args.steps
+    fused_us = {m: 1e3 * float(np.median([fev[s_][j][0].elapsed_time(fev[s_][j][1]) for s_ in range(args.steps)]))
+                for j, m in enumerate(ms)}
+    fused_ab = {"what": "norm fused into the GEMM prologue (r-per-row pass, then the GEMM normalising its x tiles "
+                        "in LDS) against bi_rmsnorm then bi_gemm_run; bit-identical outputs",
+                "separate_ms_per_step": round(ms_per_step, 4), "fused_ms_per_step": round(fused_ms_per_step, 4),
+                "per_m": [{"M": m, "separate_us": round(norm_us[m] + gemm_us[m], 2), "fused_us": round(fused_us[m], 2),
+                           "fused_gemm_kernel": handles[0].rmsnorm_kernel_name(m), "separate_gemm_kernel": names[m]}
+                          for m in ms]}
     per = [{"M": m, "norm_us": round(norm_us[m], 2), "norm_gbs": round(norm_bytes[m] / (norm_us[m] * 1e-6) / 1e9, 0),
             "gemm_us": round(gemm_us[m], 2), "gemm_kernel": names[m],
             "gemm_tflops": round(flops[m] / (gemm_us[m] * 1e-6) / 1e12, 1)} for m in ms]
@@ -740,6 +777,7 @@ def run_norm_gate_up(args, bg):
                    "m_sweep": ms, "weight_copies_rotated": copies, "kernel_source_sha256_16": kernel_hash()},
         "roofline": roof,
         "norm_roofline": dict(norm_roof, kernel="rmsnorm_rows", share_of_step=round(norm_total_us / (ms_per_step * 1e3), 4)),
+        "fused_norm_ab": fused_ab,
         "cpu_baseline": None,
         "per_m": per,
     }

@@ -44,6 +44,35 @@ extern "C" {
  */
 bi_status_t bi_rmsnorm(const void *x, const void *gain, int T, int H, float eps, void *y, void *stream);
 
+/*
+ * The RMSNorm fused into the prologue of the projection that follows it
+ * (the gate+up projection of a Llama block): y = bf16(RMSNorm(x) * gain) W^T
+ * for the M raw rows of x, bit for bit what bi_rmsnorm into a bf16 buffer
+ * followed by bi_gemm_run on it gives, without that buffer.  A row pass
+ * writes each row's r = 1 / sqrt(mean(x^2) + eps) (the tree above) to rstd;
+ * the GEMM then loads the raw rows into LDS and rewrites each stage's x tile
+ * in place as bf16((x * r) * g), the rounding bi_rmsnorm uses, before its
+ * MFMAs read it.  The pages measure a separate batch-invariant norm against
+ * stock kernels (CoRun, §II Fig. 2a; LLM-42 notes, §2.3 Fig. 4b).
+ *   h: dense handle of a layer [N, K]; H = K (8 <= K <= 65536).
+ *   x: bf16 [M, K] raw rows; gain: bf16 [K]; both 16-byte aligned.
+ *   rstd: fp32 [M] out, 4-byte aligned (the rows' r; also what a backward
+ *         pass of the norm keeps).
+ *   y: fp32 [M, N] out, 16-byte aligned; must not overlap x or rstd.
+ *   eps: finite, >= 0.  M: 0 <= M, M * max(N, K) < 2^31; M == 0 launches
+ *   nothing.
+ * The GEMM runs the handle's tree; where the handle's tiling names a
+ * streaming or four-wave kernel, the tiled kernel that normalises its tiles
+ * runs instead (64x32, or 128x128 with eight waves): same tree, other speed.
+ * Asynchronous and allocation-free like bi_gemm_run.
+ */
+bi_status_t bi_rmsnorm_gemm_run(bi_gemm_t h, const void *x, const void *gain, float eps, int M, float *rstd,
+                                float *y, void *stream);
+
+/* The GEMM kernel bi_rmsnorm_gemm_run launches for M rows ("" for an
+ * invalid handle or M <= 0). */
+const char *bi_rmsnorm_gemm_kernel_name(bi_gemm_t h, int M);
+
 #ifdef __cplusplus
 }
 #endif

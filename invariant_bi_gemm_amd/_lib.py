@@ -103,6 +103,8 @@ def _declare(lib):
         "bi_moe_run": ([P, P, I, P, P], S),
         "bi_moe_destroy": ([P], None),
         "bi_rmsnorm": ([P, P, I, I, ctypes.c_float, P, P], S),
+        "bi_rmsnorm_gemm_run": ([P, P, P, ctypes.c_float, I, P, P, P], S),
+        "bi_rmsnorm_gemm_kernel_name": ([P, I], ctypes.c_char_p),
         "bi_attn_create": ([I, I, I, I, I, I, ctypes.POINTER(P)], S),
         "bi_attn_decode": ([P, P, P, P, P, I, I, ctypes.c_float, P, P], S),
         "bi_attn_destroy": ([P], None),
@@ -248,6 +250,37 @@ class Gemm:
                                            ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0),
                                            _stream_ptr(stream)))
         return out
+
+    def rmsnorm_run(self, x, gain, eps, out=None, rstd=None, stream=None):
+        """``RMSNorm(x) * gain @ W.T`` with the norm in the GEMM's prologue
+        (bi_rmsnorm_gemm_run): x raw bf16 [M, K], gain bf16 [K].  Returns
+        (y, rstd)."""
+        import torch
+
+        _need(x, torch.bfloat16, 2, "x")
+        _need(gain, torch.bfloat16, 1, "gain")
+        if x.shape[1] != self.k or gain.shape[0] != self.k:
+            raise ValueError("x and gain must have K=%d" % self.k)
+        m = int(x.shape[0])
+        if out is None:
+            out = torch.empty((m, self.n), dtype=torch.float32, device=x.device)
+        else:
+            _need(out, torch.float32, 2, "out")
+            if tuple(out.shape) != (m, self.n):
+                raise ValueError("out must be [%d, %d]" % (m, self.n))
+        if rstd is None:
+            rstd = torch.empty(m, dtype=torch.float32, device=x.device)
+        else:
+            _need(rstd, torch.float32, 1, "rstd")
+            if rstd.shape[0] != m:
+                raise ValueError("rstd must hold M values")
+        check(self._lib.bi_rmsnorm_gemm_run(self._h, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(gain.data_ptr()),
+                                            ctypes.c_float(eps), m, ctypes.c_void_p(rstd.data_ptr()),
+                                            ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)))
+        return out, rstd
+
+    def rmsnorm_kernel_name(self, m: int) -> str:
+        return self._lib.bi_rmsnorm_gemm_kernel_name(self._h, int(m)).decode()
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:

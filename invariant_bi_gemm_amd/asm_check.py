@@ -23,10 +23,10 @@ SRC = os.path.join(build.CSRC, "bigemm_kernels.hip")
 # comparison path's split-K instance) and the grouped one (plain and indexed
 # rows; both block heights in one kernel), with the accumulator tiles each of
 # their epilogues reads
-KERNELS = {"_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi8ELb0E": [64],
-           "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi4ELb0E": [32],
-           "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi8ELb1E": [64],
-           "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi4ELb1E": [32],
+KERNELS = {"_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi8ELi0E": [64],
+           "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi4ELi0E": [32],
+           "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi8ELi1E": [64],
+           "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi4ELi1E": [32],
            "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb0E": [64, 32],
            "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1E": [64, 32]}
 MFMA_AGPR = re.compile(r"v_mfma_f32_16x16x32_bf16 a\[\d+:\d+\], v\[\d+:\d+\], v\[\d+:\d+\], (a\[\d+:\d+\]|0)$")

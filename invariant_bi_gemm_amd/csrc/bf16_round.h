@@ -18,4 +18,26 @@ __device__ __forceinline__ uint16_t to_bf16(float f)
 // bf16 bits -> fp32, exactly.
 __device__ __forceinline__ float from_bf16(uint32_t b) { return __uint_as_float(b << 16); }
 
+// The RMSNorm scaling of two packed bf16 values: bf16((x * r) * g) for the
+// pair in x2 with the gain pair in g2, both products rounded in fp32 (two
+// separate multiplies), each result rounded to bf16 to nearest even by one
+// v_cvt_pk_bf16_f32; low value in the low half.  The standalone RMSNorm and
+// the GEMM that normalises its x tiles both call this, so their bf16 inputs
+// to the projection are the same bits.
+__device__ __forceinline__ uint32_t rms_scale_pair(uint32_t x2, float r, uint32_t g2)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    f32x2 v;
+    v.x = (__uint_as_float(x2 << 16) * r) * __uint_as_float(g2 << 16);
+    v.y = (__uint_as_float(x2 & 0xffff0000u) * r) * __uint_as_float(g2 & 0xffff0000u);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ uint4 rms_scale_chunk(const uint4& x, float r, const uint4& g)
+{
+    return uint4{rms_scale_pair(x.x, r, g.x), rms_scale_pair(x.y, r, g.y), rms_scale_pair(x.z, r, g.z),
+                 rms_scale_pair(x.w, r, g.w)};
+}
+
 }  // namespace bi

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cerrno>
+#include <cmath>
 #include <climits>
 #include <cstdio>
 #include <cstdlib>
@@ -21,6 +22,8 @@
 #include <vector>
 
 #include "../../include/bi_gemm_ref.h"
+#include "../../include/bi_norm.h"
+#include "norm_internal.h"
 #include "bigemm_internal.h"
 
 namespace {
@@ -643,6 +646,56 @@ bi_status_t bi_gemm_run_splitk(bi_gemm_t hh, const void* x, int M, float* y, int
     if (e != hipSuccess)
         return fail(BI_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return BI_OK;
+}
+
+bi_status_t bi_rmsnorm_gemm_run(bi_gemm_t hh, const void* x, const void* gain, float eps, int M, float* rstd,
+                                float* y, void* stream)
+{
+    bi_gemm* h = handle_of(hh);
+    if (!h)
+        return fail(BI_ERR_INVALID_ARGUMENT, "invalid handle");
+    if (h->plan.experts != 0)
+        return fail(BI_ERR_INVALID_ARGUMENT, "grouped handle passed to bi_rmsnorm_gemm_run");
+    if (h->plan.k > 65536)
+        return fail(BI_ERR_INVALID_ARGUMENT, "the normalised width K must be at most 65536");
+    if (!std::isfinite(eps) || eps < 0.f)
+        return fail(BI_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    if (M < 0)
+        return fail(BI_ERR_INVALID_ARGUMENT, "M must be >= 0");
+    if (M == 0)
+        return BI_OK;
+    if (!x || !gain || !rstd || !y)
+        return fail(BI_ERR_INVALID_ARGUMENT, "x, gain, rstd or y is NULL");
+    if (!aligned16(x) || !aligned16(gain) || !aligned16(y) || (reinterpret_cast<uintptr_t>(rstd) & 3u) != 0)
+        return fail(BI_ERR_MISALIGNED, "x, gain and y must be 16-byte aligned, rstd 4-byte aligned");
+    const long long wide = h->plan.n > h->plan.k ? h->plan.n : h->plan.k;
+    if ((long long)M * wide >= (1LL << 31))
+        return fail(BI_ERR_INVALID_ARGUMENT, "M*max(N,K) must be below 2^31");
+    const char* yb = reinterpret_cast<const char*>(y);
+    const char* xb = static_cast<const char*>(x);
+    const char* rb = reinterpret_cast<const char*>(rstd);
+    const size_t ybytes = (size_t)M * h->plan.n * 4, xbytes = (size_t)M * h->plan.k * 2, rbytes = (size_t)M * 4;
+    if ((xb < yb + ybytes && yb < xb + xbytes) || (rb < yb + ybytes && yb < rb + rbytes) ||
+        (rb < xb + xbytes && xb < rb + rbytes))
+        return fail(BI_ERR_INVALID_ARGUMENT, "y, x and rstd must not overlap");
+    bi_status_t st = check_run_device(h);
+    if (st != BI_OK)
+        return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = binorm::launch_rstd(x, M, h->plan.k, eps, rstd, s);
+    if (e == hipSuccess)
+        e = bigemm::launch_dense_norm(h->plan, h->W, x, rstd, gain, M, y, s);
+    if (e != hipSuccess)
+        return fail(BI_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return BI_OK;
+}
+
+const char* bi_rmsnorm_gemm_kernel_name(bi_gemm_t hh, int M)
+{
+    bi_gemm* h = handle_of(hh);
+    if (!h || M <= 0 || h->plan.experts != 0)
+        return "";
+    return bigemm::dense_norm_kernel_name(h->plan, M);
 }
 
 namespace {

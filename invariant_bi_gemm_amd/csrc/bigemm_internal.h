@@ -76,6 +76,12 @@ hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, floa
 // partials of splits 1.. in part ([splits-1][M][N] fp32), then added to y.
 hipError_t launch_splitk(const Plan& p, int kind, int splits, const void* W, const void* x, int M, float* y,
                          float* part, hipStream_t stream);
+// y = RMSNorm(x) W^T with the norm applied to the x tiles in LDS: rstd
+// [M] fp32 from the RMSNorm row pass, gain bf16 [K]; the kernel a call with
+// M rows runs (a tiled kind; see norm_kind).
+hipError_t launch_dense_norm(const Plan& p, const void* W, const void* x, const float* rstd, const void* gain,
+                             int M, float* y, hipStream_t stream);
+const char* dense_norm_kernel_name(const Plan& p, int M);
 // xidx (optional): row i of the grouped x is row xidx[i] of x (xn rows).
 hipError_t launch_grouped(const Plan& p, const void* W, const void* x,
                           const int32_t* offsets, int R, float* y, const int32_t* xidx, int xn,

@@ -33,6 +33,7 @@
 
 #include <type_traits>
 
+#include "bf16_round.h"
 #include "bigemm_internal.h"
 
 namespace bigemm {
@@ -147,16 +148,21 @@ __device__ __forceinline__ void emit4(float* p, const f32x4& v, int fold)
 }
 
 // Concurrent split-K for the non-invariant comparison path only
-// (bi_gemm_run_splitk): the kernels instantiated with kCmp = true run split
+// (bi_gemm_run_splitk): the kernels instantiated with kMode == kCmp run split
 // blockIdx.y of gridDim.y, each a chain over its own K range from +0; split 0
 // stores into y and split s > 0 into partial s - 1 of `part` ([splits-1][M][N]),
 // which splitk_reduce adds to y afterwards.  Where the splits fall follows
 // the caller's choice per M, so rows are not batch-invariant there.  The
-// product kernels are the kCmp = false instances and never take this path.
-template <bool kCmp>
+// product kernels are other instances and never take this path.
+// What a dense kernel instance does: the product GEMM, the comparison
+// path's concurrent split-K, or the product GEMM of RMSNorm'd rows (x raw,
+// normalised in LDS before the MFMAs).
+enum Mode { kPlain = 0, kCmp = 1, kNormX = 2 };
+
+template <int kMode>
 __device__ __forceinline__ float* cmp_split(Split& sp, float* y, float* part, int M, int N)
 {
-    if constexpr (kCmp) {
+    if constexpr (kMode == kCmp) {
         sp.k0 = (int)blockIdx.y * sp.klen;
         sp.fold = 0;
         if (blockIdx.y > 0)
@@ -349,12 +355,21 @@ struct TiledCfg {
 // With kIdx, row i of the logical x is row xidx[i] of the stored x (xn rows;
 // an index outside 0..xn-1 is clamped into it): the MoE layer's gather of
 // token rows into expert order, done by the loads themselves.
-template <int BM, int BN, int WM, int WN, int BK, int NS, bool kIdx = false>
+//
+// With kNorm, x holds raw rows and the block multiplies the RMSNorm of them:
+// before any fragment read of a stage, its x tile is rewritten in LDS as
+// bf16((x * r) * g) (bi::rms_scale_chunk, the standalone RMSNorm's rounding),
+// r = rstd[row] and g the gain of the stage's k range.  Each thread rewrites
+// one row's chunks, the same logical chunks in every wave, so the gain
+// arrives through scalar loads.
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool kIdx = false, bool kNorm = false>
 __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ Wb,
                                             float* __restrict__ y, int m0, int row_hi, int n0,
                                             int N, int K, Split sp,
-                                            const int32_t* __restrict__ xidx = nullptr, int xn = 0)
+                                            const int32_t* __restrict__ xidx = nullptr, int xn = 0,
+                                            const float* __restrict__ rstd = nullptr,
+                                            const uint4* __restrict__ gain = nullptr)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     constexpr int kCh = C::kCh;
@@ -362,6 +377,11 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave % WM;
     const int wn = wave / WM;
+    static_assert(!kNorm || (C::kThreads % BM == 0 && (8 * BM) % C::kThreads == 0), "normalising split");
+    static_assert(!kNorm || NS >= 3, "the norm rewrites a stage two ahead of the one being read");
+    constexpr int kNC = kNorm ? 8 * BM / C::kThreads : 0;  // chunks of a row per thread
+    const int nrow = threadIdx.x % BM;
+    const int nc0 = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / BM) * kNC);
     const uint32_t rowb = (uint32_t)K * 2;
 
     const int wrows = min(BN, N - n0);
@@ -443,13 +463,41 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
     constexpr int kHalf = C::FN / 2 > 0 ? C::FN / 2 : 1;
 
     const int nk = sp.klen / BK;
+    float nr = 0.f;
+    if constexpr (kNorm)
+        nr = rstd[m0 + min(nrow, xrows - 1)];
+    // the x tile of stage s in place, as the model's normalised rows
+    auto normalize = [&](int s) {
+        if constexpr (kNorm) {
+            uint4* sX = lds + (s % NS) * C::kStageUnits + BN * kCh;
+            const uint4* g = gain + (sp.k0 + s * BK) / 8;
+#pragma unroll
+            for (int c = 0; c < kNC; ++c) {
+                const int cc = nc0 + c;
+                uint4* q = sX + nrow * kCh + swz<kCh>(nrow, cc);
+                *q = bi::rms_scale_chunk(*q, nr, g[cc]);
+            }
+        }
+    };
     // Stage s lives in buffer s % NS.  All NS buffers are filled up front;
-    // stage s + NS is issued once every wave has read stage s.
+    // stage s + NS is issued once every wave has read stage s.  With kNorm
+    // the x tile of stage s + 2 is rewritten while stage s + 1 is read, so
+    // its latency stays off the path from the barrier to the MFMAs: the
+    // barrier after stage s then also waits for stage s + 2 to land.
 #pragma unroll
     for (int q = 0; q < NS; ++q)
         issue(min(q, nk - 1), q);
-    wait_vmcnt<C::kInstr * (NS - 1)>();  // stage 0 has landed
-    barrier_after_lds_reads();
+    if constexpr (kNorm) {
+        wait_vmcnt<C::kInstr * (NS - 2)>();  // stages 0 and 1 have landed
+        barrier_after_lds_reads();
+        normalize(0);
+        if (nk > 1)
+            normalize(1);
+        barrier_after_lds_reads();  // stages 0 and 1 rewritten by every wave
+    } else {
+        wait_vmcnt<C::kInstr * (NS - 1)>();  // stage 0 has landed
+        barrier_after_lds_reads();
+    }
     read_frags(0, 0, fa0, fb0);
 
     // k-step ks of stage s, which has a successor step; branch free so the
@@ -463,10 +511,18 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
         constexpr int ks = decltype(ksc)::value;
         mfmas(fa, fb, 0, kHalf);
         if constexpr (ks + 1 == C::kSteps) {
-            wait_vmcnt<C::kInstr * (NS - 2)>();  // this wave's loads of stage s+1 have landed
+            if constexpr (kNorm)
+                wait_vmcnt<C::kInstr * (NS - 3)>();  // this wave's loads of stage s+2 have landed
+            else
+                wait_vmcnt<C::kInstr * (NS - 2)>();  // this wave's loads of stage s+1 have landed
             barrier_after_lds_reads();           // every wave's have; all have read stage s
             issue(min(s + NS, nk - 1), s % NS);
             read_frags(s + 1, 0, na, nb);
+            if constexpr (kNorm) {
+                // stage s+2 is read after the next barrier, which orders these writes
+                if (s + 2 < nk)
+                    normalize(s + 2);
+            }
         } else {
             read_frags(s, ks + 1, na, nb);
         }
@@ -531,18 +587,19 @@ __device__ __forceinline__ void tile_of_block(int b, int nblocks, int tiles_m, i
     *tn = r / rows;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, bool kCmp = false>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int kMode = kPlain>
 __global__ void __launch_bounds__(WM * WN * 64)
     bigemm_tiled(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                  float* __restrict__ y, int M, int N, int K, Split sp, int tiles_m, int tiles_n,
-                 int group_m, float* part)
+                 int group_m, float* part, const float* __restrict__ rstd, const uint4* __restrict__ gain)
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     __shared__ uint4 lds[NS * C::kStageUnits];
-    y = cmp_split<kCmp>(sp, y, part, M, N);
+    y = cmp_split<kMode>(sp, y, part, M, N);
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
-    tiled_block<BM, BN, WM, WN, BK, NS>(lds, x, W, y, tm * BM, M, tn * BN, N, K, sp);
+    tiled_block<BM, BN, WM, WN, BK, NS, false, kMode == kNormX>(lds, x, W, y, tm * BM, M, tn * BN, N, K, sp,
+                                                               nullptr, 0, rstd, gain);
 }
 
 // ---------------------------------------------------------------------------
@@ -778,13 +835,13 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
 }
 
 // (32 XT) x 256 output blocks, one per workgroup.
-template <int XT, bool kCmp = false>
+template <int XT, int kMode = kPlain>
 __global__ void __launch_bounds__(256)
     bigemm_tiled4(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ y, int M,
                    int N, int K, Split sp, int tiles_m, int tiles_n, int group_m, float* part)
 {
     __shared__ uint4 lds[3 * 256 * 8 + 2 * 32 * XT * 8];
-    y = cmp_split<kCmp>(sp, y, part, M, N);
+    y = cmp_split<kMode>(sp, y, part, M, N);
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
     tiled4_block<XT>(lds, x, W, y, tm * 32 * XT, M, tn * 256, N, K, sp);
@@ -1075,14 +1132,14 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
     }
 }
 
-template <int MB, int XR, int BKS, int NP, bool kCmp = false>
+template <int MB, int XR, int BKS, int NP, int kMode = kPlain>
 __global__ void __launch_bounds__((MB + NP) * 64)
     bigemm_stream(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                   float* __restrict__ y, int M, int N, int K, Split sp, float* part)
 {
     using C = StreamCfg<MB, XR, BKS, NP>;
     __shared__ uint4 ring[C::NR * C::kStageUnits];
-    y = cmp_split<kCmp>(sp, y, part, M, N);
+    y = cmp_split<kMode>(sp, y, part, M, N);
     const int tiles_n = N / 16;
     const int mblocks = (M + 16 * MB - 1) / (16 * MB);
     stream_body<MB, XR, BKS, NP>(ring, x, W, y, N, K, sp, tiles_n, mblocks * tiles_n, M, nullptr, nullptr);
@@ -1120,35 +1177,56 @@ __global__ void __launch_bounds__((MB + NP) * 64)
 // ---------------------------------------------------------------------------
 // ysplits > 1 (comparison path only): the kCmp instance over a grid of
 // ysplits concurrent K splits, partials of splits 1.. into `part`.
+// Extra inputs of a launch beyond the product GEMM's: ysplits > 1 and part
+// (comparison path only) run the kCmp instance over a grid of ysplits
+// concurrent K splits, partials of splits 1.. into part; rstd and gain
+// (RMSNorm'd rows) run the kNormX instance.
+struct LaunchExtra {
+    int ysplits = 1;
+    float* part = nullptr;
+    const float* rstd = nullptr;
+    const void* gain = nullptr;
+};
+
 template <int BM, int BN, int WM, int WN, int BK, int NS>
 hipError_t run_tiled(const void* W, const void* x, int M, float* y, int N, int K, Split sp,
-                     hipStream_t stream, int ysplits = 1, float* part = nullptr)
+                     hipStream_t stream, const LaunchExtra& ex = LaunchExtra())
 {
     using C = TiledCfg<BM, BN, WM, WN, BK, NS>;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int nblocks = tiles_m * tiles_n;
-    if (ysplits > 1)
-        hipLaunchKernelGGL((bigemm_tiled<BM, BN, WM, WN, BK, NS, true>), dim3(nblocks, ysplits), dim3(C::kThreads),
-                           0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
-                           y, M, N, K, sp, tiles_m, tiles_n, 4, part);
-    else
-        hipLaunchKernelGGL((bigemm_tiled<BM, BN, WM, WN, BK, NS>), dim3(nblocks), dim3(C::kThreads),
-                           0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
-                           y, M, N, K, sp, tiles_m, tiles_n, 4, nullptr);
+    const uint16_t* xx = static_cast<const uint16_t*>(x);
+    const uint16_t* ww = static_cast<const uint16_t*>(W);
+    const uint4* g = static_cast<const uint4*>(ex.gain);
+    if (ex.ysplits > 1)
+        hipLaunchKernelGGL((bigemm_tiled<BM, BN, WM, WN, BK, NS, kCmp>), dim3(nblocks, ex.ysplits),
+                           dim3(C::kThreads), 0, stream, xx, ww, y, M, N, K, sp, tiles_m, tiles_n, 4, ex.part,
+                           nullptr, nullptr);
+    else if (ex.rstd) {
+        if constexpr (NS >= 3)
+            hipLaunchKernelGGL((bigemm_tiled<BM, BN, WM, WN, BK, NS, kNormX>), dim3(nblocks), dim3(C::kThreads), 0,
+                               stream, xx, ww, y, M, N, K, sp, tiles_m, tiles_n, 4, nullptr, ex.rstd, g);
+        else
+            return hipErrorInvalidValue;  // too shallow to normalise its tiles
+    } else
+        hipLaunchKernelGGL((bigemm_tiled<BM, BN, WM, WN, BK, NS>), dim3(nblocks), dim3(C::kThreads), 0, stream, xx,
+                           ww, y, M, N, K, sp, tiles_m, tiles_n, 4, nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 
 template <int XT>
 hipError_t run_tiled4(const void* W, const void* x, int M, float* y, int N, int K, Split sp, hipStream_t stream,
-                      int ysplits = 1, float* part = nullptr)
+                      const LaunchExtra& ex = LaunchExtra())
 {
     const int tiles_m = (M + 32 * XT - 1) / (32 * XT);
     const int tiles_n = (N + 255) / 256;
-    if (ysplits > 1)
-        hipLaunchKernelGGL((bigemm_tiled4<XT, true>), dim3(tiles_m * tiles_n, ysplits), dim3(256), 0, stream,
+    if (ex.rstd)
+        return hipErrorInvalidValue;  // no normalising instance of this kernel
+    if (ex.ysplits > 1)
+        hipLaunchKernelGGL((bigemm_tiled4<XT, kCmp>), dim3(tiles_m * tiles_n, ex.ysplits), dim3(256), 0, stream,
                            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K, sp,
-                           tiles_m, tiles_n, 4, part);
+                           tiles_m, tiles_n, 4, ex.part);
     else
         hipLaunchKernelGGL(bigemm_tiled4<XT>, dim3(tiles_m * tiles_n), dim3(256), 0, stream,
                            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K, sp,
@@ -1158,15 +1236,17 @@ hipError_t run_tiled4(const void* W, const void* x, int M, float* y, int N, int 
 
 template <int MB, int XR, int BKS, int NP>
 hipError_t run_stream(const void* W, const void* x, int M, float* y, int N, int K, Split sp,
-                      int num_cus, hipStream_t stream, int ysplits = 1, float* part = nullptr)
+                      int num_cus, hipStream_t stream, const LaunchExtra& ex = LaunchExtra())
 {
     using C = StreamCfg<MB, XR, BKS, NP>;
     const int items = ((M + 16 * MB - 1) / (16 * MB)) * (N / 16);
     const int grid = items < num_cus ? items : num_cus;
-    if (ysplits > 1)
-        hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP, true>), dim3(grid, ysplits), dim3(C::kThreads), 0,
+    if (ex.rstd)
+        return hipErrorInvalidValue;  // no normalising instance of this kernel
+    if (ex.ysplits > 1)
+        hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP, kCmp>), dim3(grid, ex.ysplits), dim3(C::kThreads), 0,
                            stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K,
-                           sp, part);
+                           sp, ex.part);
     else
         hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP>), dim3(grid), dim3(C::kThreads), 0, stream,
                            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K, sp,
@@ -1179,21 +1259,19 @@ hipError_t run_stream(const void* W, const void* x, int M, float* y, int N, int 
 // 64-row load group of that stage width needs.
 template <int MB, int XR>
 hipError_t run_stream_k(const void* W, const void* x, int M, float* y, int N, int K, Split sp,
-                        int num_cus, hipStream_t stream, int ysplits = 1, float* part = nullptr)
+                        int num_cus, hipStream_t stream, const LaunchExtra& ex = LaunchExtra())
 {
     if constexpr (MB == 1) {
         if (sp.klen % 512 == 0)
-            return run_stream<MB, XR, 512, stream_producers<MB, 512>()>(W, x, M, y, N, K, sp, num_cus, stream,
-                                                                        ysplits, part);
+            return run_stream<MB, XR, 512, stream_producers<MB, 512>()>(W, x, M, y, N, K, sp, num_cus, stream, ex);
     }
     if (sp.klen % 256 == 0)
-        return run_stream<MB, XR, 256, stream_producers<MB, 256>()>(W, x, M, y, N, K, sp, num_cus, stream, ysplits,
-                                                                    part);
+        return run_stream<MB, XR, 256, stream_producers<MB, 256>()>(W, x, M, y, N, K, sp, num_cus, stream, ex);
     if (sp.klen % 128 == 0)
         return run_stream<MB, (XR < 4 ? 4 : XR), 128, stream_producers<MB, 128>()>(W, x, M, y, N, K, sp, num_cus,
-                                                                                   stream, ysplits, part);
+                                                                                   stream, ex);
     return run_stream<MB, (XR < 8 ? 8 : XR), 64, stream_producers<MB, 64>()>(W, x, M, y, N, K, sp, num_cus, stream,
-                                                                             ysplits, part);
+                                                                             ex);
 }
 
 // y += part[0] + part[1] + ... (in that order), 4 values per thread and step:
@@ -1381,39 +1459,39 @@ const char* dense_kernel_name(DenseKernel k)
 namespace {
 
 hipError_t launch_dense_split(const Plan& p, DenseKernel kind, const void* W, const void* x, int M,
-                              float* y, Split sp, hipStream_t stream, int ys = 1, float* part = nullptr)
+                              float* y, Split sp, hipStream_t stream, const LaunchExtra& ex = LaunchExtra())
 {
     switch (kind) {
     case DenseKernel::kStream16:
         if (M <= 2)
-            return run_stream_k<1, 2>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ys, part);
+            return run_stream_k<1, 2>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ex);
         if (M <= 4)
-            return run_stream_k<1, 4>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ys, part);
+            return run_stream_k<1, 4>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ex);
         if (M <= 8)
-            return run_stream_k<1, 8>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ys, part);
-        return run_stream_k<1, 16>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ys, part);
+            return run_stream_k<1, 8>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ex);
+        return run_stream_k<1, 16>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ex);
     case DenseKernel::kStream32:
-        return run_stream_k<2, 32>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ys, part);
+        return run_stream_k<2, 32>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ex);
     case DenseKernel::kStream64:
-        return run_stream_k<4, 64>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ys, part);
+        return run_stream_k<4, 64>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ex);
     case DenseKernel::kTiled256:
-        return run_tiled4<8>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
+        return run_tiled4<8>(W, x, M, y, p.n, p.k, sp, stream, ex);
     case DenseKernel::kTiled128x256:
-        return run_tiled4<4>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
+        return run_tiled4<4>(W, x, M, y, p.n, p.k, sp, stream, ex);
     case DenseKernel::kTiled128:
-        return run_tiled<128, 128, 2, 2, 64, 2>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
+        return run_tiled<128, 128, 2, 2, 64, 2>(W, x, M, y, p.n, p.k, sp, stream, ex);
     case DenseKernel::kTiled128x64:
-        return run_tiled<128, 64, 2, 2, 64, 3>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
+        return run_tiled<128, 64, 2, 2, 64, 3>(W, x, M, y, p.n, p.k, sp, stream, ex);
     case DenseKernel::kTiled128x64Deep:
-        return run_tiled<128, 64, 2, 2, 64, 6>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
+        return run_tiled<128, 64, 2, 2, 64, 6>(W, x, M, y, p.n, p.k, sp, stream, ex);
     case DenseKernel::kTiled128Deep:
-        return run_tiled<128, 128, 2, 4, 64, 4>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
+        return run_tiled<128, 128, 2, 4, 64, 4>(W, x, M, y, p.n, p.k, sp, stream, ex);
     case DenseKernel::kTiled64x32:
-        return run_tiled<64, 32, 2, 2, 64, 8>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
+        return run_tiled<64, 32, 2, 2, 64, 8>(W, x, M, y, p.n, p.k, sp, stream, ex);
     case DenseKernel::kTiled64:
         break;
     }
-    return run_tiled<64, 64, 2, 2, 64, 4>(W, x, M, y, p.n, p.k, sp, stream, ys, part);
+    return run_tiled<64, 64, 2, 2, 64, 4>(W, x, M, y, p.n, p.k, sp, stream, ex);
 }
 
 }  // namespace
@@ -1469,11 +1547,52 @@ const char* grouped_kernel_name(const Plan& p, int R)
     return g.big ? "bigemm_tiled4_grouped" : "bigemm_tiled_grouped<128x128>";
 }
 
+// The kernels that can normalise their x tiles: the tiled ones with at
+// least three stages.  A streaming kind of the pin runs as the 64x32 tiled
+// kernel, and the two-stage 128x128 and the four-wave kinds as the deep
+// 128x128 one; every kind realises the same tree, so only the speed differs.
+DenseKernel norm_kind(DenseKernel k)
+{
+    switch (k) {
+    case DenseKernel::kStream16:
+    case DenseKernel::kStream32:
+    case DenseKernel::kStream64:
+        return DenseKernel::kTiled64x32;
+    case DenseKernel::kTiled128:  // two stages: too shallow to rewrite one ahead
+    case DenseKernel::kTiled128x256:
+    case DenseKernel::kTiled256:
+        return DenseKernel::kTiled128Deep;
+    default:
+        return k;
+    }
+}
+
+hipError_t launch_dense_norm(const Plan& p, const void* W, const void* x, const float* rstd, const void* gain,
+                             int M, float* y, hipStream_t stream)
+{
+    const DenseKernel kind = norm_kind(choose_dense(p, M));
+    const int klen = p.k / p.splits;
+    LaunchExtra ex;
+    ex.rstd = rstd;
+    ex.gain = gain;
+    for (int s = 0; s < p.splits; ++s) {
+        const hipError_t e = launch_dense_split(p, kind, W, x, M, y, Split{s * klen, klen, s > 0}, stream, ex);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+const char* dense_norm_kernel_name(const Plan& p, int M) { return dense_kernel_name(norm_kind(choose_dense(p, M))); }
+
 hipError_t launch_splitk(const Plan& p, int kind, int splits, const void* W, const void* x, int M, float* y,
                          float* part, hipStream_t stream)
 {
     const Split sp{0, p.k / splits, 0};
-    hipError_t e = launch_dense_split(p, static_cast<DenseKernel>(kind), W, x, M, y, sp, stream, splits, part);
+    LaunchExtra ex;
+    ex.ysplits = splits;
+    ex.part = part;
+    hipError_t e = launch_dense_split(p, static_cast<DenseKernel>(kind), W, x, M, y, sp, stream, ex);
     if (e != hipSuccess || splits == 1)
         return e;
     const long long n4 = (long long)M * p.n / 4;

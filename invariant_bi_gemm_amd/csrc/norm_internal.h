@@ -8,5 +8,7 @@ namespace binorm {
 
 hipError_t launch_rmsnorm(const void* x, const void* g, int T, int H, float eps, void* y,
                           hipStream_t stream);
+// rstd[t] = the r of row t by the same tree, nothing else written.
+hipError_t launch_rstd(const void* x, int T, int H, float eps, float* rstd, hipStream_t stream);
 
 }  // namespace binorm

@@ -87,21 +87,23 @@ def cost(profile, timing):
     return sum(n * timing[m] for m, n in profile)
 
 
-TIE = 0.03  # kernels within 3% of the fastest count as equally fast
+TIE = 0.03        # kernels within 3% of the fastest count as equally fast,
+TIE_ABS = 0.5e-6  # and so do kernels within half a microsecond (launch jitter)
 
 
-def pick_kernels(times, kinds=KERNEL_KINDS, tie=TIE):
+def pick_kernels(times, kinds=KERNEL_KINDS, tie=TIE, tie_abs=TIE_ABS):
     """{M: {kind: seconds}} -> {M: (kind, seconds)}, ascending in M: the
     fastest kind, except that the kind of the previous M is kept while it is
-    within `tie` of the fastest (timings of equal kernels differ by noise,
-    which would otherwise cut the tiling into many small ranges); ties
-    between new kinds go to the earlier kind."""
+    within `tie` (relative) or `tie_abs` (seconds) of the fastest: timings of
+    equally fast kernels differ by noise, which would otherwise cut the
+    tiling into many small ranges.  Ties between new kinds go to the earlier
+    kind."""
     out, prev = {}, None
     for m in sorted(times):
         cand = [(t, kinds.index(kd), kd) for kd, t in times[m].items() if kd in kernel_candidates(m, kinds)]
         best_t = min(c[0] for c in cand)
         if prev is not None and prev in times[m] and prev in kernel_candidates(m, kinds) and \
-                times[m][prev] <= best_t * (1 + tie):
+                times[m][prev] <= max(best_t * (1 + tie), best_t + tie_abs):
             out[m] = (prev, times[m][prev])
         else:
             t, _, kd = min(cand)
@@ -128,6 +130,12 @@ def choose(profile, measure, splits, kinds=KERNEL_KINDS, tie=TIE):
                 if kd in kernel_candidates(m, kinds):
                     times[m][kd] = t[m]
         per_m = pick_kernels(times, kinds, tie)
+        # a tiling list holds at most MAX_TILINGS ranges: widen the tie until
+        # the picks fit (only noise-level differences are ever merged first)
+        t_ = tie
+        while len(tiling_from_choice({m: v[0] for m, v in per_m.items()}, check=False)) > MAX_TILINGS:
+            t_ *= 2
+            per_m = pick_kernels(times, kinds, t_)
         total = cost(profile, {m: v[1] for m, v in per_m.items()})
         report.append((s, total, per_m))
         if best is None or total < best[1]:
@@ -136,7 +144,7 @@ def choose(profile, measure, splits, kinds=KERNEL_KINDS, tie=TIE):
     return s, {m: v[0] for m, v in per_m.items()}, {m: v[1] for m, v in per_m.items()}, report
 
 
-def tiling_from_choice(choice):
+def tiling_from_choice(choice, check=True):
     """{M: kind} at the profile points -> [(m_max, kind)], the switch between
     neighbouring points at their geometric mean, equal neighbours merged, the
     last bound None (every larger M)."""
@@ -148,7 +156,7 @@ def tiling_from_choice(choice):
             out[-1] = (bound, choice[m])
         else:
             out.append((bound, choice[m]))
-    if len(out) > MAX_TILINGS:
+    if check and len(out) > MAX_TILINGS:
         raise ValueError("the tiling needs %d entries, at most %d fit" % (len(out), MAX_TILINGS))
     return out
 
@@ -235,43 +243,56 @@ def update_table(path: str, arch: str, n: int, k: int, pin, tree: str):
 
 # --- measurement on the device ------------------------------------------------
 
-def device_measure(n: int, k: int, profile, reps: int = 20, rotate_bytes: float = 2 ** 30):
+def device_measure(n: int, k: int, profile, reps: int = 20, rotate_bytes: float = 2 ** 30, batches: int = 3):
     """A `measure(s, kind)` function timing bi_gemm_run with HIP events on
-    cuda:0, the kernel forced by a one-entry tiling list.
+    cuda:0, the kernel forced by a one-entry tiling list: per M, the fastest
+    of `batches` batches of `reps` back-to-back calls (the mean of a batch),
+    the calls made straight through the C ABI with prepared arguments so the
+    host keeps ahead of the GPU.
 
     Weights rotate over copies totalling `rotate_bytes` so that the Infinity
     Cache does not serve them to small-M calls.
     """
+    import ctypes
+
     import torch
 
     from . import _lib
 
-    _lib.load()
+    lib = _lib.load()
     w0 = (torch.randn(n, k, device="cuda:0") * 0.02).to(torch.bfloat16)
     copies = max(1, int(rotate_bytes // (2 * n * k)) + 1)
     ws = [w0] + [w0.clone() for _ in range(copies - 1)]
     mmax = max(m for m, _ in profile)
     x = torch.randn(mmax, k, device="cuda:0").to(torch.bfloat16)
     ys = {m: torch.empty(m, n, device="cuda:0") for m, _ in profile}
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    xp = ctypes.c_void_p(x.data_ptr())
+    run = lib.bi_gemm_run
 
     def measure(s, kind):
         hs = [_lib.Gemm(w, pin={"splits": s, "stream_max_m": 0, "tiling": [(None, kind)]}) for w in ws]
+        hp = [h._h for h in hs]
         out = {}
         for m, _ in profile:
             if kind not in kernel_candidates(m):
                 out[m] = float("inf")
                 continue
+            yp = ctypes.c_void_p(ys[m].data_ptr())
             for i in range(3):
-                hs[i % copies](x[:m], out=ys[m])
+                _lib.check(run(hp[i % copies], xp, m, yp, stream))
             torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for i in range(reps):
-                hs[i % copies](x[:m], out=ys[m])
-            e1.record()
-            torch.cuda.synchronize()
-            out[m] = e0.elapsed_time(e1) * 1e-3 / reps
+            best = float("inf")
+            for _ in range(batches):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(reps):
+                    run(hp[i % copies], xp, m, yp, stream)
+                e1.record()
+                torch.cuda.synchronize()
+                best = min(best, e0.elapsed_time(e1) * 1e-3 / reps)
+            out[m] = best
         for h in hs:
             h.close()
         return out

@@ -52,7 +52,7 @@ def test_all_checks_together(asm):
 
 
 # hand-made assembly: one kernel whose body has the mistake each check is for
-_K = "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi4ELb0E"
+_K = "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi4ELi0E"
 
 
 def _fake(lines, nv=384, acc=128, scratch=0):

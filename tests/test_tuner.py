@@ -67,6 +67,18 @@ def test_pick_kernels_keeps_near_ties():
                               ("stream_mb1", "tiled_64x64"))[5][0] == "stream_mb1"
 
 
+def test_choose_fits_the_tiling_list():
+    """Noise-level timings that alternate between two kinds at 32 profile
+    points still give a tiling list within BI_MAX_TILINGS."""
+    prof = [(m, 1) for m in range(1, 33)]
+
+    def measure(s_, kd):
+        return {m: 10e-6 * (1.0 + (0.04 if (m % 2) == (kd == "tiled_64x64") else 0.0)) for m, _ in prof}
+
+    s, choice, _, _ = tuner.choose(prof, measure, [1], ("stream_mb1", "tiled_64x64"))
+    assert len(tuner.tiling_from_choice(choice)) <= tuner.MAX_TILINGS
+
+
 def test_tiling_from_choice():
     choice = {1: "stream_mb1", 16: "stream_mb1", 64: "stream_mb4", 256: "tiled_64x64", 4096: "tiled4_256x256",
               8192: "tiled4_256x256"}
