@@ -84,6 +84,33 @@ bi_status_t bi_attn_decode(bi_attn_t h, const void *q, const void *k, const void
 /* Release a handle (NULL is ignored). */
 void bi_attn_destroy(bi_attn_t h);
 
+/*
+ * Largest split workspace bi_attn_decode_noalloc serves: 64 MiB, enough for
+ * 256 sequences of up to 4096 keys with 32 query heads and split size 512.
+ */
+#define BI_ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * bi_attn_decode without a handle and without any allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The split partials and
+ * the work list go to a static device array of BI_ATTN_NOALLOC_SCRATCH_BYTES
+ * per GPU instead of a handle's workspace; everything else -- the kernels,
+ * the tree, the output bits -- is exactly bi_attn_create(Hq, Hkv, D, split,
+ * B, max_seq_len) followed by bi_attn_decode.  The argument rules are those
+ * two calls' combined; in addition the partials must fit:
+ * B * Hq * ceil(max_seq_len / split) * (D + 2) * 4 + (B + 1) * 4 <=
+ * BI_ATTN_NOALLOC_SCRATCH_BYTES, else BI_ERR_INVALID_ARGUMENT (before any HIP
+ * call).  The array of a GPU is looked up once (hipGetSymbolAddress) on the
+ * first call on that device and is shared by every call on it: calls that
+ * overlap on one GPU (on different streams, or from several threads) race
+ * and must not be made.  Nothing in it needs to start at zero: each call
+ * writes every partial and plan entry it reads.
+ */
+bi_status_t bi_attn_decode_noalloc(int Hq, int Hkv, int D, int split, int max_seq_len, const void *q,
+                                   const void *k, const void *v, const int32_t *seq_start, int B, int Ntok,
+                                   float scale, float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -108,6 +108,7 @@ def _declare(lib):
         "bi_attn_create": ([I, I, I, I, I, I, ctypes.POINTER(P)], S),
         "bi_attn_decode": ([P, P, P, P, P, I, I, ctypes.c_float, P, P], S),
         "bi_attn_destroy": ([P], None),
+        "bi_attn_decode_noalloc": ([I, I, I, I, I, P, P, P, P, I, I, ctypes.c_float, P, P], S),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
