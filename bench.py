@@ -60,20 +60,40 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from committed rocprof counters, or
-    None when absent or taken on another version of the kernels."""
-    if not os.path.exists(TRAFFIC_FILE):
+CLOCK_FILE = os.path.join(ROOT, "profiles", "clock_llama8b_down_sweep.txt")
+
+
+def read_profile_kv(path: str, kernel: str):
+    """key = value lines of a committed profile summary, or None when absent,
+    for another kernel, or taken on another version of the kernels."""
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if "=" in line and not line.startswith("#"):
             key, val = line.split("=", 1)
             kv[key.strip()] = val.strip()
     if kv.get("kernel_source_sha256_16") != kernel_hash() or kv.get("kernel") != kernel:
         return None
+    return kv
+
+
+def read_clock(kernel: str):
+    """The engine clock the kernel sustains (GHz) from committed rocprof
+    counters: busy cycles (GRBM_GUI_ACTIVE) over the dispatch's duration."""
+    kv = read_profile_kv(CLOCK_FILE, kernel)
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["sustained_clock_ghz"]) if kv else None
+    except (KeyError, ValueError):
+        return None
+
+
+def read_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from committed rocprof counters, or
+    None when absent or taken on another version of the kernels."""
+    kv = read_profile_kv(TRAFFIC_FILE, kernel)
+    try:
+        return float(kv["hbm_bytes_per_launch"]) if kv else None
     except (KeyError, ValueError):
         return None
 
@@ -198,77 +218,6 @@ def invariance_cost(bg, ws, xd, ms, n, k, reps=10):
             "noninvariant_sweep_ms": round(tot_best, 4),
             "hipblaslt_bf16out_sweep_ms": round(tot_blas, 4),
             "per_m": rows}
-
-
-class ClockSampler:
-    """The GPU's graphics clock sampled from a host thread while work runs
-    (amdsmi GPU metrics, read only); `mean_ghz` is None when the metrics are
-    not readable."""
-
-    KEYS = ("current_gfxclk", "average_gfxclk_frequency")
-
-    def __init__(self, period_s=0.002):
-        import threading
-
-        self.samples = []
-        self.source = None
-        self._stop = threading.Event()
-        self._thread = None
-        self._period = period_s
-        try:
-            import amdsmi
-
-            amdsmi.amdsmi_init()
-            self._amdsmi = amdsmi
-            self._h = amdsmi.amdsmi_get_processor_handles()[0]
-            self._read()
-        except Exception as e:  # noqa: BLE001 (metrics are optional)
-            self._amdsmi = None
-            self.error = "%s: %s" % (type(e).__name__, e)
-
-    def _read(self):
-        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
-        for key in self.KEYS:
-            v = m.get(key)
-            if isinstance(v, (list, tuple)):
-                v = [u for u in v if isinstance(u, (int, float)) and 0 < u < 10000]
-                v = sum(v) / len(v) if v else None
-            if isinstance(v, (int, float)) and 0 < v < 10000:
-                self.source = "amdsmi gpu_metrics %s" % key
-                return float(v)
-        return None
-
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                v = self._read()
-                if v:
-                    self.samples.append(v)
-            except Exception:  # noqa: BLE001
-                pass
-            self._stop.wait(self._period)
-
-    def __enter__(self):
-        import threading
-
-        if self._amdsmi is not None:
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self._thread is not None:
-            self._thread.join()
-        if self._amdsmi is not None:
-            try:
-                self._amdsmi.amdsmi_shut_down()
-            except Exception:  # noqa: BLE001
-                pass
-
-    @property
-    def mean_ghz(self):
-        return sum(self.samples) / len(self.samples) / 1000.0 if self.samples else None
 
 
 # MI355X's peak engine clock: the nominal bf16 peak is quoted at it
@@ -1006,12 +955,11 @@ def main(argv=None):
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        t_start.record()
-        for s in range(args.steps):
-            step(ev[s])
-        t_end.record()
-        torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        step(ev[s])
+    t_end.record()
+    torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     # per call: the median over the timed steps of its launch's event pair
     per_call_ms = {m: float(np.median([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
@@ -1044,11 +992,14 @@ def main(argv=None):
     roof["avg_launch_us"] = d["ms"] * 1e3 / d["launches"]
     roof["launch_us_statistic"] = "median over the timed steps, per launch"
     # the MFMA peak scales with the engine clock: the same fraction against
-    # the peak at the clock sampled during the timed region
-    roof["sustained_clock_ghz"] = round(clock.mean_ghz, 3) if clock.mean_ghz else None
-    roof["clock_source"] = clock.source if clock.mean_ghz else getattr(clock, "error", "no samples")
-    if clock.mean_ghz and roof["bound"] == "mfma":
-        peak_at_clock = PEAK_BF16_TFLOPS * clock.mean_ghz / PEAK_CLOCK_GHZ
+    # the peak at the clock the kernel sustains (committed rocprof counters of
+    # the current kernels; null otherwise)
+    clock = read_clock(dom)
+    roof["sustained_clock_ghz"] = clock
+    roof["clock_source"] = ("rocprof GRBM_GUI_ACTIVE / dispatch duration, %s" % os.path.relpath(CLOCK_FILE, ROOT)
+                            if clock else "no current counter profile")
+    if clock and roof["bound"] == "mfma":
+        peak_at_clock = PEAK_BF16_TFLOPS * clock / PEAK_CLOCK_GHZ
         roof["peak_at_sustained_clock"] = round(peak_at_clock, 1)
         roof["frac_at_sustained_clock"] = roof["achieved"] / peak_at_clock
 

@@ -90,8 +90,12 @@ typedef struct bi_pin_info {
     int32_t splits;               /* S: contiguous equal K splits                */
     int32_t split_len;            /* K / S                                       */
     int32_t fold;                 /* 0: in-order left fold in fp32 RNE           */
-    int32_t stream_max_m;         /* tiling: rows at or below which the
-                                     weight-streaming kernel runs                */
+    int32_t stream_max_m;         /* tiling: a grouped call streams the experts
+                                     with at most min(this, 16) rows, unless its
+                                     experts average 64 rows or more (then the
+                                     four-wave kernel takes them all); a dense
+                                     call without a tiling list streams calls
+                                     with at most this many rows                */
     int32_t from_table;           /* 1: pin read from the pin table; 0: default  */
     int32_t table_version;        /* version line of the pin table (0: none)     */
     int32_t tilings;              /* entries used below; 0: the built-in rule

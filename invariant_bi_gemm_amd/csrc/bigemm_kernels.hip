@@ -587,6 +587,30 @@ __device__ __forceinline__ void tile_of_block(int b, int nblocks, int tiles_m, i
     *tn = r / rows;
 }
 
+// Block -> tile for the four-wave kernels: the tile grid is cut into 8
+// rectangles, 4 along m by 2 along n, and XCD x (which hardware hands block
+// b when b % 8 == x) takes rectangle (x % 4, x / 4), walking groups of 4 of
+// its m-blocks column by column.  So each half of the W columns is read by
+// one set of four XCDs (x / 4), and the four XCDs of a set share those W
+// tiles while each keeps its own x rows; with the order of tile_of_block
+// every XCD reads the same W half at once.  Measured on the down-proj: about
+// 3% faster at M = 4096 and 8192.  Grids that do not cut evenly use
+// tile_of_block.
+__device__ __forceinline__ void tile_of_block_rect(int b, int nblocks, int tiles_m, int tiles_n, int* tm, int* tn)
+{
+    if (tiles_m % 4 != 0 || tiles_n % 2 != 0 || nblocks != tiles_m * tiles_n) {
+        tile_of_block(b, nblocks, tiles_m, tiles_n, 4, tm, tn);
+        return;
+    }
+    const int xcd = b % 8, i = b / 8;
+    const int rm = tiles_m / 4, rn = tiles_n / 2;
+    const int gm = rm < 4 ? rm : 4;  // rm is a multiple of gm: 1, 2, 3 or a multiple of 4 ...
+    const int rows = rm % gm == 0 ? gm : 1;  // ... else walk one m-block at a time
+    const int span = rows * rn, g = i / span, r = i % span;
+    *tm = (xcd % 4) * rm + g * rows + r % rows;
+    *tn = (xcd / 4) * rn + r / rows;
+}
+
 template <int BM, int BN, int WM, int WN, int BK, int NS, int kMode = kPlain>
 __global__ void __launch_bounds__(WM * WN * 64)
     bigemm_tiled(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
@@ -843,7 +867,7 @@ __global__ void __launch_bounds__(256)
     __shared__ uint4 lds[3 * 256 * 8 + 2 * 32 * XT * 8];
     y = cmp_split<kMode>(sp, y, part, M, N);
     int tm, tn;
-    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
+    tile_of_block_rect(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
     tiled4_block<XT>(lds, x, W, y, tm * 32 * XT, M, tn * 256, N, K, sp);
 }
 

@@ -139,9 +139,13 @@ def test_indexed_rows_equal_gathered_rows(gpu, experts, tokens):
 @pytest.mark.parametrize("name", list(SHAPES))
 def test_block_boundaries_every_row_equals_dense(gpu, experts, name):
     """Experts on both sides of the 256-row blocks of the four-wave kernel
-    (127 .. 640 rows, a 3000-row one) and of the streaming kernel (1, 16, 17):
+    (127 .. 640 rows, a 3000-row one) and small experts (1, 16, 17 rows):
     rows at every block edge equal the dense rows of their expert, bit
-    for bit, for plain and (up) indexed rows; sampled rows pass the oracle."""
+    for bit, for plain and (up) indexed rows; sampled rows pass the oracle.
+    The call has R = 8501 >= 64 E rows, so the four-wave kernel takes every
+    expert here, the small ones as 128-row blocks (no streaming launch);
+    test_uneven_groups_cross_paths puts streamed experts next to four-wave
+    ones."""
     n, k = SHAPES[name]
     w, wd = experts[name]
     g = gpu.GroupedGemm(wd)
