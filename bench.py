@@ -164,6 +164,79 @@ def _time_calls(fn, reps):
 
 SPLITK_CHOICES = (1, 2, 4, 8)
 
+# A second pin of the down-projection, tuned for a chunked-prefill serving
+# profile (most calls 64..1024 rows) instead of the sweep's one call per M.
+PREFILL_PINS = os.path.join(ROOT, "invariant_bi_gemm_amd", "pins", "gfx950_chunked_prefill.txt")
+PREFILL_PROFILE = "1:4,16:4,64:8,128:16,256:16,512:16,1024:8,2048:2,4096:1,8192:1"
+
+
+def alternative_pin(bg, ws, xd, ms, n, k, steps, warmup, table_ms):
+    """The sweep under the chunked-prefill pin (its own tree and tiling),
+    timed like the headline (events around each launch, median over the
+    steps), and both pins' costs over that profile (Detent eq. 3: sum of
+    count x time) -- the pin follows the workload profile."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import invariant_bi_gemm_amd.tuner as tuner
+
+    if not os.path.exists(PREFILL_PINS):
+        return None
+    _, _, _, rows = tuner.read_table(PREFILL_PINS)
+    if ("gfx950", n, k) not in rows:
+        return None
+    s_, smax, tiling = rows[("gfx950", n, k)]
+    pin = {"splits": s_, "stream_max_m": smax, "tiling": tiling}
+    hs = [bg.Gemm(w, pin=pin) for w in ws]
+    copies = len(hs)
+    lib = bg.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    xp = ctypes.c_void_p(xd.data_ptr())
+    ys = {m: torch.empty((m, n), dtype=torch.float32, device="cuda:0") for m in ms}
+    yps = {m: ctypes.c_void_p(ys[m].data_ptr()) for m in ms}
+    call = [0]
+
+    def step(events=None):
+        for j, m in enumerate(ms):
+            h = hs[call[0] % copies]._h
+            call[0] += 1
+            if events is not None:
+                events[j][0].record()
+            st = lib.bi_gemm_run(h, xp, m, yps[m], stream)
+            if st != 0:
+                bg.check(st)
+            if events is not None:
+                events[j][1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ms]
+          for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step(ev[i])
+    t1.record()
+    torch.cuda.synchronize()
+    per = {m: float(np.median([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)])) for j, m in enumerate(ms)}
+    prof = tuner.parse_profile(PREFILL_PROFILE)
+    cost_alt = sum(c * per[m] for m, c in prof if m in per)
+    cost_tab = sum(c * table_ms[m] for m, c in prof if m in table_ms)
+    out = {"what": "the same sweep under the pin tuned for a chunked-prefill profile (%s): tree of %d splits, "
+                   "tiling %s; events around each launch, median over the steps" % (PREFILL_PROFILE, s_,
+                                                                                  tuner.format_tiling(tiling)),
+           "pins_file": os.path.relpath(PREFILL_PINS, ROOT),
+           "sweep_ms_per_step": round(t0.elapsed_time(t1) / steps, 4),
+           "profile_cost_us": {"sweep_pin": round(cost_tab * 1e3, 1), "chunked_prefill_pin": round(cost_alt * 1e3, 1)},
+           "per_m": [{"M": m, "us": round(per[m] * 1e3, 2), "kernel": hs[0].kernel_name(m),
+                      "sweep_pin_us": round(table_ms[m] * 1e3, 2)} for m in ms]}
+    for h in hs:
+        h.close()
+    return out
+
 
 def invariance_cost(bg, ws, xd, ms, n, k, reps=10):
     """Cost of invariance: the pinned call at each M against the fastest
@@ -1011,8 +1084,11 @@ def main(argv=None):
                       "hbm_gbs": round(hbm_bytes[m] / t / 1e9, 0)})
 
     compare = None
+    alt = None
     if not args.no_compare:
         compare = invariance_cost(bg, ws, xd, ms, n, k)
+        if args.workload == "llama8b_down" and not args.m:
+            alt = alternative_pin(bg, ws, xd, ms, n, k, args.steps, args.warmup, per_call_ms)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -1037,6 +1113,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "per_m": per_m,
         "invariance_cost": compare,
+        "alternative_pin": alt,
         "peak_tflops_in_sweep": max(p["tflops"] for p in per_m),
         "context": "pages' numbers (H100, other hardware): vendor GEMM 527 TFLOPS vs Triton "
                    "batch-invariant 194 TFLOPS peak on this layer",

@@ -34,7 +34,10 @@
  *
  * Threading.  A handle may be used from several host threads for `run` calls
  * on the same or different streams: `run` keeps no per-call state in the
- * handle.  `destroy` must not race with any other call on that handle.
+ * handle -- except a handle whose pin runs splits concurrently
+ * (BI_KERNEL_CONCURRENT_SPLITS, bi_pin_info.split_ws_rows > 0): its calls
+ * share the handle's split workspace and must not overlap.  `destroy` must
+ * not race with any other call on that handle.
  */
 #ifndef BI_GEMM_H
 #define BI_GEMM_H
@@ -81,6 +84,20 @@ typedef enum {
 /* Most entries of a pin's tiling list. */
 #define BI_MAX_TILINGS 12
 
+/*
+ * Flag of a tiling entry (tile_kernel[i] | BI_KERNEL_CONCURRENT_SPLITS; in a
+ * pin table the kind's name followed by "+cs"): when the tree has S > 1
+ * splits, the entry's calls run the S splits concurrently -- S times the
+ * workgroups over the same tiles, each summing its own K range from +0 --
+ * with splits 1..S-1 writing partials into the handle's split workspace and
+ * a final kernel adding them to y in split order, ((p0 + p1) + p2) + ...
+ * That is the tree's in-order fold, so the bits are those of the splits run
+ * one after another.  Only entries with a finite row bound may carry it:
+ * create allocates (S - 1) * bound * N fp32 of workspace for the largest
+ * such bound (a call with more rows runs the splits one after another).
+ */
+#define BI_KERNEL_CONCURRENT_SPLITS 0x100
+
 /* Tree and tiling a handle runs with (introspection for tests and benches). */
 typedef struct bi_pin_info {
     int32_t n, k;                 /* layer shape                                 */
@@ -104,7 +121,11 @@ typedef struct bi_pin_info {
     int32_t tile_m_max[BI_MAX_TILINGS];  /* ascending row bounds: entry i serves
                                      tile_m_max[i-1] < M <= tile_m_max[i]; the
                                      last entry is INT32_MAX (every larger M)   */
-    int32_t tile_kernel[BI_MAX_TILINGS]; /* bi_kernel_kind_t of each entry      */
+    int32_t tile_kernel[BI_MAX_TILINGS]; /* bi_kernel_kind_t of each entry, with
+                                     BI_KERNEL_CONCURRENT_SPLITS where the entry
+                                     runs its splits concurrently               */
+    int32_t split_ws_rows;        /* rows the handle's split workspace holds (0:
+                                     none; concurrent splits need it)            */
 } bi_pin_info;
 
 /*
@@ -134,7 +155,8 @@ const char *bi_gemm_kernel_kind_name(int kind);
  * bi_gemm_tree_id(), then one line per layer shape,
  *   arch N K splits stream_max_m [M:kind,M:kind,...,*:kind]
  * where the optional last field is the tiling list (kinds by their
- * bi_gemm_kernel_kind_name, bounds ascending, the last `*`).
+ * bi_gemm_kernel_kind_name, optionally followed by "+cs" for concurrent
+ * splits on an entry with a finite bound; bounds ascending, the last `*`).
  * Returns BI_OK, BI_ERR_INVALID_ARGUMENT (unreadable file) or
  * BI_ERR_BAD_PIN_TABLE (with the offending line in bi_last_error()).
  */

@@ -40,26 +40,43 @@ KERNEL_KINDS = ("stream_mb1", "stream_mb2", "stream_mb4", "tiled_64x32", "tiled_
                 "tiled_128x64_deep", "tiled_128x128", "tiled_128x128_deep", "tiled4_128x256", "tiled4_256x256")
 
 
+CONCURRENT_SPLITS = 0x100  # BI_KERNEL_CONCURRENT_SPLITS; "+cs" in a kind's name
+
+
+def kind_value(kind) -> int:
+    """A kind name ("tiled_64x64", "tiled_64x64+cs") or value -> its tile_kernel value."""
+    if not isinstance(kind, str):
+        return int(kind)
+    if kind.endswith("+cs"):
+        return KERNEL_KINDS.index(kind[:-3]) | CONCURRENT_SPLITS
+    return KERNEL_KINDS.index(kind)
+
+
+def kind_name(value: int) -> str:
+    return KERNEL_KINDS[value & ~CONCURRENT_SPLITS] + ("+cs" if value & CONCURRENT_SPLITS else "")
+
+
 class BiPinInfo(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "n", "k", "experts", "mfma_m", "mfma_n", "mfma_k", "k_map", "splits", "split_len",
         "fold", "stream_max_m", "from_table", "table_version", "tilings")] + [
-        ("tile_m_max", ctypes.c_int32 * MAX_TILINGS), ("tile_kernel", ctypes.c_int32 * MAX_TILINGS)]
+        ("tile_m_max", ctypes.c_int32 * MAX_TILINGS), ("tile_kernel", ctypes.c_int32 * MAX_TILINGS),
+        ("split_ws_rows", ctypes.c_int32)]
 
     def as_dict(self):
-        d = {name: int(getattr(self, name)) for name, _ in self._fields_[:-2]}
-        d["tiling"] = [(int(self.tile_m_max[i]), KERNEL_KINDS[self.tile_kernel[i]]) for i in range(self.tilings)]
+        d = {name: int(getattr(self, name)) for name, t in self._fields_ if t is ctypes.c_int32}
+        d["tiling"] = [(int(self.tile_m_max[i]), kind_name(self.tile_kernel[i])) for i in range(self.tilings)]
         return d
 
     def set_tiling(self, tiling):
-        """tiling: [(m_max, kind name or index), ...], the last m_max None or
+        """tiling: [(m_max, kind name or value), ...], the last m_max None or
         INT32_MAX (every larger M)."""
         if len(tiling) > MAX_TILINGS:
             raise ValueError("at most %d tiling entries" % MAX_TILINGS)
         self.tilings = len(tiling)
         for i, (m, kind) in enumerate(tiling):
             self.tile_m_max[i] = INT32_MAX if m is None else int(m)
-            self.tile_kernel[i] = KERNEL_KINDS.index(kind) if isinstance(kind, str) else int(kind)
+            self.tile_kernel[i] = kind_value(kind)
 
 
 class BiGemmError(RuntimeError):

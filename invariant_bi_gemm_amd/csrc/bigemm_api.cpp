@@ -99,8 +99,13 @@ bool pin_legal(int N, int K, int splits, int stream_max_m, std::string* why)
     return true;
 }
 
+// Largest row bound of a tiling entry that runs concurrent splits (it sizes
+// the handle's split workspace).
+constexpr int kMaxSplitWsRows = 16384;
+
 // A tiling list is legal when its bounds ascend, are positive, end with
-// INT32_MAX and every kernel is a known kind.
+// INT32_MAX and every kernel is a known kind; concurrent splits only on
+// entries with a bound of at most kMaxSplitWsRows.
 bool tiling_legal(int count, const int* m_max, const int* kernel, std::string* why)
 {
     if (count < 0 || count > BI_MAX_TILINGS) {
@@ -108,8 +113,17 @@ bool tiling_legal(int count, const int* m_max, const int* kernel, std::string* w
         return false;
     }
     for (int i = 0; i < count; ++i) {
-        if (kernel[i] < 0 || kernel[i] >= BI_KERNEL_COUNT) {
+        const int kind = kernel[i] & ~BI_KERNEL_CONCURRENT_SPLITS;
+        if (kind < 0 || kind >= BI_KERNEL_COUNT) {
             *why = "unknown kernel kind " + std::to_string(kernel[i]);
+            return false;
+        }
+        if ((kernel[i] & BI_KERNEL_CONCURRENT_SPLITS) && i == count - 1) {
+            *why = "the entry that covers every larger M cannot run concurrent splits (its workspace would be unbounded)";
+            return false;
+        }
+        if ((kernel[i] & BI_KERNEL_CONCURRENT_SPLITS) && m_max[i] > kMaxSplitWsRows) {
+            *why = "concurrent splits are allowed up to " + std::to_string(kMaxSplitWsRows) + " rows";
             return false;
         }
         if (m_max[i] < 1 || (i > 0 && m_max[i] <= m_max[i - 1])) {
@@ -157,10 +171,16 @@ bool parse_tiling(const char* text, Tiling* t, std::string* why)
             }
             bound = (int)v;
         }
+        std::string base = kind;
+        int flag = 0;
+        if (base.size() > 3 && base.compare(base.size() - 3, 3, "+cs") == 0) {
+            base = base.substr(0, base.size() - 3);
+            flag = BI_KERNEL_CONCURRENT_SPLITS;
+        }
         int k = -1;
         for (int c = 0; c < BI_KERNEL_COUNT; ++c)
-            if (kind == bigemm::kernel_kind_name(c))
-                k = c;
+            if (base == bigemm::kernel_kind_name(c))
+                k = c | flag;
         if (k < 0) {
             *why = "unknown kernel kind '" + kind + "'";
             return false;
@@ -316,6 +336,7 @@ struct bi_gemm {
     uint32_t magic;
     int device;
     void* W;  // the handle's packed copy of the weights (slab-major), owned
+    void* split_ws;  // partials of concurrent splits, owned (or null)
     bigemm::Plan plan;
     bi_pin_info pin;
 };
@@ -436,14 +457,34 @@ bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info*
         return fail(BI_ERR_HIP, std::string("packing W: ") + hipGetErrorString(he));
     }
 
+    // the split workspace: (S - 1) partials of the largest row bound whose
+    // tiling entry runs its splits concurrently
+    int ws_rows = 0;
+    if (E == 0 && splits > 1)
+        for (int i = 0; i < tiling.count; ++i)
+            if ((tiling.kernel[i] & BI_KERNEL_CONCURRENT_SPLITS) && tiling.m_max[i] > ws_rows)
+                ws_rows = tiling.m_max[i];
+    void* split_ws = nullptr;
+    if (ws_rows > 0) {
+        const size_t bytes = (size_t)(splits - 1) * ws_rows * N * sizeof(float);
+        if (hipMalloc(&split_ws, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            (void)hipFree(packed);
+            return fail(BI_ERR_OUT_OF_MEMORY, "out of device memory for the split workspace (" +
+                                                  std::to_string(bytes) + " bytes)");
+        }
+    }
+
     bi_gemm* h = new (std::nothrow) bi_gemm;
     if (!h) {
         (void)hipFree(packed);
+        (void)hipFree(split_ws);
         return fail(BI_ERR_OUT_OF_MEMORY, "out of host memory");
     }
     h->magic = kMagic;
     h->device = dev;
     h->W = packed;
+    h->split_ws = split_ws;
     h->plan.n = N;
     h->plan.k = K;
     h->plan.experts = E;
@@ -456,6 +497,8 @@ bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info*
         h->plan.tile_m_max[i] = tiling.m_max[i];
         h->plan.tile_kernel[i] = tiling.kernel[i];
     }
+    h->plan.split_ws = static_cast<float*>(split_ws);
+    h->plan.split_ws_rows = ws_rows;
     bi_pin_info& p = h->pin;
     std::memset(&p, 0, sizeof p);
     p.n = N;
@@ -476,11 +519,13 @@ bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info*
         p.tile_m_max[i] = h->plan.tile_m_max[i];
         p.tile_kernel[i] = h->plan.tile_kernel[i];
     }
+    p.split_ws_rows = ws_rows;
     try {
         std::lock_guard<std::mutex> g(g_live_mu);
         g_live.insert(h);
     } catch (...) {
         (void)hipFree(h->W);
+        (void)hipFree(h->split_ws);
         delete h;
         return fail(BI_ERR_OUT_OF_MEMORY, "out of host memory");
     }
@@ -769,6 +814,7 @@ void bi_gemm_destroy(bi_gemm_t hh)
     const bool switched = hipGetDevice(&cur) == hipSuccess && cur != hh->device &&
                           hipSetDevice(hh->device) == hipSuccess;
     (void)hipFree(hh->W);
+    (void)hipFree(hh->split_ws);
     if (switched)
         (void)hipSetDevice(cur);
     delete hh;
@@ -792,7 +838,8 @@ const char* bi_gemm_kernel_name(bi_gemm_t hh, int M)
         return "";
     if (h->plan.experts != 0)
         return bigemm::grouped_kernel_name(h->plan, M);
-    return bigemm::dense_kernel_name(bigemm::choose_dense(h->plan, M));
+    const bigemm::DenseKernel k = bigemm::choose_dense(h->plan, M);
+    return bigemm::concurrent_splits(h->plan, M) ? bigemm::dense_kernel_name_cs(k) : bigemm::dense_kernel_name(k);
 }
 
 const char* bi_status_string(bi_status_t s)

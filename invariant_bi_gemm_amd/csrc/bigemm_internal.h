@@ -34,7 +34,9 @@ struct Plan {
     int num_cus;           // compute units of the bound device
     int tilings;           // dense tiling list from the pin (0: built-in rule)
     int tile_m_max[BI_MAX_TILINGS];
-    int tile_kernel[BI_MAX_TILINGS];
+    int tile_kernel[BI_MAX_TILINGS];  // kind, | BI_KERNEL_CONCURRENT_SPLITS
+    float* split_ws;       // (splits-1) * split_ws_rows * n fp32, or null
+    int split_ws_rows;
 };
 
 // The dense kernels `run` may launch; M picks one, the tree is the same.
@@ -53,7 +55,12 @@ enum class DenseKernel {
     kTiled256 = BI_KERNEL_TILED4_256X256,
 };
 DenseKernel choose_dense(const Plan& p, int M);
+// Whether a call with M rows runs its splits concurrently (the tiling
+// entry's flag, S > 1, and M within the split workspace).
+bool concurrent_splits(const Plan& p, int M);
 const char* dense_kernel_name(DenseKernel k);
+// The name with ",concurrent splits" appended.
+const char* dense_kernel_name_cs(DenseKernel k);
 // Table name of a kind ("" when unknown).
 const char* kernel_kind_name(int kind);
 // The launches a grouped call with R rows makes, e.g.

@@ -147,13 +147,14 @@ __device__ __forceinline__ void emit4(float* p, const f32x4& v, int fold)
     }
 }
 
-// Concurrent split-K for the non-invariant comparison path only
-// (bi_gemm_run_splitk): the kernels instantiated with kMode == kCmp run split
+// Concurrent K splits: the kernels instantiated with kMode == kCmp run split
 // blockIdx.y of gridDim.y, each a chain over its own K range from +0; split 0
 // stores into y and split s > 0 into partial s - 1 of `part` ([splits-1][M][N]),
-// which splitk_reduce adds to y afterwards.  Where the splits fall follows
-// the caller's choice per M, so rows are not batch-invariant there.  The
-// product kernels are other instances and never take this path.
+// which splitk_reduce then adds to y in split order, ((p0 + p1) + p2) + ...
+// Two callers: a pin whose tiling runs its S splits concurrently (the same
+// tree as the splits one after another, so the same bits), and the
+// non-invariant comparison path (bi_gemm_run_splitk), where the caller picks
+// the split count per call.
 // What a dense kernel instance does: the product GEMM, the comparison
 // path's concurrent split-K, or the product GEMM of RMSNorm'd rows (x raw,
 // normalised in LDS before the MFMAs).
@@ -1426,7 +1427,7 @@ DenseKernel choose_dense(const Plan& p, int M)
     // the pin's tiling list, when it has one: the entry whose row range holds M
     for (int i = 0; i < p.tilings; ++i)
         if (M <= p.tile_m_max[i])
-            return static_cast<DenseKernel>(p.tile_kernel[i]);
+            return static_cast<DenseKernel>(p.tile_kernel[i] & ~BI_KERNEL_CONCURRENT_SPLITS);
     if (M <= p.stream_max_m) {
         if (M <= 16)
             return DenseKernel::kStream16;
@@ -1442,6 +1443,34 @@ DenseKernel choose_dense(const Plan& p, int M)
             return blocks <= p.num_cus ? t.deep : t.kind;
     }
     return DenseKernel::kTiled64x32;
+}
+
+bool concurrent_splits(const Plan& p, int M)
+{
+    if (p.splits < 2 || !p.split_ws || M > p.split_ws_rows)
+        return false;
+    for (int i = 0; i < p.tilings; ++i)
+        if (M <= p.tile_m_max[i])
+            return (p.tile_kernel[i] & BI_KERNEL_CONCURRENT_SPLITS) != 0;
+    return false;
+}
+
+const char* dense_kernel_name_cs(DenseKernel k)
+{
+    switch (k) {
+    case DenseKernel::kStream16: return "bigemm_stream<mb=1>,concurrent splits";
+    case DenseKernel::kStream32: return "bigemm_stream<mb=2>,concurrent splits";
+    case DenseKernel::kStream64: return "bigemm_stream<mb=4>,concurrent splits";
+    case DenseKernel::kTiled64x32: return "bigemm_tiled<64x32>,concurrent splits";
+    case DenseKernel::kTiled64: return "bigemm_tiled<64x64>,concurrent splits";
+    case DenseKernel::kTiled128x64: return "bigemm_tiled<128x64>,concurrent splits";
+    case DenseKernel::kTiled128x64Deep: return "bigemm_tiled<128x64,deep>,concurrent splits";
+    case DenseKernel::kTiled128: return "bigemm_tiled<128x128>,concurrent splits";
+    case DenseKernel::kTiled128Deep: return "bigemm_tiled<128x128,deep>,concurrent splits";
+    case DenseKernel::kTiled128x256: return "bigemm_tiled<128x256>,concurrent splits";
+    case DenseKernel::kTiled256: return "bigemm_tiled<256x256>,concurrent splits";
+    }
+    return "?";
 }
 
 const char* kernel_kind_name(int kind)
@@ -1524,6 +1553,10 @@ hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, floa
                         hipStream_t stream)
 {
     const DenseKernel kind = choose_dense(p, M);
+    // the same tree with its splits side by side: partials of splits 1..S-1
+    // into the handle's workspace, then folded into y in split order
+    if (concurrent_splits(p, M))
+        return launch_splitk(p, static_cast<int>(kind), p.splits, W, x, M, y, p.split_ws, stream);
     const int klen = p.k / p.splits;
     for (int s = 0; s < p.splits; ++s) {
         const hipError_t e = launch_dense_split(p, kind, W, x, M, y, Split{s * klen, klen, s > 0}, stream);

@@ -77,9 +77,23 @@ def legal_splits(k: int, choices=SPLIT_CHOICES):
     return [s for s in choices if 1 <= s <= MAX_SPLITS and k % (64 * s) == 0]
 
 
+CS = "+cs"        # a kind running the tree's splits concurrently (S > 1 only)
+CS_LIMIT = 16384  # the library's bound on the rows of such an entry
+
+
+def base_kind(kd: str) -> str:
+    return kd[:-len(CS)] if kd.endswith(CS) else kd
+
+
 def kernel_candidates(m: int, kinds=KERNEL_KINDS):
     """Kernel kinds tried at M rows."""
-    return [kd for kd in kinds if m <= STREAM_LIMIT or kd not in STREAM_KINDS]
+    return [kd for kd in kinds if m <= STREAM_LIMIT or base_kind(kd) not in STREAM_KINDS]
+
+
+def tree_kinds(s: int, kinds=KERNEL_KINDS):
+    """The kinds measured for a tree with s splits: with s > 1 each kind also
+    with its splits run concurrently."""
+    return list(kinds) + ([kd + CS for kd in kinds] if s > 1 else [])
 
 
 def cost(profile, timing):
@@ -100,7 +114,7 @@ def pick_kernels(times, kinds=KERNEL_KINDS, tie=TIE, tie_abs=TIE_ABS):
     kind."""
     out, prev = {}, None
     for m in sorted(times):
-        cand = [(t, kinds.index(kd), kd) for kd, t in times[m].items() if kd in kernel_candidates(m, kinds)]
+        cand = [(t, kinds.index(kd), kd) for kd, t in times[m].items() if kd in kinds and kd in kernel_candidates(m, kinds)]
         best_t = min(c[0] for c in cand)
         if prev is not None and prev in times[m] and prev in kernel_candidates(m, kinds) and \
                 times[m][prev] <= max(best_t * (1 + tie), best_t + tie_abs):
@@ -122,20 +136,24 @@ def choose(profile, measure, splits, kinds=KERNEL_KINDS, tie=TIE):
     the earlier candidate (fewer splits)."""
     report = []
     best = None
+    mmax = max(m for m, _ in profile)
     for s in splits:
+        skinds = tree_kinds(s, kinds)
         times = {m: {} for m, _ in profile}
-        for kd in kinds:
+        for kd in skinds:
             t = measure(s, kd)
             for m, _ in profile:
-                if kd in kernel_candidates(m, kinds):
+                # the last range covers every larger M: no concurrent splits there
+                if kd in kernel_candidates(m, skinds) and not (kd.endswith(CS) and (m == mmax or m > CS_LIMIT)):
                     times[m][kd] = t[m]
-        per_m = pick_kernels(times, kinds, tie)
+        kinds_ = skinds
+        per_m = pick_kernels(times, kinds_, tie)
         # a tiling list holds at most MAX_TILINGS ranges: widen the tie until
         # the picks fit (only noise-level differences are ever merged first)
         t_ = tie
         while len(tiling_from_choice({m: v[0] for m, v in per_m.items()}, check=False)) > MAX_TILINGS:
             t_ *= 2
-            per_m = pick_kernels(times, kinds, t_)
+            per_m = pick_kernels(times, kinds_, t_)
         total = cost(profile, {m: v[1] for m, v in per_m.items()})
         report.append((s, total, per_m))
         if best is None or total < best[1]:
@@ -166,7 +184,7 @@ def stream_threshold(tiling, default=16):
     it); `default` when it streams nothing."""
     last = 0
     for bound, kind in tiling:
-        if kind in STREAM_KINDS:
+        if base_kind(kind) in STREAM_KINDS:
             last = bound if bound is not None else 4096
     return min(last, 4096) if last else default
 
@@ -179,12 +197,14 @@ def parse_tiling(text: str):
     out = []
     for item in text.split(","):
         b, _, kd = item.partition(":")
-        if kd not in KERNEL_KINDS:
+        if base_kind(kd) not in KERNEL_KINDS:
             raise ValueError("unknown kernel kind %r" % kd)
         out.append((None if b == "*" else int(b), kd))
     bounds = [b for b, _ in out[:-1]]
     if not out or out[-1][0] is not None or bounds != sorted(set(bounds)) or any(b < 1 for b in bounds):
         raise ValueError("tiling bounds must ascend and end with '*': %r" % text)
+    if out[-1][1].endswith(CS) or any(kd.endswith(CS) and b > CS_LIMIT for b, kd in out[:-1]):
+        raise ValueError("concurrent splits only on bounded entries of at most %d rows: %r" % (CS_LIMIT, text))
     return out
 
 
@@ -270,12 +290,17 @@ def device_measure(n: int, k: int, profile, reps: int = 20, rotate_bytes: float 
     xp = ctypes.c_void_p(x.data_ptr())
     run = lib.bi_gemm_run
 
+    cs_rows = min(mmax, CS_LIMIT)
+
     def measure(s, kind):
-        hs = [_lib.Gemm(w, pin={"splits": s, "stream_max_m": 0, "tiling": [(None, kind)]}) for w in ws]
+        # a kind with concurrent splits serves every measured M up to the
+        # largest (its workspace sized for it); the plain kind covers the rest
+        tiling = [(cs_rows, kind), (None, base_kind(kind))] if kind.endswith(CS) else [(None, kind)]
+        hs = [_lib.Gemm(w, pin={"splits": s, "stream_max_m": 0, "tiling": tiling}) for w in ws]
         hp = [h._h for h in hs]
         out = {}
         for m, _ in profile:
-            if kind not in kernel_candidates(m):
+            if kind not in kernel_candidates(m, [kind]):
                 out[m] = float("inf")
                 continue
             yp = ctypes.c_void_p(ys[m].data_ptr())
@@ -316,7 +341,7 @@ def main(argv=None):
     kinds = tuple(v for v in args.kinds.split(",") if v)
     for kd in kinds:
         if kd not in KERNEL_KINDS:
-            raise SystemExit("unknown kernel kind %r" % kd)
+            raise SystemExit("unknown kernel kind %r (concurrent variants are added for S > 1)" % kd)
     splits = legal_splits(k, tuple(int(v) for v in args.splits.split(",")))
     measure = device_measure(n, k, profile, reps=args.reps)
     s, choice, times, report = choose(profile, measure, splits, kinds)

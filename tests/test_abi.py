@@ -174,6 +174,9 @@ def _head(lib):
     "HEAD gfx950 256 512 1 16 64:tiled_96x96,*:tiled4_256x256\n",                 # unknown kind
     "HEAD gfx950 256 512 1 16 0:stream_mb1,*:tiled4_256x256\n",                   # bound below 1
     "HEAD gfx950 256 512 1 16 *:tiled4_256x256 extra\n",    # trailing field
+    "HEAD gfx950 256 512 2 16 *:tiled_64x64+cs\n",          # concurrent splits on the unbounded entry
+    "HEAD gfx950 256 512 2 16 20000:tiled_64x64+cs,*:tiled4_256x256\n",  # beyond 16384 rows
+    "HEAD gfx950 256 512 2 16 64:tiled_64x64+xx,*:tiled4_256x256\n",     # unknown suffix
     "version x\n",
 ])
 def test_bad_pin_tables_rejected(lib, tmp_path, body):
@@ -184,7 +187,8 @@ def test_bad_pin_tables_rejected(lib, tmp_path, body):
 
 
 def test_tiled_pin_table_accepted(lib, tmp_path):
-    body = _head(lib) + "gfx950 256 512 1 16 16:stream_mb1,100:tiled_64x32,*:tiled4_256x256\n"
+    body = _head(lib) + ("gfx950 256 512 1 16 16:stream_mb1,100:tiled_64x32,*:tiled4_256x256\n"
+                         "gfx950 256 1024 2 16 16:stream_mb1,100:tiled_64x32+cs,*:tiled4_256x256\n")
     assert lib.bi_gemm_load_pins(_table(tmp_path, body)) == 0, lib.bi_last_error()
     assert lib.bi_gemm_load_pins(bg.PIN_TABLE.encode()) == 0
 
@@ -201,7 +205,10 @@ def test_create_pinned_rejects_illegal_tilings(lib):
     for tiling in ([(64, "tiled_64x64")],                                   # last bound not 'every M'
                    [(64, "tiled_64x64"), (32, "tiled_64x32"), (None, "tiled4_256x256")],
                    [(0, "stream_mb1"), (None, "tiled4_256x256")],
-                   [(None, 11)], [(None, -1)]):
+                   [(None, 11)], [(None, -1)],
+                   [(None, "tiled_64x64+cs")],                               # unbounded concurrent splits
+                   [(16385, "tiled_64x64+cs"), (None, "tiled_64x64")],
+                   [(None, 0x200)]):
         p = BiPinInfo()
         p.splits, p.stream_max_m = 1, 16
         p.set_tiling(tiling)
@@ -251,3 +258,16 @@ def test_env_pin_table_failure_stops_create(lib, tmp_path, body, want):
 def test_missing_pin_table(lib):
     assert lib.bi_gemm_load_pins(b"/nonexistent/pins.txt") == INV
     assert lib.bi_gemm_load_pins(bg.PIN_TABLE.encode()) == 0
+
+
+def test_every_shipped_pin_table_parses(lib):
+    """Every table under pins/ (one per workload profile) loads in the C
+    parser and names the library's tree."""
+    pins_dir = os.path.dirname(bg.PIN_TABLE)
+    tables = sorted(f for f in os.listdir(pins_dir) if f.endswith(".txt"))
+    assert "gfx950.txt" in tables and "gfx950_chunked_prefill.txt" in tables
+    try:
+        for t in tables:
+            assert lib.bi_gemm_load_pins(os.path.join(pins_dir, t).encode()) == 0, (t, lib.bi_last_error())
+    finally:
+        assert lib.bi_gemm_load_pins(bg.PIN_TABLE.encode()) == 0

@@ -117,3 +117,15 @@ def test_fused_norm_gemm_graph_and_stream(gpu):
     y = torch.empty((m, n), dtype=torch.float32, device=DEV)
     r = torch.empty(m, dtype=torch.float32, device=DEV)
     check_graph_and_stream(lambda: g.rmsnorm_run(x, gain, 1e-5, out=y, rstd=r), [y, r], "RMSNorm+GEMM M=%d" % m)
+
+
+def test_concurrent_split_pin_graph(gpu):
+    """A pin whose splits run concurrently uses the handle's workspace; the
+    captured call replays to the same bits."""
+    n, k = 1024, 4096
+    g = gpu.Gemm(to_dev(synth.normal_bf16(540, (n, k), 0.02)),
+                 pin={"splits": 2, "stream_max_m": 0, "tiling": [(512, "tiled_64x64+cs"), (None, "tiled_64x64")]})
+    x = to_dev(synth.normal_bf16(541, (300, k)))
+    y = torch.empty((300, n), dtype=torch.float32, device=DEV)
+    assert g.kernel_name(300).endswith("concurrent splits")
+    check_graph_and_stream(lambda: g(x, out=y), [y], "S=2 concurrent M=300")

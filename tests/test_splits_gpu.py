@@ -177,3 +177,74 @@ def test_split_four_wave_kernels(gpu, m, kernel):
     for r in synth.probe_rows(219 + m, m, 6):
         r = int(r)
         assert_bits_equal(yb[r], bits32(gf(xf[r:r + 1]))[0], "S=2 %s row %d vs alone" % (kernel, r))
+
+
+@pytest.mark.parametrize("splits", [2, 4])
+@pytest.mark.parametrize("kind", ["stream_mb1", "tiled_64x32", "tiled_64x64", "tiled_128x128_deep", "tiled4_128x256",
+                                  "tiled4_256x256"])
+def test_concurrent_splits_same_bits(gpu, kind, splits):
+    """A tiling entry that runs the tree's splits concurrently (partials in
+    the handle's workspace, folded in split order) gives the bits of the same
+    kernel running the splits one after another, up to its row bound and
+    beyond it (where it falls back to the splits in sequence)."""
+    n, k = 1024, 4096
+    w = synth.normal_bf16(240, (n, k), 0.02)
+    x = synth.normal_bf16(241, (700, k))
+    wd, xd = to_dev(w), to_dev(x)
+    gc = gpu.Gemm(wd, pin={"splits": splits, "stream_max_m": 0, "tiling": [(512, kind + "+cs"), (None, kind)]})
+    gs = gpu.Gemm(wd, pin={"splits": splits, "stream_max_m": 0, "tiling": [(None, kind)]})
+    assert gc.pin["split_ws_rows"] == 512 and gs.pin["split_ws_rows"] == 0
+    for m in (1, 37, 300, 512, 513, 700):
+        assert gc.kernel_name(m).endswith(",concurrent splits") == (m <= 512)
+        assert_bits_equal(bits32(gc(xd[:m])), bits32(gs(xd[:m])), "%s S=%d M=%d" % (kind, splits, m))
+
+
+def test_concurrent_splits_integer_exact_and_invariant(gpu):
+    """The Llama-3.1-8B down-proj shape with an S = 2 tree whose mid-M
+    entries run concurrently: integer inputs give exact sums at every M, and
+    each row's bits equal the row computed alone (M = 1, which streams)."""
+    n, k = 4096, 14336
+    w = synth.int_bf16(242, (n, k))
+    x = synth.int_bf16(243, (600, k))
+    tiling = [(16, "stream_mb1"), (64, "tiled_64x32+cs"), (512, "tiled_128x64_deep+cs"), (None, "tiled4_256x256")]
+    g = gpu.Gemm(to_dev(w), pin={"splits": 2, "stream_max_m": 16, "tiling": tiling})
+    xd = to_dev(x)
+    rows = np.array([0, 5, 63, 64, 299, 511, 599])
+    alone = np.stack([bits32(g(xd[r:r + 1]))[0] for r in rows])
+    yi = oracle.gemm_i64(x[rows], w)
+    for m in (64, 300, 512, 600):
+        y = g(xd[:m])
+        idx = rows[rows < m]
+        assert_bits_equal(bits32(y)[idx], alone[:len(idx)], "M=%d" % m)
+        assert np.array_equal(y.cpu().numpy()[idx].astype(np.float64), yi[:len(idx)].astype(np.float64)), m
+
+
+def test_chunked_prefill_pin_rows_invariant(gpu):
+    """The shipped chunked-prefill pin of the Llama-3.1-8B down-proj (four
+    splits, concurrent up to its bound): at every M of the sweep, probe rows
+    equal the rows alone, and sampled rows pass the oracle bound."""
+    import os
+
+    from invariant_bi_gemm_amd import tuner
+
+    path = os.path.join(os.path.dirname(gpu.PIN_TABLE), "gfx950_chunked_prefill.txt")
+    _, _, _, rows = tuner.read_table(path)
+    s_, smax, tiling = rows[("gfx950", 4096, 14336)]
+    n, k = 4096, 14336
+    w = synth.normal_bf16(250, (n, k), 0.02)
+    ms = [1, 16, 64, 128, 256, 512, 1024, 2048, 8192]
+    x = synth.silu_mul_bf16(251, (max(ms), k))
+    g = gpu.Gemm(to_dev(w), pin={"splits": s_, "stream_max_m": smax, "tiling": tiling})
+    assert g.pin["splits"] == s_ and g.pin["split_ws_rows"] > 0
+    xd = to_dev(x)
+    probes = {m: synth.probe_rows(252 + m, m, 8) for m in ms}
+    allrows = np.unique(np.concatenate(list(probes.values())))
+    alone = {}
+    for r in allrows:
+        alone[int(r)] = bits32(g(xd[int(r):int(r) + 1]))[0]
+    for m in ms:
+        y = g(xd[:m])
+        got = bits32(y)[probes[m]]
+        assert_bits_equal(got, np.stack([alone[int(r)] for r in probes[m]]), "%s M=%d" % (g.kernel_name(m), m))
+        yr, a = oracle.gemm_f64(x[:m], w, rows=probes[m][:4])
+        assert_parity(y.cpu().numpy()[probes[m][:4]], yr, a, "M=%d" % m)

@@ -41,6 +41,8 @@ def test_cost_and_choose():
         (1, "tiled4_256x256"): {1: 60e-6, 4096: 400e-6},
         (2, "stream_mb1"): {1: 15e-6, 4096: float("inf")},
         (2, "tiled4_256x256"): {1: 70e-6, 4096: 460e-6},
+        (2, "stream_mb1+cs"): {1: 1.0, 4096: 1.0},
+        (2, "tiled4_256x256+cs"): {1: 1.0, 4096: 1.0},
     }
     kinds = ("stream_mb1", "tiled4_256x256")
     s, choice, times, report = tuner.choose(prof, lambda s_, kd: table[(s_, kd)], [1, 2], kinds)
@@ -141,3 +143,25 @@ def test_tuner_on_device(gpu):
         assert g.kernel_name(m) == want
     y = g(torch.randn(5, 512, device="cuda:0").to(torch.bfloat16))
     assert torch.isfinite(y).all()
+
+
+def test_concurrent_split_candidates():
+    assert tuner.tree_kinds(1) == list(tuner.KERNEL_KINDS)
+    k2 = tuner.tree_kinds(2)
+    assert "tiled_64x64+cs" in k2 and len(k2) == 2 * len(tuner.KERNEL_KINDS)
+    assert tuner.base_kind("tiled_64x64+cs") == "tiled_64x64"
+    # S = 2 with concurrent splits faster in the middle; never chosen for the last range
+    prof = [(1, 1), (256, 1), (8192, 1)]
+    t = {(1, "stream_mb1"): {1: 20e-6, 256: 1.0, 8192: 1.0},
+         (1, "tiled_64x64"): {1: 30e-6, 256: 70e-6, 8192: 900e-6},
+         (2, "stream_mb1"): {1: 20e-6, 256: 1.0, 8192: 1.0},
+         (2, "tiled_64x64"): {1: 30e-6, 256: 75e-6, 8192: 905e-6},
+         (2, "stream_mb1+cs"): {1: 24e-6, 256: 1.0, 8192: 1e-6},
+         (2, "tiled_64x64+cs"): {1: 30e-6, 256: 40e-6, 8192: 1e-6}}
+    s, choice, times, report = tuner.choose(prof, lambda s_, kd: t[(s_, kd)], [1, 2], ("stream_mb1", "tiled_64x64"))
+    assert s == 2 and choice == {1: "stream_mb1", 256: "tiled_64x64+cs", 8192: "tiled_64x64"}
+    tiling = tuner.tiling_from_choice(choice)
+    assert tiling[-1] == (None, "tiled_64x64") and tuner.parse_tiling(tuner.format_tiling(tiling)) == tiling
+    for bad in ("16:stream_mb1,*:tiled_64x64+cs", "20000:tiled_64x64+cs,*:tiled_64x64"):
+        with pytest.raises(ValueError):
+            tuner.parse_tiling(bad)
