@@ -71,8 +71,9 @@ __global__ void __launch_bounds__(kThreads)
 {
     __shared__ float s_wave[kWaves];
     const int h8 = H / 8;
-    uint4 v[CPT];
+    uint4 v[CPT], gv[CPT];
     load_row<CPT>(x + (size_t)blockIdx.x * h8, h8, v);
+    load_row<CPT>(g, h8, gv);  // issued with the row, so the reduction hides its latency
     const float r = row_rstd<CPT>(v, H, eps, s_wave);
     uint4* yr = y + (size_t)blockIdx.x * h8;
 #pragma unroll
@@ -80,7 +81,7 @@ __global__ void __launch_bounds__(kThreads)
         const int c = threadIdx.x + kThreads * q;
         if (c >= h8)
             break;
-        yr[c] = bi::rms_scale_chunk(v[q], r, g[c]);
+        yr[c] = bi::rms_scale_chunk(v[q], r, gv[q]);
     }
 }
 
