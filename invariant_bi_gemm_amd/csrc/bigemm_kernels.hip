@@ -938,6 +938,7 @@ __global__ void __launch_bounds__(WM * WN * 64)
 // consumer of a single m-tile then re-reads row XR-1 for its padding rows).
 // NP producer waves split a stage's loads; NR stages live in an LDS ring.
 constexpr int kStreamLdsBudget = 144 * 1024;
+constexpr int kStreamWInFlight = 32 * 1024;
 // Producer waves per streaming workgroup: the WG has at most 8 waves (two
 // per SIMD, so each may use 256 VGPRs); narrower stages have fewer loads and
 // use fewer producers.
@@ -956,8 +957,16 @@ struct StreamShape {
     static constexpr int kLo = kT / NP;             // share of the others
     static constexpr int kByLds = kStreamLdsBudget / (kStageUnits * 16);
     static constexpr int kByVmcnt = 63 / kHi + 1;
-    static constexpr int kNR = kByLds < kByVmcnt ? (kByLds < 16 ? kByLds : 16)
-                                                 : (kByVmcnt < 16 ? kByVmcnt : 16);
+    // 512-wide stages: at most 32 KB of W in flight per workgroup (8 MB over
+    // 256 CUs, about HBM's bandwidth-latency product).  Deeper rings queue
+    // more requests at HBM and stream slower (M = 1 on a 117 MB weight:
+    // 19.7 us with two stages in flight against 21.2 us with seven).  The
+    // narrower stages keep their depth: the grouped kernel's short items
+    // (K = 768: three stages an item) lose 3% when capped the same way.
+    static constexpr int kByFlight = BKS >= 512 ? kStreamWInFlight / (16 * BKS * 2) + 1 : 16;
+    static constexpr int kNR0 = kByLds < kByVmcnt ? kByLds : kByVmcnt;
+    static constexpr int kNR1 = kNR0 < kByFlight ? kNR0 : kByFlight;
+    static constexpr int kNR = kNR1 < 16 ? kNR1 : 16;
 };
 
 template <int MB, int XR, int BKS, int NP>
