@@ -213,12 +213,15 @@ __global__ void __launch_bounds__(kThreads)
 
     // group grp takes keys grp, grp+16, ..., kUnroll at a time in ascending order
     constexpr int kUnroll = unroll_of<G>();
+    // byte offset of key kidx's slice; keys past the split read as zeros
+    // (the buffers end there), and an index past it is clamped to cnt so that
+    // the 32-bit offset cannot wrap back into the split
+    auto key_off = [&](int kidx) { return (uint32_t)min(kidx, cnt) * rowb + (uint32_t)r * 16; };
     for (int t = grp; t < cnt; t += kGroups * kUnroll) {
-        // keys past the split read as zeros (the buffers end there)
         uint4 kk[kUnroll], vv[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t off = (uint32_t)(t + kGroups * u) * rowb + (uint32_t)r * 16;
+            const uint32_t off = key_off(t + kGroups * u);
             kk[u] = load16(rK, off);
             vv[u] = load16(rV, off);
         }
