@@ -78,7 +78,9 @@ typedef enum {
     BI_KERNEL_TILED_128X128_DEEP = 8,
     BI_KERNEL_TILED4_128X256 = 9, /* four waves, accumulators in AGPRs           */
     BI_KERNEL_TILED4_256X256 = 10,
-    BI_KERNEL_COUNT = 11
+    BI_KERNEL_TILED4_160X256 = 11, /* the four-wave kernel at other block heights, */
+    BI_KERNEL_TILED4_192X256 = 12, /* for M that 128 and 256 rows divide badly     */
+    BI_KERNEL_COUNT = 13
 } bi_kernel_kind_t;
 
 /* Most entries of a pin's tiling list. */

@@ -1,5 +1,5 @@
-"""Checks on the built code of the four-wave kernels (dense 256x256 and
-128x256 blocks, grouped), run on the CPU by every build.
+"""Checks on the built code of the four-wave kernels (dense 256x256,
+192x256, 160x256 and 128x256 blocks, grouped), run on the CPU by every build.
 
 Their accumulators live in a0..a255, written only by inline-asm MFMAs and
 read only by the epilogue; the compiler does not know they are live.  So the
@@ -19,7 +19,7 @@ import subprocess
 from . import build
 
 SRC = os.path.join(build.CSRC, "bigemm_kernels.hip")
-# the dense kernels (8 and 4 x tiles per wave; the product instance and the
+# the dense kernels (8, 6, 5 and 4 x tiles per wave; the product instance and the
 # comparison path's split-K instance) and the grouped one (plain and indexed
 # rows; both block heights in one kernel), with the accumulator tiles each of
 # their epilogues reads
@@ -27,6 +27,10 @@ KERNELS = {"_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi8ELi0E": [64],
            "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi4ELi0E": [32],
            "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi8ELi1E": [64],
            "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi4ELi1E": [32],
+           "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi5ELi0E": [40],
+           "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi5ELi1E": [40],
+           "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi6ELi0E": [48],
+           "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi6ELi1E": [48],
            "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb0E": [64, 32],
            "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1E": [64, 32]}
 MFMA_AGPR = re.compile(r"v_mfma_f32_16x16x32_bf16 a\[\d+:\d+\], v\[\d+:\d+\], v\[\d+:\d+\], (a\[\d+:\d+\]|0)$")

@@ -53,6 +53,8 @@ enum class DenseKernel {
     kTiled128Deep = BI_KERNEL_TILED_128X128_DEEP,
     kTiled128x256 = BI_KERNEL_TILED4_128X256,
     kTiled256 = BI_KERNEL_TILED4_256X256,
+    kTiled160x256 = BI_KERNEL_TILED4_160X256,
+    kTiled192x256 = BI_KERNEL_TILED4_192X256,
 };
 DenseKernel choose_dense(const Plan& p, int M);
 // Whether a call with M rows runs its splits concurrently (the tiling

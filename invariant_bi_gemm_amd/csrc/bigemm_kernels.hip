@@ -720,7 +720,7 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
                                               int row_hi, int n0, int N, int K, Split sp,
                                               const int32_t* __restrict__ xidx = nullptr, int xn = 0)
 {
-    static_assert(XT == 4 || XT == 8, "x tiles per wave");
+    static_assert(XT >= 4 && XT <= 8, "x tiles per wave");
     constexpr int BM = 32 * XT, BN = 256, BK = 64, kCh = BK / 8;
     constexpr int kPart = 256 * kCh;      // units (16 B) of one 256-row W part of a stage: 32 KB
     constexpr int kXPart = BM * kCh;      // units of one stage's x rows
@@ -1478,6 +1478,8 @@ const char* dense_kernel_name_cs(DenseKernel k)
     case DenseKernel::kTiled128Deep: return "bigemm_tiled<128x128,deep>,concurrent splits";
     case DenseKernel::kTiled128x256: return "bigemm_tiled<128x256>,concurrent splits";
     case DenseKernel::kTiled256: return "bigemm_tiled<256x256>,concurrent splits";
+    case DenseKernel::kTiled160x256: return "bigemm_tiled<160x256>,concurrent splits";
+    case DenseKernel::kTiled192x256: return "bigemm_tiled<192x256>,concurrent splits";
     }
     return "?";
 }
@@ -1496,6 +1498,8 @@ const char* kernel_kind_name(int kind)
     case BI_KERNEL_TILED_128X128_DEEP: return "tiled_128x128_deep";
     case BI_KERNEL_TILED4_128X256: return "tiled4_128x256";
     case BI_KERNEL_TILED4_256X256: return "tiled4_256x256";
+    case BI_KERNEL_TILED4_160X256: return "tiled4_160x256";
+    case BI_KERNEL_TILED4_192X256: return "tiled4_192x256";
     }
     return "";
 }
@@ -1514,6 +1518,8 @@ const char* dense_kernel_name(DenseKernel k)
     case DenseKernel::kTiled128Deep: return "bigemm_tiled<128x128,deep>";
     case DenseKernel::kTiled128x256: return "bigemm_tiled<128x256>";
     case DenseKernel::kTiled256: return "bigemm_tiled<256x256>";
+    case DenseKernel::kTiled160x256: return "bigemm_tiled<160x256>";
+    case DenseKernel::kTiled192x256: return "bigemm_tiled<192x256>";
     }
     return "?";
 }
@@ -1540,6 +1546,10 @@ hipError_t launch_dense_split(const Plan& p, DenseKernel kind, const void* W, co
         return run_tiled4<8>(W, x, M, y, p.n, p.k, sp, stream, ex);
     case DenseKernel::kTiled128x256:
         return run_tiled4<4>(W, x, M, y, p.n, p.k, sp, stream, ex);
+    case DenseKernel::kTiled160x256:
+        return run_tiled4<5>(W, x, M, y, p.n, p.k, sp, stream, ex);
+    case DenseKernel::kTiled192x256:
+        return run_tiled4<6>(W, x, M, y, p.n, p.k, sp, stream, ex);
     case DenseKernel::kTiled128:
         return run_tiled<128, 128, 2, 2, 64, 2>(W, x, M, y, p.n, p.k, sp, stream, ex);
     case DenseKernel::kTiled128x64:
@@ -1627,6 +1637,8 @@ DenseKernel norm_kind(DenseKernel k)
     case DenseKernel::kTiled128:  // two stages: too shallow to rewrite one ahead
     case DenseKernel::kTiled128x256:
     case DenseKernel::kTiled256:
+    case DenseKernel::kTiled160x256:
+    case DenseKernel::kTiled192x256:
         return DenseKernel::kTiled128Deep;
     default:
         return k;

@@ -45,7 +45,8 @@ SPLIT_CHOICES = (1, 2, 4, 7, 8, 14, 16)
 MAX_SPLITS = 16
 STREAM_KINDS = ("stream_mb1", "stream_mb2", "stream_mb4")
 KERNEL_KINDS = ("stream_mb1", "stream_mb2", "stream_mb4", "tiled_64x32", "tiled_64x64", "tiled_128x64",
-                "tiled_128x64_deep", "tiled_128x128", "tiled_128x128_deep", "tiled4_128x256", "tiled4_256x256")
+                "tiled_128x64_deep", "tiled_128x128", "tiled_128x128_deep", "tiled4_128x256", "tiled4_256x256",
+                "tiled4_160x256", "tiled4_192x256")
 STREAM_LIMIT = 256  # streamers are candidates at M <= this
 MAX_TILINGS = 12
 INT32_MAX = 2 ** 31 - 1
@@ -131,7 +132,8 @@ def choose(profile, measure, splits, kinds=KERNEL_KINDS, tie=TIE):
 
     ``measure(s, kind)`` returns {M: seconds} for the profile's M (only the
     M where ``kind`` is a candidate are read).  Returns (S, {M: kind},
-    {M: seconds}, report) with report = [(S, total, {M: (kind, seconds)})].
+    {M: seconds}, report) with report = [(S, total, {M: (kind, seconds)},
+    {M: {kind: seconds}})], the last the times of every candidate measured.
     Per S the kernels are those of pick_kernels; ties between trees go to
     the earlier candidate (fewer splits)."""
     report = []
@@ -155,7 +157,7 @@ def choose(profile, measure, splits, kinds=KERNEL_KINDS, tie=TIE):
             t_ *= 2
             per_m = pick_kernels(times, kinds_, t_)
         total = cost(profile, {m: v[1] for m, v in per_m.items()})
-        report.append((s, total, per_m))
+        report.append((s, total, per_m, times))
         if best is None or total < best[1]:
             best = (s, total, per_m)
     s, _, per_m = best
@@ -335,6 +337,7 @@ def main(argv=None):
     ap.add_argument("--splits", default=",".join(map(str, SPLIT_CHOICES)))
     ap.add_argument("--kinds", default=",".join(KERNEL_KINDS))
     ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--show", type=int, default=5, help="candidates listed per M in the report (fastest first)")
     args = ap.parse_args(argv)
     n, k = (int(v) for v in args.shape.lower().split("x"))
     profile = parse_profile(args.profile)
@@ -345,9 +348,12 @@ def main(argv=None):
     splits = legal_splits(k, tuple(int(v) for v in args.splits.split(",")))
     measure = device_measure(n, k, profile, reps=args.reps)
     s, choice, times, report = choose(profile, measure, splits, kinds)
-    for s_, total, per_m in report:
+    for s_, total, per_m, cand in report:
         print("S=%-2d cost %.1f us  %s" % (s_, total * 1e6, " ".join(
             "%d:%s:%.1f" % (m, kd, t * 1e6) for m, (kd, t) in sorted(per_m.items()))), flush=True)
+        for m in sorted(cand):
+            fastest = sorted(cand[m].items(), key=lambda kv: kv[1])[:args.show]
+            print("    M=%-6d %s" % (m, "  ".join("%s %.1f" % (kd, t * 1e6) for kd, t in fastest)), flush=True)
     tiling = tiling_from_choice(choice)
     smax = stream_threshold(tiling)
     print("chosen: N=%d K=%d splits=%d stream_max_m=%d tiling=%s" % (n, k, s, smax, format_tiling(tiling)),

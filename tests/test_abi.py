@@ -205,7 +205,7 @@ def test_create_pinned_rejects_illegal_tilings(lib):
     for tiling in ([(64, "tiled_64x64")],                                   # last bound not 'every M'
                    [(64, "tiled_64x64"), (32, "tiled_64x32"), (None, "tiled4_256x256")],
                    [(0, "stream_mb1"), (None, "tiled4_256x256")],
-                   [(None, 11)], [(None, -1)],
+                   [(None, len(bg.KERNEL_KINDS))], [(None, -1)],
                    [(None, "tiled_64x64+cs")],                               # unbounded concurrent splits
                    [(16385, "tiled_64x64+cs"), (None, "tiled_64x64")],
                    [(None, 0x200)]):

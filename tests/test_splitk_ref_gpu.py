@@ -38,7 +38,7 @@ def test_splitk_argument_checks(gpu):
     y = torch.zeros((4, 256), dtype=torch.float32, device=DEV)
     ws = torch.zeros(8 * 4 * 256, dtype=torch.float32, device=DEV)
     h, xp, yp, wp = g._h, P(x.data_ptr()), P(y.data_ptr()), P(ws.data_ptr())
-    assert lib.bi_gemm_run_splitk(h, xp, 4, yp, 11, 1, None, None) == INV       # unknown kind
+    assert lib.bi_gemm_run_splitk(h, xp, 4, yp, len(gpu.KERNEL_KINDS), 1, None, None) == INV  # unknown kind
     assert lib.bi_gemm_run_splitk(h, xp, 4, yp, -1, 1, None, None) == INV
     assert lib.bi_gemm_run_splitk(h, xp, 4, yp, 0, 3, wp, None) == INV         # 512 is not 3 x 64k
     assert lib.bi_gemm_run_splitk(h, xp, 4, yp, 0, 16, wp, None) == INV        # 512 / 16 < 64

@@ -50,6 +50,10 @@ def test_cost_and_choose():
     assert tuner.cost(prof, times) == pytest.approx(600e-6)
     assert [r[0] for r in report] == [1, 2]
     assert report[1][1] == pytest.approx(610e-6)
+    # the report keeps every measured candidate (+cs kinds never at the largest M)
+    assert report[0][3] == {1: {"stream_mb1": 20e-6, "tiled4_256x256": 60e-6}, 4096: {"tiled4_256x256": 400e-6}}
+    assert set(report[1][3][1]) == {"stream_mb1", "tiled4_256x256", "stream_mb1+cs", "tiled4_256x256+cs"}
+    assert set(report[1][3][4096]) == {"tiled4_256x256"}
     # heavier decode weight flips the tree
     prof2 = [(1, 100), (4096, 1)]
     s2, _, _, _ = tuner.choose(prof2, lambda s_, kd: table[(s_, kd)], [1, 2], kinds)
@@ -129,7 +133,7 @@ def test_tuner_on_device(gpu):
     s, choice, times, report = tuner.choose(prof, measure, [1, 2, 8], kinds)
     assert s in (1, 2, 8) and len(report) == 3
     assert set(choice) == {1, 24, 200, 300} and choice[300] not in tuner.STREAM_KINDS
-    for _, total, per_m in report:
+    for _, total, per_m, cand in report:
         assert 0 < total < float("inf") and set(per_m) == {1, 24, 200, 300}
     tiling = tuner.tiling_from_choice(choice)
     import torch
