@@ -14,7 +14,9 @@ serving the weights to the decode-size calls, the calls rotate over copies of
 W totalling at least 1 GiB (identical values, separate memory).
 
 Also reported: the dominant kernel's roofline (achieved vs MI355X peak, from
-HIP events around each launch in the timed region), HBM traffic from rocprof
+HIP events around its launches in the timed region, the only events there),
+per-M times (events around every launch, in as many instrumented steps run
+before the timed region), HBM traffic from rocprof
 counters when a current measurement is committed under profiles/, and the CPU
 oracle's throughput on a bounded sample of the same workload.
 
@@ -172,8 +174,8 @@ PREFILL_PROFILE = "1:4,16:4,64:8,128:16,256:16,512:16,1024:8,2048:2,4096:1,8192:
 
 def alternative_pin(bg, ws, xd, ms, n, k, steps, warmup, table_ms):
     """The sweep under the chunked-prefill pin (its own tree and tiling),
-    timed like the headline (events around each launch, median over the
-    steps), and both pins' costs over that profile (Detent eq. 3: sum of
+    timed like the headline's per-M figures (events around each launch,
+    median over the steps), and both pins' costs over that profile (Detent eq. 3: sum of
     count x time) -- the pin follows the workload profile."""
     import ctypes
 
@@ -1006,52 +1008,72 @@ def main(argv=None):
     run = lib.bi_gemm_run
     call_no = [0]
 
-    def step(events=None):
+    def step(events=None, timed=None):
+        # events[j]: the event pair around launch j, for the launches j in timed
         for j, m in enumerate(ms):
             h = hps[call_no[0] % copies]
             call_no[0] += 1
-            if events is not None:
+            on = events is not None and (timed is None or j in timed)
+            if on:
                 events[j][0].record()
             st = run(h, xp, m, yps[m], stream)
             if st != 0:
                 bg.check(st)
-            if events is not None:
+            if on:
                 events[j][1].record()
+
+    def new_events():
+        return [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ms]
+                for _ in range(args.steps)]
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, events around every launch on the launch stream
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ms]
-          for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
+    # per call: K instrumented steps, outside the timed region, with an event
+    # pair around every launch (the median over the steps of each launch's
+    # pair); a marker between every two launches of a step costs the step
+    # about 3% on the GPU, so the timed steps carry only the dominant
+    # kernel's
+    ev = new_events()
     for s in range(args.steps):
         step(ev[s])
-    t_end.record()
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    # per call: the median over the timed steps of its launch's event pair
     per_call_ms = {m: float(np.median([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
                    for j, m in enumerate(ms)}
-
-    step_flops = sum(flops.values())
-    ms_per_step = total_ms / args.steps
-    value = step_flops / (ms_per_step * 1e-3) / 1e12
 
     # dominant kernel: the one with the most time per step
     by_kernel = {}
     for m in ms:
         d = by_kernel.setdefault(names[m], {"ms": 0.0, "flops": 0.0, "bytes": 0.0, "launches": 0})
-        d["ms"] += per_call_ms[m]
         d["flops"] += flops[m]
         d["bytes"] += hbm_bytes[m]
         d["launches"] += 1
-    dom = max(by_kernel, key=lambda kname: by_kernel[kname]["ms"])
+        d["ms_probe"] = d.get("ms_probe", 0.0) + per_call_ms[m]
+    dom = max(by_kernel, key=lambda kname: by_kernel[kname]["ms_probe"])
+    dom_calls = {j for j, m in enumerate(ms) if names[m] == dom}
+
+    # timed region: K steps, events around the dominant kernel's launches
+    # (on the launch stream) for its roofline
+    ev = new_events()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        step(ev[s], dom_calls)
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    dom_call_ms = {j: float(np.median([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
+                   for j in dom_calls}
+
+    step_flops = sum(flops.values())
+    ms_per_step = total_ms / args.steps
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
     d = by_kernel[dom]
+    d["ms"] = sum(dom_call_ms.values())
     if "stream" in dom:
         achieved = d["bytes"] / (d["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -1063,7 +1085,7 @@ def main(argv=None):
     roof["kernel"] = dom
     roof["launches_per_step"] = d["launches"]
     roof["avg_launch_us"] = d["ms"] * 1e3 / d["launches"]
-    roof["launch_us_statistic"] = "median over the timed steps, per launch"
+    roof["launch_us_statistic"] = "median over the timed steps, per launch (its events are the only ones there)"
     # the MFMA peak scales with the engine clock: the same fraction against
     # the peak at the clock the kernel sustains (committed rocprof counters of
     # the current kernels; null otherwise)
@@ -1076,7 +1098,7 @@ def main(argv=None):
         roof["peak_at_sustained_clock"] = round(peak_at_clock, 1)
         roof["frac_at_sustained_clock"] = roof["achieved"] / peak_at_clock
 
-    per_m = []
+    per_m = []  # from the instrumented steps before the timed region
     for m in ms:
         t = per_call_ms[m] * 1e-3
         per_m.append({"M": m, "us": round(per_call_ms[m] * 1e3, 2), "kernel": names[m],
