@@ -115,7 +115,12 @@ bi_status_t bi_moe_create(int E, int k, int H, int I, const void *W_router, cons
 /*
  * y: fp32 [T, H] = the layer applied to x: bf16 [T, H]; 0 <= T <= max_tokens
  * (T == 0 launches nothing).  A token's row of y is a function of its row of
- * x and the weights only.  One handle runs one call at a time: its
+ * x and the weights only: the steps above, bit for bit as the step functions
+ * and bi_grouped_gemm_run compute them.  (The layer packs W_up with its gate
+ * and up rows interleaved 16 at a time; when the rows average at least 64 per
+ * expert the up projection's epilogue applies SwiGLU in registers and writes
+ * a directly.  Each product element keeps its tree and SwiGLU its arithmetic,
+ * so neither changes a bit.)  One handle runs one call at a time: its
  * workspace is shared by the calls, so calls on one handle must not overlap.
  */
 bi_status_t bi_moe_run(bi_moe_t h, const void *x, int T, float *y, void *stream);

@@ -21,8 +21,8 @@ from . import build
 SRC = os.path.join(build.CSRC, "bigemm_kernels.hip")
 # the dense kernels (8, 6, 5 and 4 x tiles per wave; the product instance and the
 # comparison path's split-K instance) and the grouped one (plain and indexed
-# rows; both block heights in one kernel), with the accumulator tiles each of
-# their epilogues reads
+# rows, and the gated projection's SwiGLU epilogue; both block heights in one
+# kernel), with the accumulator tiles each of their epilogues reads
 KERNELS = {"_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi8ELi0E": [64],
            "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi4ELi0E": [32],
            "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi8ELi1E": [64],
@@ -31,8 +31,9 @@ KERNELS = {"_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi8ELi0E": [64],
            "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi5ELi1E": [40],
            "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi6ELi0E": [48],
            "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi6ELi1E": [48],
-           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb0E": [64, 32],
-           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1E": [64, 32]}
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb0ELb0E": [64, 32],
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1ELb0E": [64, 32],
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1ELb1E": [64, 32]}
 MFMA_AGPR = re.compile(r"v_mfma_f32_16x16x32_bf16 a\[\d+:\d+\], v\[\d+:\d+\], v\[\d+:\d+\], (a\[\d+:\d+\]|0)$")
 AGPR = re.compile(r"\ba\d+\b|\ba\[\d+:\d+\]")
 

@@ -40,4 +40,23 @@ __device__ __forceinline__ uint4 rms_scale_chunk(const uint4& x, float r, const 
                  rms_scale_pair(x.w, r, g.w)};
 }
 
+// SwiGLU of one gate value g and its up value u: bf16(g / (1 + exp(-g)) * u),
+// every step in fp32 (a correctly rounded divide, the device library's expf).
+// The standalone SwiGLU kernel and the up projection that applies it in its
+// epilogue both call this, so their activations are the same bits.
+__device__ __forceinline__ uint16_t swiglu_bf16(float g, float u)
+{
+    const float sg = g / (1.0f + expf(-g));
+    return to_bf16(sg * u);
+}
+
+// Four of them, packed as four bf16 in column order (low half first).
+__device__ __forceinline__ uint2 swiglu4(const float* g, const float* u)
+{
+    uint2 p;
+    p.x = (uint32_t)swiglu_bf16(g[0], u[0]) | ((uint32_t)swiglu_bf16(g[1], u[1]) << 16);
+    p.y = (uint32_t)swiglu_bf16(g[2], u[2]) | ((uint32_t)swiglu_bf16(g[3], u[3]) << 16);
+    return p;
+}
+
 }  // namespace bi

@@ -361,7 +361,7 @@ bi_gemm* handle_of(bi_gemm_t h)
 }
 
 bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info* forced,
-                          bi_gemm_t* out)
+                          bi_gemm_t* out, int gated_i = 0)
 {
     if (!out)
         return fail(BI_ERR_INVALID_ARGUMENT, "out is NULL");
@@ -449,7 +449,7 @@ bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info*
         return fail(BI_ERR_OUT_OF_MEMORY, "out of device memory for the packed weights (" +
                                               std::to_string(wbytes) + " bytes)");
     }
-    he = bigemm::pack_weights(W, packed, E, N, K, nullptr);
+    he = bigemm::pack_weights(W, packed, E, N, K, nullptr, gated_i);
     if (he == hipSuccess)
         he = hipStreamSynchronize(nullptr);
     if (he != hipSuccess) {
@@ -499,6 +499,7 @@ bi_status_t create_common(int E, int N, int K, const void* W, const bi_pin_info*
     }
     h->plan.split_ws = static_cast<float*>(split_ws);
     h->plan.split_ws_rows = ws_rows;
+    h->plan.gated_i = gated_i;
     bi_pin_info& p = h->pin;
     std::memset(&p, 0, sizeof p);
     p.n = N;
@@ -745,21 +746,26 @@ const char* bi_rmsnorm_gemm_kernel_name(bi_gemm_t hh, int M)
 
 namespace {
 
+// y: the product (fp32 [R, N]); or, for a gated handle, a: the product with
+// SwiGLU applied (bf16 [R, N / 2]), y then NULL.
 bi_status_t grouped_run(bi_gemm_t hh, const void* x, int xn, const int32_t* xidx, const int32_t* expert_offsets,
-                        int R, float* y, void* stream)
+                        int R, float* y, void* stream, void* a = nullptr)
 {
     bi_gemm* h = handle_of(hh);
     if (!h)
         return fail(BI_ERR_INVALID_ARGUMENT, "invalid handle");
     if (h->plan.experts == 0)
         return fail(BI_ERR_INVALID_ARGUMENT, "dense handle passed to bi_grouped_gemm_run");
+    if (a && (h->plan.gated_i == 0 || !bigemm::grouped_swiglu_fits(h->plan, R)))
+        return fail(BI_ERR_INVALID_ARGUMENT, "the fused SwiGLU needs a gated handle and a call it fits");
     if (R < 0)
         return fail(BI_ERR_INVALID_ARGUMENT, "R must be >= 0");
     if (R == 0)
         return BI_OK;
-    if (!x || !y || !expert_offsets)
+    void* out = a ? a : static_cast<void*>(y);
+    if (!x || !out || !expert_offsets)
         return fail(BI_ERR_INVALID_ARGUMENT, "x, y or expert_offsets is NULL");
-    if (!aligned16(x) || !aligned16(y))
+    if (!aligned16(x) || !aligned16(out))
         return fail(BI_ERR_MISALIGNED, "x and y must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(expert_offsets) & 3u) != 0)
         return fail(BI_ERR_MISALIGNED, "expert_offsets must be 4-byte aligned");
@@ -775,8 +781,10 @@ bi_status_t grouped_run(bi_gemm_t hh, const void* x, int xn, const int32_t* xidx
     bi_status_t st = check_run_device(h);
     if (st != BI_OK)
         return st;
-    hipError_t e = bigemm::launch_grouped(h->plan, h->W, x, expert_offsets, R, y, xidx, xn,
-                                          static_cast<hipStream_t>(stream));
+    hipError_t e = a ? bigemm::launch_grouped_swiglu(h->plan, h->W, x, expert_offsets, R, a, xidx, xn,
+                                                     static_cast<hipStream_t>(stream))
+                     : bigemm::launch_grouped(h->plan, h->W, x, expert_offsets, R, y, xidx, xn,
+                                              static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(BI_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return BI_OK;
@@ -797,6 +805,7 @@ bi_status_t bi_grouped_gemm_run_indexed(bi_gemm_t hh, const void* x, int x_rows,
         return fail(BI_ERR_INVALID_ARGUMENT, "row_index is NULL");
     return grouped_run(hh, x, x_rows, R > 0 ? row_index : nullptr, expert_offsets, R, y, stream);
 }
+
 
 void bi_gemm_destroy(bi_gemm_t hh)
 {
@@ -860,3 +869,34 @@ const char* bi_status_string(bi_status_t s)
 const char* bi_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"
+
+namespace bigemm {
+
+bi_status_t create_gated(int E, int I, int K, const void* W, bi_gemm_t* out)
+{
+    if (E <= 0 || I <= 0 || I % 16 != 0 || (long long)E * 2 * I * K >= (1LL << 40)) {
+        if (out)
+            *out = nullptr;
+        return fail(BI_ERR_INVALID_ARGUMENT, "gated up projection: need E >= 1, I a multiple of 16");
+    }
+    return create_common(E, 2 * I, K, W, nullptr, out, I);
+}
+
+bool swiglu_fits(bi_gemm_t hh, int R)
+{
+    bi_gemm* h = handle_of(hh);
+    return h && h->plan.gated_i > 0 && grouped_swiglu_fits(h->plan, R);
+}
+
+bi_status_t run_swiglu_indexed(bi_gemm_t hh, const void* x, int x_rows, const int32_t* row_index,
+                               const int32_t* expert_offsets, int R, void* a, void* stream)
+{
+    if (R > 0 && !row_index)
+        return fail(BI_ERR_INVALID_ARGUMENT, "row_index is NULL");
+    if (R > 0 && !a)
+        return fail(BI_ERR_INVALID_ARGUMENT, "a is NULL");
+    return grouped_run(hh, x, x_rows, R > 0 ? row_index : nullptr, expert_offsets, R, nullptr, stream, a);
+}
+
+}  // namespace bigemm
+

@@ -37,6 +37,9 @@ struct Plan {
     int tile_kernel[BI_MAX_TILINGS];  // kind, | BI_KERNEL_CONCURRENT_SPLITS
     float* split_ws;       // (splits-1) * split_ws_rows * n fp32, or null
     int split_ws_rows;
+    int gated_i;           // grouped, gated (the MoE layer's up projection):
+                           // n = 2 gated_i and W's rows packed 16 gate rows,
+                           // then their 16 up rows (pack_weights); 0 otherwise
 };
 
 // The dense kernels `run` may launch; M picks one, the tree is the same.
@@ -78,7 +81,8 @@ bi_status_t api_device(int* dev, int* num_cus);
 // Launchers (bigemm_kernels.hip).  They assume validated arguments.  The
 // weights they take are packed by pack_weights: slab-major, element (n, k)
 // of an [N, K] matrix at index (k / 64) * 64N + 64n + k % 64.
-hipError_t pack_weights(const void* W, void* packed, int E, int N, int K, hipStream_t stream);
+// gated_i > 0: the gate/up row interleave of a gated up projection (Plan).
+hipError_t pack_weights(const void* W, void* packed, int E, int N, int K, hipStream_t stream, int gated_i = 0);
 hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, float* y,
                         hipStream_t stream);
 // Non-invariant comparison: kernel `kind` over `splits` concurrent K splits,
@@ -95,5 +99,23 @@ const char* dense_norm_kernel_name(const Plan& p, int M);
 hipError_t launch_grouped(const Plan& p, const void* W, const void* x,
                           const int32_t* offsets, int R, float* y, const int32_t* xidx, int xn,
                           hipStream_t stream);
+// A gated handle's product with SwiGLU in the four-wave kernel's epilogue:
+// a [R, gated_i] bf16, a[r][c] = swiglu_bf16(gate, up) of the row's product
+// columns c and gated_i + c.  Only when grouped_swiglu_fits (one split, and
+// R large enough that every expert runs in the four-wave kernel).
+bool grouped_swiglu_fits(const Plan& p, int R);
+hipError_t launch_grouped_swiglu(const Plan& p, const void* W, const void* x, const int32_t* offsets, int R,
+                                 void* a, const int32_t* xidx, int xn, hipStream_t stream);
+
+// The MoE layer's gated up projection (bigemm_api.cpp): a grouped handle over
+// W [E, 2I, K] (gate rows 0..I-1, up rows I..2I-1) whose weights are packed
+// with the gate/up row interleave, so that its product columns come out
+// interleaved the same way (16 gate columns, then their 16 up columns;
+// bi_grouped_gemm_run and _run_indexed work on it as on any grouped handle),
+// and its product with SwiGLU applied (a [R, I] bf16) when the call fits.
+bi_status_t create_gated(int E, int I, int K, const void* W, bi_gemm_t* out);
+bool swiglu_fits(bi_gemm_t h, int R);
+bi_status_t run_swiglu_indexed(bi_gemm_t h, const void* x, int x_rows, const int32_t* row_index,
+                               const int32_t* expert_offsets, int R, void* a, void* stream);
 
 }  // namespace bigemm

@@ -714,7 +714,11 @@ constexpr int tiled4_read_at(int T)
     return -1;
 }
 
-template <int XT, bool kIdx = false>
+// kSwiGLU: W is a gated projection packed with the gate/up row interleave
+// (bigemm_pack_w), so W tiles 2t and 2t+1 of a wave hold 16 gate columns and
+// their up columns; the epilogue writes bf16 SwiGLU of each pair, a
+// [rows, N / 2] bf16 at y, instead of the fp32 product.
+template <int XT, bool kIdx = false, bool kSwiGLU = false>
 __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restrict__ x,
                                               const uint16_t* __restrict__ Wb, float* __restrict__ y, int m0,
                                               int row_hi, int n0, int N, int K, Split sp,
@@ -848,15 +852,35 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
 
     // x tile j outer, W tile i inner: the two 64-byte halves of a 128-byte
     // line of y (tiles i and i+1 of one row) are stored back to back
-    for_each_t([&](auto uc) {
-        constexpr int U = decltype(uc)::value;
-        constexpr int j = U / 8, i = U % 8, T = XT * i + j;
-        const int m = m0 + wm * 16 * XT + j * 16 + (lane & 15);
-        const int n = n0 + wn * 128 + i * 16 + 4 * (lane >> 4);
-        const f32x4 v = read_agpr_tile<T>();
-        if (m < row_hi && n < N)
-            emit4(y + (size_t)m * N + n, v, sp.fold);
-    }, std::make_integer_sequence<int, kT>{});
+    if constexpr (kSwiGLU) {
+        // tiles i (gate) and i+1 (up) of x tile j: 4 columns of a row per
+        // lane, gate column c = (row of tile i) / 2 within the 32-row group
+        const int half = N / 2;
+        uint16_t* a = reinterpret_cast<uint16_t*>(y);
+        for_each_t([&](auto uc) {
+            constexpr int U = decltype(uc)::value;
+            constexpr int j = U / 4, i = 2 * (U % 4);
+            const int m = m0 + wm * 16 * XT + j * 16 + (lane & 15);
+            const int c = (n0 + wn * 128 + i * 16) / 2 + 4 * (lane >> 4);
+            const f32x4 g = read_agpr_tile<XT * i + j>();
+            const f32x4 u = read_agpr_tile<XT * (i + 1) + j>();
+            if (m < row_hi && c < half) {
+                const float gg[4] = {g[0], g[1], g[2], g[3]};
+                const float uu[4] = {u[0], u[1], u[2], u[3]};
+                *reinterpret_cast<uint2*>(a + (size_t)m * half + c) = bi::swiglu4(gg, uu);
+            }
+        }, std::make_integer_sequence<int, kT / 2>{});
+    } else {
+        for_each_t([&](auto uc) {
+            constexpr int U = decltype(uc)::value;
+            constexpr int j = U / 8, i = U % 8, T = XT * i + j;
+            const int m = m0 + wm * 16 * XT + j * 16 + (lane & 15);
+            const int n = n0 + wn * 128 + i * 16 + 4 * (lane >> 4);
+            const f32x4 v = read_agpr_tile<T>();
+            if (m < row_hi && n < N)
+                emit4(y + (size_t)m * N + n, v, sp.fold);
+        }, std::make_integer_sequence<int, kT>{});
+    }
 }
 
 // (32 XT) x 256 output blocks, one per workgroup.
@@ -876,7 +900,8 @@ __global__ void __launch_bounds__(256)
 // than cmin rows, by 256 W rows; a block of at most 128 rows runs as a
 // 128x256 block.  The tiles are cut into 8 contiguous ranges, one per XCD,
 // as in bigemm_tiled_grouped.  kIdx: x rows are read through xidx.
-template <bool kIdx>
+// kSwiGLU: a gated projection's SwiGLU, bf16 [R, N / 2] at y (tiled4_block).
+template <bool kIdx, bool kSwiGLU = false>
 __global__ void __launch_bounds__(256)
     bigemm_tiled4_grouped(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ y,
                           const int32_t* __restrict__ off, int E, int R, int N, int K, Split sp, int tiles_n,
@@ -892,9 +917,11 @@ __global__ void __launch_bounds__(256)
         const int e = big_slot(off, E, R, cmin, t / tiles_n, &m0, &hi);
         barrier_after_lds_reads();  // every wave is done with the previous tile's stages
         if (hi - m0 <= 128)
-            tiled4_block<4, kIdx>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K, sp, xidx, xn);
+            tiled4_block<4, kIdx, kSwiGLU>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K, sp,
+                                           xidx, xn);
         else
-            tiled4_block<8, kIdx>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K, sp, xidx, xn);
+            tiled4_block<8, kIdx, kSwiGLU>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K, sp,
+                                           xidx, xn);
     }
 }
 
@@ -1371,10 +1398,18 @@ hipError_t run_tiled_grouped(const void* W, const void* x, const int32_t* off, i
 // per CU (its LDS holds one), a multiple of 8.
 hipError_t run_tiled4_grouped(const void* W, const void* x, const int32_t* off, int E, int R, float* y, int N,
                               int K, Split sp, int cmin, int num_cus, const int32_t* xidx, int xn,
-                              hipStream_t stream)
+                              hipStream_t stream, bool swiglu = false)
 {
     const int tiles_n = (N + 255) / 256;
     const int grid = (num_cus + 7) / 8 * 8;
+    if (swiglu) {  // the MoE layer's gated up projection: rows always indexed
+        if (!xidx)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL((bigemm_tiled4_grouped<true, true>), dim3(grid), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, off, E, R, N, K,
+                           sp, tiles_n, cmin, xidx, xn);
+        return hipGetLastError();
+    }
     if (xidx)
         hipLaunchKernelGGL(bigemm_tiled4_grouped<true>, dim3(grid), dim3(256), 0, stream,
                            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, off, E, R, N, K,
@@ -1406,8 +1441,11 @@ constexpr TileShape kTileShapes[] = {
 // W [E][N][K] row-major -> the packed slab-major layout, 16 bytes per
 // thread and step; a bitwise copy.  Thread v reads unit v of W (row n, the 8
 // values from k = 8c) and writes it where the packed layout puts (n, 8c).
+// gated_i > 0 (N = 2 gated_i: gate rows, then up rows): packed row n holds,
+// for n % 32 < 16, gate row 16 (n / 32) + n % 32, else the up row 16 after
+// it, so that a 32-row group holds 16 gate columns and their up columns.
 __global__ void __launch_bounds__(256)
-    bigemm_pack_w(const uint4* __restrict__ W, uint4* __restrict__ P, int N, int K, long long units)
+    bigemm_pack_w(const uint4* __restrict__ W, uint4* __restrict__ P, int N, int K, long long units, int gated_i)
 {
     const long long per = (long long)N * K / 8;  // units per expert
     const int rowu = K / 8;                      // units per W row
@@ -1415,19 +1453,24 @@ __global__ void __launch_bounds__(256)
          v += (long long)gridDim.x * blockDim.x) {
         const long long e = v / per;
         const long long w = v - e * per;
-        const int n = (int)(w / rowu), c = (int)(w % rowu);
+        int n = (int)(w / rowu);
+        const int c = (int)(w % rowu);
+        if (gated_i > 0) {
+            const int up = n >= gated_i, s = up ? n - gated_i : n;
+            n = 32 * (s / 16) + 16 * up + s % 16;
+        }
         P[e * per + (long long)(c / 8) * N * 8 + n * 8 + c % 8] = W[v];
     }
 }
 
 }  // namespace
 
-hipError_t pack_weights(const void* W, void* packed, int E, int N, int K, hipStream_t stream)
+hipError_t pack_weights(const void* W, void* packed, int E, int N, int K, hipStream_t stream, int gated_i)
 {
     const long long units = (long long)(E > 0 ? E : 1) * N * K / 8;
     const long long blocks = (units + 255) / 256;
     hipLaunchKernelGGL(bigemm_pack_w, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, stream,
-                       static_cast<const uint4*>(W), static_cast<uint4*>(packed), N, K, units);
+                       static_cast<const uint4*>(W), static_cast<uint4*>(packed), N, K, units, gated_i);
     return hipGetLastError();
 }
 
@@ -1611,6 +1654,22 @@ GroupedSplit grouped_split(const Plan& p, int R)
 }
 
 }  // namespace
+
+bool grouped_swiglu_fits(const Plan& p, int R)
+{
+    const GroupedSplit g = grouped_split(p, R);
+    return p.gated_i > 0 && p.splits == 1 && g.smax == 0 && g.big;
+}
+
+hipError_t launch_grouped_swiglu(const Plan& p, const void* W, const void* x, const int32_t* offsets, int R,
+                                 void* a, const int32_t* xidx, int xn, hipStream_t stream)
+{
+    if (!grouped_swiglu_fits(p, R))
+        return hipErrorInvalidValue;
+    // one split, no streaming experts: every expert, whole, in the four-wave kernel
+    return run_tiled4_grouped(W, x, offsets, p.experts, R, static_cast<float*>(a), p.n, p.k, Split{0, p.k, 0}, 0,
+                              p.num_cus, xidx, xn, stream, true);
+}
 
 const char* grouped_kernel_name(const Plan& p, int R)
 {

@@ -242,7 +242,7 @@ bi_status_t bi_moe_create(int E, int k, int H, int I, const void* W_router, cons
     m->I = I;
     m->max_tokens = max_tokens;
     if ((st = bi_gemm_create(E, H, W_router, &m->router)) != BI_OK ||
-        (st = bi_grouped_gemm_create(E, 2 * I, H, W_up, &m->up)) != BI_OK ||
+        (st = bigemm::create_gated(E, I, H, W_up, &m->up)) != BI_OK ||
         (st = bi_grouped_gemm_create(E, H, I, W_down, &m->down)) != BI_OK) {
         release(m);
         return st;
@@ -317,11 +317,19 @@ bi_status_t bi_moe_run(bi_moe_t hh, const void* x, int T, float* y, void* stream
         return st;
     if ((st = launched(bimoe::launch_permute(m->ids, T, m->E, m->k, m->offsets, m->tok, m->row_of, s))) != BI_OK)
         return st;
-    // the up projection reads each row's token straight from x (no gathered copy)
-    if ((st = bi_grouped_gemm_run_indexed(m->up, x, T, m->tok, m->offsets, R, m->h, stream)) != BI_OK)
-        return st;
-    if ((st = launched(bimoe::launch_swiglu(m->h, R, m->I, m->a, s))) != BI_OK)
-        return st;
+    // the up projection reads each row's token straight from x (no gathered
+    // copy); its weights are packed gate/up interleaved, so that when every
+    // expert runs in the four-wave kernel its epilogue applies SwiGLU and
+    // writes a directly (same bits as the product then the SwiGLU kernel)
+    if (bigemm::swiglu_fits(m->up, R)) {
+        if ((st = bigemm::run_swiglu_indexed(m->up, x, T, m->tok, m->offsets, R, m->a, stream)) != BI_OK)
+            return st;
+    } else {
+        if ((st = bi_grouped_gemm_run_indexed(m->up, x, T, m->tok, m->offsets, R, m->h, stream)) != BI_OK)
+            return st;
+        if ((st = launched(bimoe::launch_swiglu(m->h, R, m->I, m->a, s, true))) != BI_OK)
+            return st;
+    }
     if ((st = bi_grouped_gemm_run(m->down, m->a, m->offsets, R, m->o, stream)) != BI_OK)
         return st;
     return launched(bimoe::launch_combine(m->o, R, m->ids, m->w, m->row_of, T, m->k, m->H, y, s));

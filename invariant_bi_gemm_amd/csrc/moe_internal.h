@@ -18,7 +18,9 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offs
                           int32_t* row_of, hipStream_t stream);
 hipError_t launch_gather(const void* src, int nsrc, const int32_t* idx, int R, int K, void* dst,
                          hipStream_t stream);
-hipError_t launch_swiglu(const float* h, int R, int I, void* a, hipStream_t stream);
+// interleaved: h's columns as the layer's gated up projection leaves them
+// (16 gate columns, then their 16 up columns, and so on)
+hipError_t launch_swiglu(const float* h, int R, int I, void* a, hipStream_t stream, bool interleaved = false);
 hipError_t launch_combine(const float* o, int R, const int32_t* ids, const float* w,
                           const int32_t* row_of, int T, int k, int H, float* y, hipStream_t stream);
 

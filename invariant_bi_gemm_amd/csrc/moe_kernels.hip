@@ -265,9 +265,13 @@ __global__ void __launch_bounds__(256)
 }
 
 // ---------------------------------------------------------------------------
-// SwiGLU: a[r][i] = bf16(g / (1 + exp(-g)) * u), g = h[r][i], u = h[r][I+i],
-// four columns per thread (I is a multiple of 4).
+// SwiGLU: a[r][i] = bf16(g / (1 + exp(-g)) * u) (bi::swiglu_bf16), four
+// columns per thread (I a multiple of 4; of 16 interleaved).  Plain layout: g = h[r][i],
+// u = h[r][I+i].  Interleaved layout (the MoE layer's up projection, whose
+// weight rows are packed 16 gate rows then the 16 matching up rows): g =
+// h[r][32(i/16) + i%16], u 16 columns after it.
 // ---------------------------------------------------------------------------
+template <bool kInterleaved>
 __global__ void __launch_bounds__(256)
     swiglu(const float* __restrict__ h, int R, int I, uint16_t* __restrict__ a)
 {
@@ -276,20 +280,13 @@ __global__ void __launch_bounds__(256)
     for (long long i = blockIdx.x * 256LL + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
         const int r = (int)(i / q4);
         const int c = (int)(i % q4) * 4;
-        const float4 g = *reinterpret_cast<const float4*>(h + (size_t)r * 2 * I + c);
-        const float4 u = *reinterpret_cast<const float4*>(h + (size_t)r * 2 * I + I + c);
+        const int cg = kInterleaved ? 32 * (c / 16) + c % 16 : c;
+        const int cu = kInterleaved ? cg + 16 : I + c;
+        const float4 g = *reinterpret_cast<const float4*>(h + (size_t)r * 2 * I + cg);
+        const float4 u = *reinterpret_cast<const float4*>(h + (size_t)r * 2 * I + cu);
         const float gg[4] = {g.x, g.y, g.z, g.w};
         const float uu[4] = {u.x, u.y, u.z, u.w};
-        uint16_t out[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float sg = gg[j] / (1.0f + expf(-gg[j]));
-            out[j] = bi::to_bf16(sg * uu[j]);
-        }
-        uint2 packed;
-        packed.x = (uint32_t)out[0] | ((uint32_t)out[1] << 16);
-        packed.y = (uint32_t)out[2] | ((uint32_t)out[3] << 16);
-        *reinterpret_cast<uint2*>(a + (size_t)r * I + c) = packed;
+        *reinterpret_cast<uint2*>(a + (size_t)r * I + c) = bi::swiglu4(gg, uu);
     }
 }
 
@@ -418,10 +415,13 @@ hipError_t launch_gather(const void* src, int nsrc, const int32_t* idx, int R, i
     return hipGetLastError();
 }
 
-hipError_t launch_swiglu(const float* h, int R, int I, void* a, hipStream_t stream)
+hipError_t launch_swiglu(const float* h, int R, int I, void* a, hipStream_t stream, bool interleaved)
 {
-    hipLaunchKernelGGL(swiglu, dim3(grid_for((long long)R * (I / 4), 256)), dim3(256), 0, stream, h,
-                       R, I, static_cast<uint16_t*>(a));
+    const dim3 grid(grid_for((long long)R * (I / 4), 256));
+    if (interleaved)
+        hipLaunchKernelGGL(swiglu<true>, grid, dim3(256), 0, stream, h, R, I, static_cast<uint16_t*>(a));
+    else
+        hipLaunchKernelGGL(swiglu<false>, grid, dim3(256), 0, stream, h, R, I, static_cast<uint16_t*>(a));
     return hipGetLastError();
 }
 
