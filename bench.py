@@ -124,6 +124,18 @@ def to_dev(bits):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda:0")
 
 
+def host_cpu() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), for the CPU baseline."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w_bits, x_bits, n, k, target_s=15.0):
     """The oracle, as it stands, on the host cores: rows of the same layer.
 
@@ -144,7 +156,7 @@ def cpu_baseline(w_bits, x_bits, n, k, target_s=15.0):
     oracle.gemm_f64(x_bits, w_bits, rows=idx)
     dt = time.perf_counter() - t0
     tflops = 2.0 * rows * n * k / dt / 1e12
-    return {"value": tflops, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+    return {"value": tflops, "unit": "TFLOPS", "cores": threads, "cpu": host_cpu(), "kind": "oracle",
             "sample": "fp64 oracle on %d rows (all %d columns) of the same layer, %.1f s" % (rows, n, dt)}
 
 
@@ -428,7 +440,7 @@ def moe_cpu_baseline(wbits, calls, target_s=15.0):
     oracle.grouped_f64(xb, w, offs, rows=np.arange(nrows))
     dt = time.perf_counter() - t0
     return {"value": 2.0 * nrows * n * k / dt / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(),
-            "kind": "oracle", "sample": "fp64 oracle, grouped up-projection (N=%d, K=%d), first %d of the %d "
+            "cpu": host_cpu(), "kind": "oracle", "sample": "fp64 oracle, grouped up-projection (N=%d, K=%d), first %d of the %d "
             "rows at T=%d, %.1f s" % (n, k, nrows, xb.shape[0], t, dt)}
 
 
@@ -660,7 +672,8 @@ def moe_layer_cpu_baseline(wr, wu, wd, target_s=15.0):
     chain(x[:n])
     dt = time.perf_counter() - t0
     fl = n * (2.0 * E * H + 2.0 * k * 2 * I * H + 2.0 * k * H * I)
-    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(), "kind": "oracle",
+    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(), "cpu": host_cpu(),
+            "kind": "oracle",
             "sample": "fp64 oracle steps of the layer chained on the first %d of the 4096 tokens, %.1f s" % (n, dt)}
 
 
@@ -934,7 +947,8 @@ def attn_cpu_baseline(q, k, v, st, scale, target_s=10.0):
         keys += hi - lo
         b += 1
     flops = 4.0 * keys * q.shape[1] * q.shape[2]
-    return {"value": flops / t_total / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(), "kind": "oracle",
+    return {"value": flops / t_total / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(), "cpu": host_cpu(),
+            "kind": "oracle",
             "sample": "fp64 oracle on the first %d sequences (%d keys) of the batch, %.1f s" % (b, keys, t_total)}
 
 
