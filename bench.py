@@ -440,8 +440,9 @@ def moe_cpu_baseline(wbits, calls, target_s=15.0):
     oracle.grouped_f64(xb, w, offs, rows=np.arange(nrows))
     dt = time.perf_counter() - t0
     return {"value": 2.0 * nrows * n * k / dt / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(),
-            "cpu": host_cpu(), "kind": "oracle", "sample": "fp64 oracle, grouped up-projection (N=%d, K=%d), first %d of the %d "
-            "rows at T=%d, %.1f s" % (n, k, nrows, xb.shape[0], t, dt)}
+            "cpu": host_cpu(), "kind": "oracle",
+            "sample": "fp64 oracle, grouped up-projection (N=%d, K=%d), first %d of the %d rows at T=%d, %.1f s"
+                      % (n, k, nrows, xb.shape[0], t, dt)}
 
 
 def _moe_layer_weights(seed=42):
@@ -702,7 +703,8 @@ def run_norm_gate_up(args, bg):
     raw = synth.normal_bf16(43, (mmax, k))
     scale = np.exp2(synth.rng(44).integers(-4, 5, size=(mmax, 1))).astype(np.float32)
     xraw = to_dev(synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(raw) * scale))
-    gain = to_dev(synth.f32_to_bf16_bits((1.0 + synth.bf16_bits_to_f32(synth.normal_bf16(45, (k,), 0.1))).astype(np.float32)))
+    gain_f = 1.0 + synth.bf16_bits_to_f32(synth.normal_bf16(45, (k,), 0.1))
+    gain = to_dev(synth.f32_to_bf16_bits(gain_f.astype(np.float32)))
     xn = torch.empty((mmax, k), dtype=torch.bfloat16, device="cuda:0")
     ys = {m: torch.empty((m, n), dtype=torch.float32, device="cuda:0") for m in ms}
     lib = bg.load()
@@ -817,7 +819,8 @@ def run_norm_gate_up(args, bg):
                                "W bf16 [28672,4096], M in {32,544,2080,8224}",
                    "m_sweep": ms, "weight_copies_rotated": copies, "kernel_source_sha256_16": kernel_hash()},
         "roofline": roof,
-        "norm_roofline": dict(norm_roof, kernel="rmsnorm_rows", share_of_step=round(norm_total_us / (ms_per_step * 1e3), 4)),
+        "norm_roofline": dict(norm_roof, kernel="rmsnorm_rows",
+                              share_of_step=round(norm_total_us / (ms_per_step * 1e3), 4)),
         "fused_norm_ab": fused_ab,
         "cpu_baseline": None,
         "per_m": per,
@@ -957,7 +960,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama8b_down", choices=sorted(WORKLOADS) + ["moe", "moe_layer", "norm_gate_up", "decode_attn"])
+    ap.add_argument("--workload", default="llama8b_down",
+                    choices=sorted(WORKLOADS) + ["moe", "moe_layer", "norm_gate_up", "decode_attn"])
     ap.add_argument("--rotate-gib", type=float, default=1.0,
                     help="weight copies to rotate over, in GiB (defeats the Infinity Cache)")
     ap.add_argument("--m", type=str, default=None,
