@@ -39,7 +39,8 @@ def separate(gpu, g, x, gain):
 
 
 @pytest.mark.parametrize("kind", ["stream_mb1", "tiled_64x32", "tiled_64x64", "tiled_128x64", "tiled_128x64_deep",
-                                  "tiled_128x128", "tiled_128x128_deep", "tiled4_256x256"])
+                                  "tiled_128x128", "tiled_128x128_deep", "tiled4_160x256", "tiled4_192x256",
+                                  "tiled4_256x256"])
 def test_fused_equals_norm_then_gemm(gpu, kind):
     n, k = 1024, 2048
     w = to_dev(synth.normal_bf16(400, (n, k), 0.02))

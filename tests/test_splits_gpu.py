@@ -181,7 +181,7 @@ def test_split_four_wave_kernels(gpu, m, kernel):
 
 @pytest.mark.parametrize("splits", [2, 4])
 @pytest.mark.parametrize("kind", ["stream_mb1", "tiled_64x32", "tiled_64x64", "tiled_128x128_deep", "tiled4_128x256",
-                                  "tiled4_256x256"])
+                                  "tiled4_160x256", "tiled4_192x256", "tiled4_256x256"])
 def test_concurrent_splits_same_bits(gpu, kind, splits):
     """A tiling entry that runs the tree's splits concurrently (partials in
     the handle's workspace, folded in split order) gives the bits of the same
