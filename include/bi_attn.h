@@ -58,7 +58,7 @@ typedef struct bi_attn *bi_attn_t;
  * multiple of 64 within 64 .. 16384: the pinned split stride), and the
  * largest batch and sequence length it serves (they size its workspace:
  * max_batch * Hq * ceil(max_seq_len / S) * (D + 2) floats of split partials
- * and a work list of max_batch + 1 ints, allocated here once).  1 <= max_batch, 1 <= max_seq_len <= 2^24,
+ * and a work list of max_batch + 2 ints, allocated here once).  1 <= max_batch, 1 <= max_seq_len <= 2^24,
  * and S * Hkv * D * 2 < 2^32 (one split of a kv head is addressed with 32-bit byte offsets; a split's
  * reads end at its last key, so keys past it read as zero and never outside the caches).
  * BI_ERR_INVALID_ARGUMENT otherwise.
@@ -99,7 +99,7 @@ void bi_attn_destroy(bi_attn_t h);
  * the tree, the output bits -- is exactly bi_attn_create(Hq, Hkv, D, split,
  * B, max_seq_len) followed by bi_attn_decode.  The argument rules are those
  * two calls' combined; in addition the partials must fit:
- * B * Hq * ceil(max_seq_len / split) * (D + 2) * 4 + (B + 1) * 4 <=
+ * B * Hq * ceil(max_seq_len / split) * (D + 2) * 4 + (B + 2) * 4 <=
  * BI_ATTN_NOALLOC_SCRATCH_BYTES, else BI_ERR_INVALID_ARGUMENT (before any HIP
  * call).  The array of a GPU is looked up once (hipGetSymbolAddress) on the
  * first call on that device and is shared by every call on it: calls that

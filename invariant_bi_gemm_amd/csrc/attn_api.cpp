@@ -86,7 +86,7 @@ bi_status_t bi_attn_create(int Hq, int Hkv, int D, int split, int max_batch, int
     h->max_len = max_seq_len;
     const size_t bytes_o = (size_t)entries * D * sizeof(float);
     const size_t bytes_ml = (size_t)entries * 2 * sizeof(float);
-    const size_t bytes = bytes_o + bytes_ml + (size_t)(max_batch + 1) * sizeof(int);
+    const size_t bytes = bytes_o + bytes_ml + (size_t)(max_batch + 2) * sizeof(int);
     const hipError_t e = hipMalloc(&h->mem, bytes);
     if (e != hipSuccess) {
         delete h;
@@ -201,13 +201,13 @@ bi_status_t bi_attn_decode_noalloc(int Hq, int Hkv, int D, int split, int max_se
         return api_fail(BI_ERR_INVALID_ARGUMENT, "scale must be finite");
     const long long splits = (max_seq_len + (long long)split - 1) / split;
     const long long entries = (long long)B * Hq * splits;
-    const long long need = entries * (D + 2) * (long long)sizeof(float) + (long long)(B + 1) * (long long)sizeof(int);
+    const long long need = entries * (D + 2) * (long long)sizeof(float) + (long long)(B + 2) * (long long)sizeof(int);
     if (need > (long long)BI_ATTN_NOALLOC_SCRATCH_BYTES)
         return api_fail(BI_ERR_INVALID_ARGUMENT,
                         ("the split partials need " + std::to_string(need) + " bytes, beyond the " +
                          std::to_string((long long)BI_ATTN_NOALLOC_SCRATCH_BYTES) +
                          "-byte scratch of the allocation-free entry point (B * Hq * ceil(max_seq_len / split) "
-                         "* (D + 2) * 4 + (B + 1) * 4)").c_str());
+                         "* (D + 2) * 4 + (B + 2) * 4)").c_str());
     if (B == 0)
         return BI_OK;
     if (!q || !seq_start || !out || (Ntok > 0 && (!k || !v)))

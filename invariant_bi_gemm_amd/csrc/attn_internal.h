@@ -10,7 +10,8 @@ namespace biattn {
 constexpr int kHeadDim = 128;
 
 // Split partials: o [B][Hq][splits][D] and (m, l) [B][Hq][splits][2], fp32;
-// plan [max_batch + 1]: each sequence's first work item.
+// plan [max_batch + 2]: each sequence's first work item, the number of
+// items, and the work queue's counter.
 struct Workspace {
     float* o;
     float* ml;

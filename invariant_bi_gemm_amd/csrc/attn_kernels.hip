@@ -108,7 +108,8 @@ __device__ __forceinline__ int seq_len(const int32_t* __restrict__ seq_start, in
 }
 
 // The work list: plan[b] = splits of the sequences before b, plan[B] = all
-// splits.  One block of 1024 threads, 1024 sequences at a time: a wave
+// splits, and plan[B + 1] = 0, the counter the split kernel's blocks take
+// work items from.  One block of 1024 threads, 1024 sequences at a time: a wave
 // scan, then the 16 wave totals in order.
 constexpr int kPlanThreads = 1024;
 
@@ -140,13 +141,19 @@ __global__ void __launch_bounds__(kPlanThreads)
             carry += s_w[w];
         __syncthreads();
     }
-    if (tid == 0)
+    if (tid == 0) {
         plan[B] = carry;
+        plan[B + 1] = 0;
+    }
 }
 
-// Persistent: the blocks walk the work items (split, kv head) of all
-// sequences in the order of the plan, kv heads fastest, so that the Hkv
-// blocks of one split read whole token rows together.  G query heads share
+// Persistent: the blocks take the work items (split, kv head) of all
+// sequences from a counter (queue), in the order of the plan, kv heads
+// fastest, so that the Hkv blocks of one split read whole token rows
+// together, and a block that finishes early takes the next item: the splits
+// are ragged (a sequence's last one is partial), and a fixed share per block
+// would leave the kernel waiting on the blocks dealt the most keys.  Which
+// block computes an item changes no bit: each item writes its own partials.  G query heads share
 // the kv head.
 // One pass over the split's keys: each 16-lane group keeps, per head, a
 // running max m, sum l and weighted sum o of its keys (flash-decoding's
@@ -156,17 +163,26 @@ __global__ void __launch_bounds__(kPlanThreads)
 template <int G>
 __global__ void __launch_bounds__(kThreads)
     attn_split(const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
-               const int32_t* __restrict__ seq_start, const int* __restrict__ plan, int B, int Hkv, int S,
-               int max_len, int Ntok, float scale_l2, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-               int splits)
+               const int32_t* __restrict__ seq_start, const int* __restrict__ plan, int* __restrict__ queue,
+               int B, int Hkv, int S, int max_len, int Ntok, float scale_l2, float* __restrict__ ws_o,
+               float* __restrict__ ws_ml, int splits)
 {
     __shared__ float s_m[4][G];
     __shared__ float s_l[4][G];
     __shared__ float s_o[4][G][kHeadDim];
+    __shared__ int s_item;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = wave * 4 + (lane >> 4), r = lane & 15;
     const int items = plan[B] * Hkv;
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    for (;;) {
+    if (tid == 0)
+        s_item = atomicAdd(queue, 1);
+    __syncthreads();
+    // every thread reads the same value: kept uniform, so that the buffer
+    // descriptors built from the item stay in scalar registers
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
+    if (item >= items)
+        break;
     const int kvh = item % Hkv, pair = item / Hkv;
     int lo = 0, hi = B;  // the sequence: the last b with plan[b] <= pair
     while (hi - lo > 1) {
@@ -380,7 +396,8 @@ hipError_t launch_g(const void* q, const void* k, const void* v, const int32_t* 
     }();
     hipLaunchKernelGGL(attn_split<G>, dim3(ws.num_cus * per_cu), dim3(kThreads), 0, stream,
                        static_cast<const uint4*>(q), static_cast<const uint4*>(k), static_cast<const uint4*>(v),
-                       seq_start, ws.plan, B, Hkv, S, max_len, Ntok, scale_l2, ws.o, ws.ml, ws.splits);
+                       seq_start, ws.plan, ws.plan + B + 1, B, Hkv, S, max_len, Ntok, scale_l2, ws.o, ws.ml,
+                       ws.splits);
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
