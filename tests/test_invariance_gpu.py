@@ -176,7 +176,7 @@ def test_offset_view_of_x(gpu):
 def test_every_kernel_configuration(gpu):
     """One layer through every kernel the dispatcher can pick (streaming with
     1, 2 and 4 m-tiles; tiled 64x32, 64x64, 128x64 and 128x128 in both
-    depths, 128x256 and 256x256): probe rows of each call equal the rows alone, and the values
+    depths; four-wave 128x256, 160x256, 192x256 and 256x256): probe rows of each call equal the rows alone, and the values
     pass the oracle bound."""
     import oracle
     from gpu_util import assert_parity
