@@ -490,7 +490,7 @@ def run_moe_layer(args, bg):
     experts for the next call of the same T.  A second pass runs the steps
     one by one through their own entry points (the same bits) with events
     around each, for the per-kernel breakdown and roofline.  Where the layer
-    applies SwiGLU in the up projection's epilogue (T = 4096 here), that pass
+    applies SwiGLU in the up projection's epilogue (T = 256 and 4096 here), that pass
     times the up projection and SwiGLU as the two separate calls."""
     import ctypes
 
@@ -586,7 +586,7 @@ def run_moe_layer(args, bg):
         "per_T": per,
         "steps_breakdown": breakdown,
         "breakdown_note": "steps through their own entry points; the layer itself runs the up projection and "
-                          "SwiGLU as one kernel when the rows average 64 or more per expert (T = 4096 here)",
+                          "SwiGLU as one kernel when the rows average 16 or more per expert (T = 256 and 4096 here)",
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -111,7 +111,7 @@ typedef struct bi_pin_info {
     int32_t fold;                 /* 0: in-order left fold in fp32 RNE           */
     int32_t stream_max_m;         /* tiling: a grouped call streams the experts
                                      with at most min(this, 16) rows, unless its
-                                     experts average 64 rows or more (then the
+                                     experts average 16 rows or more (then the
                                      four-wave kernel takes them all); a dense
                                      call without a tiling list streams calls
                                      with at most this many rows                */

@@ -117,7 +117,7 @@ bi_status_t bi_moe_create(int E, int k, int H, int I, const void *W_router, cons
  * (T == 0 launches nothing).  A token's row of y is a function of its row of
  * x and the weights only: the steps above, bit for bit as the step functions
  * and bi_grouped_gemm_run compute them.  (The layer packs W_up with its gate
- * and up rows interleaved 16 at a time; when the rows average at least 64 per
+ * and up rows interleaved 16 at a time; when the rows average at least 16 per
  * expert the up projection's epilogue applies SwiGLU in registers and writes
  * a directly.  Each product element keeps its tree and SwiGLU its arithmetic,
  * so neither changes a bit.)  One handle runs one call at a time: its

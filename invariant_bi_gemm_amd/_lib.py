@@ -336,6 +336,10 @@ class GroupedGemm:
         check(self._lib.bi_gemm_get_pin(self._h, ctypes.byref(info)))
         return info.as_dict()
 
+    def kernel_name(self, rows: int) -> str:
+        """The kernels a call with ``rows`` rows in all launches (no launch)."""
+        return self._lib.bi_gemm_kernel_name(self._h, int(rows)).decode()
+
     def __call__(self, x, expert_offsets, out=None, stream=None):
         import torch
 

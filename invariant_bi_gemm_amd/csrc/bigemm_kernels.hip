@@ -1631,24 +1631,25 @@ hipError_t launch_dense(const Plan& p, const void* W, const void* x, int M, floa
 namespace {
 
 // How a grouped call with R rows splits its experts between the kernels,
-// decided on the host from R and E alone.  Experts with 1..smax rows go to
-// the streaming kernel; the others to the four-wave kernel when the experts
-// average 16 rows or more (big), else to the tiled kernel.  All realise the
-// same tree, so the split points only move work, never bits.  When the
-// experts average 64 rows or more, few have 16 or fewer: the four-wave
-// kernel takes those too (as 128-row blocks), which saves the streaming
-// launch (about 4 us when it finds no work).
+// decided on the host from R and E alone.  When the experts average 16 rows
+// or more (big), the four-wave kernel takes every expert, the short ones as
+// 128-row blocks: one launch that streams each expert's weights once, faster
+// than streaming the experts with 16 or fewer rows beside it (on 128 experts
+// averaging 16 rows, 8-15% less time than the two launches).  Below
+// that, experts with 1..smax rows go to the streaming kernel and the others
+// to the tiled kernel.  All realise the same tree, so the split points only
+// move work, never bits.
 struct GroupedSplit {
     int smax;  // rows at or below which an expert streams (0: no streaming launch)
-    bool big;  // the four-wave kernel takes every other expert
+    bool big;  // the four-wave kernel takes every expert
     bool tiled_launch;  // the tiled kernel is launched (it returns at once when R <= smax)
 };
 
 GroupedSplit grouped_split(const Plan& p, int R)
 {
     GroupedSplit g;
-    g.smax = R >= 64 * p.experts ? 0 : (p.stream_max_m < 16 ? p.stream_max_m : 16);
     g.big = R >= 128 && R >= 16 * p.experts;
+    g.smax = g.big ? 0 : (p.stream_max_m < 16 ? p.stream_max_m : 16);
     g.tiled_launch = !g.big && R > g.smax;
     return g;
 }
@@ -1674,12 +1675,11 @@ hipError_t launch_grouped_swiglu(const Plan& p, const void* W, const void* x, co
 const char* grouped_kernel_name(const Plan& p, int R)
 {
     const GroupedSplit g = grouped_split(p, R);
-    if (g.smax > 0) {
-        if (g.big)
-            return "bigemm_stream_grouped+bigemm_tiled4_grouped";
+    if (g.big)
+        return "bigemm_tiled4_grouped";
+    if (g.smax > 0)
         return g.tiled_launch ? "bigemm_stream_grouped+bigemm_tiled_grouped<128x128>" : "bigemm_stream_grouped";
-    }
-    return g.big ? "bigemm_tiled4_grouped" : "bigemm_tiled_grouped<128x128>";
+    return "bigemm_tiled_grouped<128x128>";
 }
 
 // The kernels that can normalise their x tiles: the tiled ones with at
@@ -1765,7 +1765,7 @@ hipError_t launch_grouped(const Plan& p, const void* W, const void* x, const int
         // few others fill a 128-row block poorly, so the tiled kernel's
         // 128x128 tiles serve them
         const int big = g.big ? 256 : 0;
-        if (big)  // every expert above the streaming threshold, whole
+        if (big)  // every expert, whole (smax is 0 here)
             err = run_tiled4_grouped(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, p.num_cus, xidx, xn, stream);
         else
             err = run_tiled_grouped<128, 128, 2, 4, 64, 2>(W, x, offsets, p.experts, R, y, p.n, p.k, sp, smax, big,

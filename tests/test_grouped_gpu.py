@@ -68,9 +68,11 @@ def test_moe_parity_and_invariance(gpu, experts, name, tokens):
 
 @pytest.mark.parametrize("huge", [1500, 2000])
 def test_uneven_groups_cross_paths(gpu, experts, huge):
-    """Row counts 0, 1, 15, 16, 17, 300 and one huge expert: the streaming
-    kernel and, below 16 rows per expert on average (huge = 1500), the tiled
-    kernel, above it (huge = 2000) the four-wave kernel, in one call."""
+    """Row counts 0, 1, 15, 16, 17, 300 and one huge expert.  Below 16 rows
+    per expert on average (huge = 1500) the streaming kernel takes the
+    experts with 16 or fewer rows and the tiled kernel the others, in one
+    call; above it (huge = 2000) the four-wave kernel takes every expert,
+    the short ones as 128-row blocks."""
     n, k = SHAPES["down"]
     w, wd = experts["down"]
     g = gpu.GroupedGemm(wd)
@@ -80,6 +82,8 @@ def test_uneven_groups_cross_paths(gpu, experts, huge):
     off = np.zeros(E + 1, np.int32)
     off[1:] = np.cumsum(counts)
     r = int(off[-1])
+    assert g.kernel_name(r) == ("bigemm_tiled4_grouped" if huge == 2000 else
+                                "bigemm_stream_grouped+bigemm_tiled_grouped<128x128>")
     x = synth.normal_bf16(170, (r, k))
     y = g(to_dev(x), torch.as_tensor(off, device=DEV))
     torch.cuda.synchronize()
@@ -142,9 +146,9 @@ def test_block_boundaries_every_row_equals_dense(gpu, experts, name):
     (127 .. 640 rows, a 3000-row one) and small experts (1, 16, 17 rows):
     rows at every block edge equal the dense rows of their expert, bit
     for bit, for plain and (up) indexed rows; sampled rows pass the oracle.
-    The call has R = 8501 >= 64 E rows, so the four-wave kernel takes every
+    The call has R = 8501 >= 16 E rows, so the four-wave kernel takes every
     expert here, the small ones as 128-row blocks (no streaming launch);
-    test_uneven_groups_cross_paths puts streamed experts next to four-wave
+    test_uneven_groups_cross_paths puts streamed experts next to tiled
     ones."""
     n, k = SHAPES[name]
     w, wd = experts[name]
@@ -155,7 +159,7 @@ def test_block_boundaries_every_row_equals_dense(gpu, experts, name):
     off = np.zeros(E + 1, np.int32)
     off[1:] = np.cumsum(counts)
     r = int(off[-1])
-    assert r >= 16 * E  # the four-wave kernel takes part
+    assert r >= 16 * E and g.kernel_name(r) == "bigemm_tiled4_grouped"  # every expert
     x = synth.normal_bf16(190 + k, (r, k))
     offd = torch.as_tensor(off, device=DEV)
     y = g(to_dev(x), offd)

@@ -403,9 +403,10 @@ def test_layer_parity(gpu, layer, tokens):
     assert rel <= 2.0 ** -12, "layer T=%d: median error %.3e of the rms" % (tokens, rel)
 
 
-# 1023 and 1024 tokens sit either side of 64 rows per expert (8 rows a token,
-# 128 experts), where the up projection starts applying SwiGLU in its epilogue
-@pytest.mark.parametrize("tokens", [7, 256, 1023, 1024, 4096])
+# 255 and 256 tokens sit either side of 16 rows per expert (8 rows a token,
+# 128 experts), where the four-wave kernel takes every expert and the up
+# projection starts applying SwiGLU in its epilogue
+@pytest.mark.parametrize("tokens", [7, 255, 256, 1024, 4096])
 def test_layer_equals_its_steps(gpu, layer, tokens):
     x = to_dev(synth.normal_bf16(400 + tokens, (tokens, H)))
     y = bits32(layer["layer"](x))

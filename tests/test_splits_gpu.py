@@ -125,8 +125,8 @@ def test_grouped_uses_the_dense_split_tree(gpu, tmp_path):
 
 def test_grouped_big_blocks_use_the_dense_split_tree(gpu, tmp_path):
     """With an S = 2 pin and experts of 2 .. 700 rows (256-row blocks of the
-    four-wave kernel, remainders, streaming rows), every row equals the dense
-    S = 2 result of its expert."""
+    four-wave kernel, remainders and short experts as 128-row blocks), every
+    row equals the dense S = 2 result of its expert."""
     import invariant_bi_gemm_amd as bg
 
     e, n, k = 8, 256, 1024
@@ -142,7 +142,7 @@ def test_grouped_big_blocks_use_the_dense_split_tree(gpu, tmp_path):
         counts = np.array([300, 0, 700, 129, 2, 0, 256, 5])
         off = np.zeros(e + 1, np.int32)
         off[1:] = np.cumsum(counts)
-        assert off[-1] >= 64 * e  # the four-wave kernel takes part
+        assert off[-1] >= 16 * e and gg.kernel_name(int(off[-1])) == "bigemm_tiled4_grouped"
         x = synth.normal_bf16(223, (int(off[-1]), k))
         y = bits32(gg(to_dev(x), torch.as_tensor(off, device=DEV)))
         for ex in range(e):
