@@ -343,34 +343,76 @@ __global__ void __launch_bounds__(kThreads)
     }
 }
 
-// One (sequence, query head) per block, one thread per dimension.
-__global__ void __launch_bounds__(kHeadDim)
-    attn_combine(const int32_t* __restrict__ seq_start, int Hq, int S, int max_len, int Ntok,
+// The largest of the 64 lanes' values (fmax is exact, so the order of the
+// butterfly does not matter), in every lane.
+__device__ __forceinline__ float wave_max(float x)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        x = fmaxf(x, __shfl_xor(x, d, 64));
+    return x;
+}
+
+// One (sequence, query head) per wave, two dimensions per lane.  Lane j
+// holds split j's max and sum (64 splits at a time), so the splits' maxima
+// and weights come from one load and a butterfly; the rescaled sums then run
+// in ascending split order, four splits' partial outputs loaded together.
+constexpr int kCombineWaves = 4;
+
+__global__ void __launch_bounds__(64 * kCombineWaves)
+    attn_combine(const int32_t* __restrict__ seq_start, int BH, int Hq, int S, int max_len, int Ntok,
                  const float* __restrict__ ws_o, const float* __restrict__ ws_ml, int splits,
                  float* __restrict__ out)
 {
-    const int bh = blockIdx.x, b = bh / Hq;
-    const int dd = threadIdx.x;
+    const int bh = (int)blockIdx.x * kCombineWaves + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    if (bh >= BH)
+        return;
+    const int lane = threadIdx.x & 63;
+    const int b = bh / Hq;
     int t0;
     const int n = seq_len(seq_start, b, Ntok, max_len, &t0);
     const int ns = (n + S - 1) / S;
-    float* o = out + (size_t)bh * kHeadDim;
+    float2* o = reinterpret_cast<float2*>(out + (size_t)bh * kHeadDim) + lane;
     if (ns == 0) {
-        o[dd] = 0.f;
+        *o = make_float2(0.f, 0.f);
         return;
     }
-    const float* ml = ws_ml + (size_t)bh * splits * 2;
-    const float* po = ws_o + (size_t)bh * splits * kHeadDim;
+    const float2* ml = reinterpret_cast<const float2*>(ws_ml + (size_t)bh * splits * 2);  // (m, l) per split
+    const float2* po = reinterpret_cast<const float2*>(ws_o + (size_t)bh * splits * kHeadDim) + lane;
     float M = -INFINITY;
-    for (int jj = 0; jj < ns; ++jj)
-        M = fmaxf(M, ml[2 * jj]);
-    float O = 0.f, L = 0.f;
-    for (int jj = 0; jj < ns; ++jj) {
-        const float w = __builtin_amdgcn_exp2f(ml[2 * jj] - M);
-        O = O + w * po[(size_t)jj * kHeadDim + dd];
-        L = L + w * ml[2 * jj + 1];
+    for (int c = 0; c < ns; c += 64)
+        M = fmaxf(M, wave_max(c + lane < ns ? ml[c + lane].x : -INFINITY));
+    float ox = 0.f, oy = 0.f, L = 0.f;
+    for (int c = 0; c < ns; c += 64) {
+        float wj = 0.f, lj = 0.f;
+        if (c + lane < ns) {
+            const float2 mlj = ml[c + lane];
+            wj = __builtin_amdgcn_exp2f(mlj.x - M);
+            lj = mlj.y;
+        }
+        // split c + t: its weight and sum from lane t, its outputs from memory
+        auto add = [&](int t, float2 p) {
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), t));
+            const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lj), t));
+            ox = ox + w * p.x;
+            oy = oy + w * p.y;
+            L = L + w * l;
+        };
+        const int cn = min(64, ns - c);
+        int t = 0;
+        for (; t + 4 <= cn; t += 4) {
+            float2 p[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                p[u] = po[(size_t)(c + t + u) * (kHeadDim / 2)];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                add(t + u, p[u]);
+        }
+        for (; t < cn; ++t)
+            add(t, po[(size_t)(c + t) * (kHeadDim / 2)]);
     }
-    o[dd] = __fdiv_rn(O, L);
+    *o = make_float2(__fdiv_rn(ox, L), __fdiv_rn(oy, L));
 }
 
 
@@ -401,8 +443,9 @@ hipError_t launch_g(const void* q, const void* k, const void* v, const int32_t* 
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(attn_combine, dim3(B * Hkv * G), dim3(kHeadDim), 0, stream, seq_start, Hkv * G, S,
-                       max_len, Ntok, ws.o, ws.ml, ws.splits, out);
+    const int BH = B * Hkv * G;
+    hipLaunchKernelGGL(attn_combine, dim3((BH + kCombineWaves - 1) / kCombineWaves), dim3(64 * kCombineWaves), 0,
+                       stream, seq_start, BH, Hkv * G, S, max_len, Ntok, ws.o, ws.ml, ws.splits, out);
     return hipGetLastError();
 }
 
