@@ -57,8 +57,9 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// A raw buffer resource over `bytes` bytes at `base` (loads past the end
-// return zeros; the kernels never issue such loads).
+// A raw buffer resource over `bytes` bytes at `base`.  A load past the end
+// returns zeros and touches no memory: the kernels aim the loads of padding
+// rows (past the last row of x or W) there.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -351,8 +352,8 @@ struct TiledCfg {
 };
 
 // One BM x BN output block: rows m0 .. m0+BM-1 of x/y (rows at or past
-// row_hi are clamped on load and never stored), columns n0 .. n0+BN-1 of y
-// (rows of Wb past N are clamped likewise).  Wb is the packed W (slab-major).
+// row_hi read as zeros and are never stored), columns n0 .. n0+BN-1 of y
+// (rows of Wb past N likewise).  Wb is the packed W (slab-major).
 // With kIdx, row i of the logical x is row xidx[i] of the stored x (xn rows;
 // an index outside 0..xn-1 is clamped into it): the MoE layer's gather of
 // token rows into expert order, done by the loads themselves.
@@ -393,15 +394,16 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
 
     // Byte offset of each of this lane's loads within a stage's rows.  Unit
     // u of the stage (lane-linear in LDS) holds logical chunk swz(r, u % kCh)
-    // of row r; rows past the valid range re-read the last valid row.  W
-    // rows of a stage are 128 bytes apart (one slab), x rows 2K bytes.
+    // of row r; rows past the valid range get an offset past the end of
+    // their buffer (zeros, no memory access).  W rows of a stage are 128
+    // bytes apart (one slab), x rows 2K bytes.
     uint32_t voff[C::kInstr];
 #pragma unroll
     for (int j = 0; j < C::kInstr; ++j) {
         const int u = (wave * C::kInstr + j) * 64 + lane;
         if (u < BN * kCh) {
             const int r = u / kCh;
-            voff[j] = wpk_row(min(r, wrows - 1), swz<kCh>(r, u % kCh));
+            voff[j] = r < wrows ? wpk_row(r, swz<kCh>(r, u % kCh)) : wpk_bytes(N, K, wrows);
         } else {
             const int uu = u - BN * kCh;
             const int r = uu / kCh;
@@ -410,7 +412,7 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
                 const int t = xidx[m0 + (int)row];
                 row = (uint32_t)(t < 0 ? 0 : (t >= xn ? xn - 1 : t));
             }
-            voff[j] = row * rowb + swz<kCh>(r, uu % kCh) * 16;
+            voff[j] = r < xrows ? row * rowb + swz<kCh>(r, uu % kCh) * 16 : (uint32_t)(kIdx ? xn : xrows) * rowb;
         }
     }
     auto issue = [&](int s, int buf) {
@@ -750,14 +752,14 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
         const int r = u / kCh;
         const int c = swz<kCh>(r, u % kCh);
         if (j < 8) {
-            voff[j] = wpk_row(min(r, wrows - 1), c);
+            voff[j] = r < wrows ? wpk_row(r, c) : wpk_bytes(N, K, wrows);
         } else {
             uint32_t row = (uint32_t)min(r, xrows - 1);
             if constexpr (kIdx) {
                 const int t = xidx[m0 + (int)row];
                 row = (uint32_t)(t < 0 ? 0 : (t >= xn ? xn - 1 : t));
             }
-            voff[j] = row * rowb + c * 16;
+            voff[j] = r < xrows ? row * rowb + c * 16 : (uint32_t)(kIdx ? xn : xrows) * rowb;
         }
     }
     auto issueW = [&](int j, int t, int wbuf) {
@@ -1112,7 +1114,8 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
                             }
                         }
                         // W: chunk c of the stage is chunk c % 8 of its slab c / 8
-                        voff[j] = r < 16 ? wpk_slab(kSlab * (c / 8), N) + wpk_row(r, c % 8) : row * rowb + c * 16;
+                        voff[j] = r < 16 ? wpk_slab(kSlab * (c / 8), N) + wpk_row(r, c % 8)
+                                         : (r - 16 < xrows ? row * rowb + c * 16 : (uint32_t)(kIdx ? xn : xrows) * rowb);
                     }
                     if constexpr (kIdx)
                         load_idx(cur_it + 1);
