@@ -129,6 +129,22 @@ def test_attn_batch_invariance(gpu):
         assert_bits_equal(ob[b], o2[pos], "request %d in another batch at position %d" % (b, pos))
 
 
+def test_attn_more_splits_than_a_wave(gpu):
+    """The combine holds one split per lane of a wave: sequences of 64, 65 and
+    more than 128 splits (split size 64) take its later rounds, and stay within
+    the bound and invariant to the batch."""
+    split = 64
+    lengths = [64 * 64, 64 * 64 + 1, 9000, 3, 64 * 130 - 7]
+    q, k, v, st = make_case(770, lengths, 16, 8)
+    att = gpu.DecodeAttention(16, 8, split, max_batch=len(lengths), max_seq_len=9000)
+    o = run(att, q, k, v, st)
+    assert_attn_parity(o.cpu().numpy(), q, k, v, st, split, "up to 141 splits")
+    b = 2  # 141 splits, alone
+    lo, hi = int(st[b]), int(st[b + 1])
+    o1 = run(att, q[b:b + 1], k[lo:hi], v[lo:hi], np.array([0, hi - lo], np.int32))
+    assert_bits_equal(bits32(o)[b], bits32(o1)[0], "141 splits alone vs batch")
+
+
 def test_attn_split_size_is_the_pin(gpu):
     """Two split sizes give two trees: both within the bound; one request's
     bits follow the handle's split size, not the batch."""
