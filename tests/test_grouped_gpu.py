@@ -118,12 +118,14 @@ def test_grouped_empty_and_single_expert(gpu, experts):
     assert_parity(y.cpu().numpy()[rows], yr, a, "single expert")
 
 
+@pytest.mark.parametrize("name", list(SHAPES))
 @pytest.mark.parametrize("tokens", [1, 16, 256, 4096])
-def test_indexed_rows_equal_gathered_rows(gpu, experts, tokens):
+def test_indexed_rows_equal_gathered_rows(gpu, experts, tokens, name):
     """The run over indexed token rows is, bit for bit, the run over the
-    gathered rows; indices outside the token rows are clamped into them."""
-    n, k = SHAPES["up"]
-    w, wd = experts["up"]
+    gathered rows; indices outside the token rows are clamped into them.
+    (K = 2048 streams in 512-wide stages, K = 768 in 384-wide ones.)"""
+    n, k = SHAPES[name]
+    w, wd = experts[name]
     g = gpu.GroupedGemm(wd)
     tok, off, _ = synth.moe_routing(180 + tokens, tokens, E, TOPK)
     x_tok = synth.normal_bf16(181 + tokens, (tokens, k))
