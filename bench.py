@@ -585,11 +585,16 @@ def run_moe_layer(args, bg):
         "cpu_baseline": cpu,
         "per_T": per,
         "steps_breakdown": breakdown,
-        "breakdown_note": "steps through their own entry points; the layer itself runs the up projection and "
-                          "SwiGLU as one kernel when the rows average 16 or more per expert (T = 256 and 4096 here)",
+        "breakdown_note": "steps through their own entry points, each run queued behind a short spin kernel so "
+                          "that the events time the GPU rather than the host's launches; the layer itself runs the "
+                          "up projection and SwiGLU as one kernel when the rows average 16 or more per expert "
+                          "(T = 256 and 4096 here)",
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+SPIN_CYCLES = 2_000_000  # the spin kernel's clock cycles: about 1 ms, longer than queueing a run's calls
 
 
 def _moe_steps_timed(bg, lib, dev, x, t, reps):
@@ -634,6 +639,10 @@ def _moe_steps_timed(bg, lib, dev, x, t, reps):
           for _ in range(reps)]
     for i in range(reps):
         g = handles[i % len(handles)]
+        # a short spin kernel ahead of each run, so that the host has queued
+        # the run's calls before the GPU reaches them: the events then time
+        # the GPU's work, not the host's launches (which at T = 1 take longer)
+        torch.cuda._sleep(SPIN_CYCLES)
         for j, c in enumerate(calls):
             ev[i][j][0].record()
             bg.check(c(g) or 0)
