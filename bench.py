@@ -16,7 +16,9 @@ W totalling at least 1 GiB (identical values, separate memory).
 Also reported: the dominant kernel's roofline (achieved vs MI355X peak, from
 HIP events around its launches in the timed region, the only events there),
 per-M times (events around every launch, in as many instrumented steps run
-before the timed region), HBM traffic from rocprof
+before the timed region; the events around single launches are created
+without the system-scope fence that a default event's record performs, an L2
+write-back and invalidate that would slow the launch after it), HBM traffic from rocprof
 counters when a current measurement is committed under profiles/, and the CPU
 oracle's throughput on a bounded sample of the same workload.
 
@@ -160,6 +162,73 @@ def cpu_baseline(w_bits, x_bits, n, k, target_s=15.0):
             "sample": "fp64 oracle on %d rows (all %d columns) of the same layer, %.1f s" % (rows, n, dt)}
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
+_hip_rt = None
+
+
+def _hip():
+    """The HIP runtime torch has loaded (soname libamdhip64.so.7; dlopen
+    returns the loaded copy, so events and streams are shared with torch)."""
+    global _hip_rt
+    if _hip_rt is None:
+        import ctypes
+
+        import torch  # noqa: F401  (loads the runtime first)
+
+        lib = ctypes.CDLL("libamdhip64.so.7")
+        vp = ctypes.c_void_p
+        lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        lib.hipEventRecord.argtypes = [vp, vp]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        lib.hipEventDestroy.argtypes = [vp]
+        _hip_rt = lib
+    return _hip_rt
+
+
+class LaunchEvent:
+    """A HIP timing event for the events around single launches: created with
+    hipEventDisableSystemFence, so recording it does not write back and
+    invalidate the caches as a default event does (measured: about 5 us of GPU
+    time per record, and a cold L2 for the launch after it).  Used like
+    torch.cuda.Event(enable_timing=True): record() on torch's current stream
+    (or `stream`, a raw hipStream_t), elapsed_time(end) in ms once both have
+    completed.  The timed region itself is bracketed by default events and a
+    device synchronisation."""
+
+    def __init__(self):
+        import ctypes
+
+        self._lib = _hip()
+        self._e = ctypes.c_void_p()
+        st = self._lib.hipEventCreateWithFlags(ctypes.byref(self._e), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed: %d" % st)
+
+    def record(self, stream=None):
+        import ctypes
+
+        import torch
+
+        s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        st = self._lib.hipEventRecord(self._e, ctypes.c_void_p(s))
+        if st != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % st)
+
+    def elapsed_time(self, end) -> float:
+        import ctypes
+
+        ms = ctypes.c_float()
+        st = self._lib.hipEventElapsedTime(ctypes.byref(ms), self._e, end._e)
+        if st != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % st)
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "_e", None) and self._e.value:
+            self._lib.hipEventDestroy(self._e)
+            self._e = None
+
+
 def _time_calls(fn, reps):
     import torch
 
@@ -227,7 +296,7 @@ def alternative_pin(bg, ws, xd, ms, n, k, steps, warmup, table_ms):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ms]
+    ev = [[[LaunchEvent(), LaunchEvent()] for _ in ms]
           for _ in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -364,7 +433,7 @@ def run_moe(args, bg):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in calls]
+    ev = [[[LaunchEvent(), LaunchEvent()] for _ in calls]
           for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -529,7 +598,7 @@ def run_moe_layer(args, bg):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in tokens]
+    ev = [[[LaunchEvent(), LaunchEvent()] for _ in tokens]
           for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -635,7 +704,7 @@ def _moe_steps_timed(bg, lib, dev, x, t, reps):
         bg.check(c(handles[0]) or 0)
     torch.cuda.synchronize()
     touched = int(np.count_nonzero(np.diff(off.cpu().numpy())))
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+    ev = [[(LaunchEvent(), LaunchEvent()) for _ in calls]
           for _ in range(reps)]
     for i in range(reps):
         g = handles[i % len(handles)]
@@ -742,7 +811,7 @@ def run_norm_gate_up(args, bg):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in ms] for _ in range(args.steps)]
+    ev = [[[LaunchEvent() for _ in range(3)] for _ in ms] for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for s_ in range(args.steps):
@@ -792,7 +861,7 @@ def run_norm_gate_up(args, bg):
     for _ in range(args.warmup):
         fused_step()
     torch.cuda.synchronize()
-    fev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in ms] for _ in range(args.steps)]
+    fev = [[[LaunchEvent() for _ in range(2)] for _ in ms] for _ in range(args.steps)]
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     f0.record()
     for s_ in range(args.steps):
@@ -886,7 +955,7 @@ def run_decode_attn(args, bg):
         for _ in range(warmup):
             bg.check(lib.bi_attn_decode(*args_))
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        ev = [(LaunchEvent(), LaunchEvent()) for _ in range(steps)]
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record()
         for e0, e1 in ev:
@@ -1054,7 +1123,7 @@ def main(argv=None):
                 events[j][1].record()
 
     def new_events():
-        return [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ms]
+        return [[[LaunchEvent(), LaunchEvent()] for _ in ms]
                 for _ in range(args.steps)]
 
     for _ in range(args.warmup):
@@ -1063,8 +1132,8 @@ def main(argv=None):
 
     # per call: K instrumented steps, outside the timed region, with an event
     # pair around every launch (the median over the steps of each launch's
-    # pair); a marker between every two launches of a step costs the step
-    # about 3% on the GPU, so the timed steps carry only the dominant
+    # pair); the pairs leave gaps of about 8 us between launches (6% of a
+    # step in the kernel trace), so the timed steps carry only the dominant
     # kernel's
     ev = new_events()
     for s in range(args.steps):

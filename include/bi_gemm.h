@@ -80,7 +80,11 @@ typedef enum {
     BI_KERNEL_TILED4_256X256 = 10,
     BI_KERNEL_TILED4_160X256 = 11, /* the four-wave kernel at other block heights, */
     BI_KERNEL_TILED4_192X256 = 12, /* for M that 128 and 256 rows divide badly     */
-    BI_KERNEL_COUNT = 13
+    BI_KERNEL_STREAM_MB2_N2 = 13, /* weight streamer over wide W strips: x rows  */
+    BI_KERNEL_STREAM_MB4_N2 = 14, /* per m-block x W rows per strip: 32x32,      */
+    BI_KERNEL_STREAM_MB2_N4 = 15, /* 64x32, 32x64, 64x64 (mid M: fewer bytes     */
+    BI_KERNEL_STREAM_MB4_N4 = 16, /* per CU than 16-column strips)               */
+    BI_KERNEL_COUNT = 17
 } bi_kernel_kind_t;
 
 /* Most entries of a pin's tiling list. */

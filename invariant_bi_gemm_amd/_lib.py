@@ -38,7 +38,8 @@ INT32_MAX = 2 ** 31 - 1
 # bi_kernel_kind_t, by index; the names are the pin table's
 KERNEL_KINDS = ("stream_mb1", "stream_mb2", "stream_mb4", "tiled_64x32", "tiled_64x64", "tiled_128x64",
                 "tiled_128x64_deep", "tiled_128x128", "tiled_128x128_deep", "tiled4_128x256", "tiled4_256x256",
-                "tiled4_160x256", "tiled4_192x256")
+                "tiled4_160x256", "tiled4_192x256", "stream_mb2_n2", "stream_mb4_n2", "stream_mb2_n4",
+                "stream_mb4_n4")
 
 
 CONCURRENT_SPLITS = 0x100  # BI_KERNEL_CONCURRENT_SPLITS; "+cs" in a kind's name

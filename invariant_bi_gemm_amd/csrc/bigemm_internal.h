@@ -58,6 +58,10 @@ enum class DenseKernel {
     kTiled256 = BI_KERNEL_TILED4_256X256,
     kTiled160x256 = BI_KERNEL_TILED4_160X256,
     kTiled192x256 = BI_KERNEL_TILED4_192X256,
+    kStream32x32 = BI_KERNEL_STREAM_MB2_N2,
+    kStream64x32 = BI_KERNEL_STREAM_MB4_N2,
+    kStream32x64 = BI_KERNEL_STREAM_MB2_N4,
+    kStream64x64 = BI_KERNEL_STREAM_MB4_N4,
 };
 DenseKernel choose_dense(const Plan& p, int M);
 // Whether a call with M rows runs its splits concurrently (the tiling

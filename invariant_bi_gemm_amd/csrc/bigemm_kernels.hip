@@ -961,11 +961,14 @@ __global__ void __launch_bounds__(WM * WN * 64)
 // ---------------------------------------------------------------------------
 // Streaming kernel (small M)
 // ---------------------------------------------------------------------------
-// MB consumer waves (one 16-row m-tile each) share one 16-column strip of W.
-// A stage holds BKS values of k for the 16 W rows and the first XR rows of
+// MB consumer waves (one 16-row m-tile each) share one strip of 16*NT
+// columns of W; each consumer runs NT chains, one per 16-column tile.  A
+// stage holds BKS values of k for the 16*NT W rows and the first XR rows of
 // the m-block (XR = 16*MB, or fewer when the call has fewer rows: the
 // consumer of a single m-tile then re-reads row XR-1 for its padding rows).
 // NP producer waves split a stage's loads; NR stages live in an LDS ring.
+// NT > 1 (mid M): a CU's bytes are (16 MB + 16 NT) rows over K per item, so
+// a 64x64 item moves 128 rows where four 64x16 items move 320.
 constexpr int kStreamLdsBudget = 144 * 1024;
 constexpr int kStreamWInFlight = 32 * 1024;
 // Producer waves per streaming workgroup: the WG has at most 8 waves (two
@@ -977,10 +980,11 @@ constexpr int stream_producers()
     return BKS >= 256 ? 8 - MB : (BKS == 128 ? (6 - MB > 2 ? 6 - MB : 2) : 2);
 }
 
-template <int MB, int XR, int BKS, int NP>
+template <int MB, int XR, int BKS, int NP, int NT = 1>
 struct StreamShape {
+    static constexpr int kWRows = 16 * NT;   // W rows per stage
     static constexpr int kChunks = BKS / 8;  // 16-byte units per row per stage
-    static constexpr int kStageUnits = (16 + XR) * kChunks;
+    static constexpr int kStageUnits = (kWRows + XR) * kChunks;
     static constexpr int kT = kStageUnits / 64;  // load instructions per stage
     static constexpr int kHi = (kT + NP - 1) / NP;  // share of the first kT % NP producers
     static constexpr int kLo = kT / NP;             // share of the others
@@ -992,15 +996,16 @@ struct StreamShape {
     // 19.7 us with two stages in flight against 21.2 us with seven).  The
     // narrower stages keep their depth: the grouped kernel's short items
     // (K = 768: three stages an item) lose 3% when capped the same way.
-    static constexpr int kByFlight = BKS >= 512 ? kStreamWInFlight / (16 * BKS * 2) + 1 : 16;
+    static constexpr int kByFlight = BKS >= 512 ? kStreamWInFlight / (kWRows * BKS * 2) + 1 : 16;
     static constexpr int kNR0 = kByLds < kByVmcnt ? kByLds : kByVmcnt;
     static constexpr int kNR1 = kNR0 < kByFlight ? kNR0 : kByFlight;
     static constexpr int kNR = kNR1 < 16 ? kNR1 : 16;
 };
 
-template <int MB, int XR, int BKS, int NP>
+template <int MB, int XR, int BKS, int NP, int NT = 1>
 struct StreamCfg {
-    using S = StreamShape<MB, XR, BKS, NP>;
+    using S = StreamShape<MB, XR, BKS, NP, NT>;
+    static constexpr int kWRows = S::kWRows;
     static constexpr int kConsumers = MB;
     static constexpr int kProducers = NP;
     static constexpr int kThreads = (MB + NP) * 64;
@@ -1014,7 +1019,8 @@ struct StreamCfg {
     static constexpr int kLdsBytes = NR * kStageUnits * 16;
     static_assert(XR == 16 * MB || (MB == 1 && XR < 16), "x rows per stage");
     static_assert(kStageUnits % 64 == 0, "a stage is whole load instructions");
-    static_assert((16 * kChunks) % 64 == 0, "one load must not straddle W and x");
+    static_assert((kWRows * kChunks) % 64 == 0, "one load must not straddle W and x");
+    static_assert(NT == 1 || XR == 16 * MB, "wide strips take whole m-blocks");
     static_assert(kLo >= 1, "every producer loads something");
     static_assert(NR >= 3, "ring too shallow");
     static_assert(kHi * (NR - 1) < 64, "loads in flight must fit vmcnt");
@@ -1022,13 +1028,13 @@ struct StreamCfg {
 };
 
 // Where work item `item` lives: rows m0 .. row_hi-1 of x/y, W rows
-// n0 .. n0+15 of the expert weight Wb.
+// n0 .. n0+16NT-1 of the expert weight Wb.
 struct StreamItem {
     int m0, row_hi, n0;
     const uint16_t* Wb;
 };
 
-template <int MB, int XR, int BKS, int NP, bool kIdx = false>
+template <int MB, int XR, int BKS, int NP, bool kIdx = false, int NT = 1>
 __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ W, float* __restrict__ y,
                                             int N, int K, Split sp, int tiles_n, int nitems,
@@ -1038,9 +1044,10 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
                                             // grouped, kIdx: row indices into x (xn rows)
                                             const int32_t* __restrict__ xidx = nullptr, int xn = 0)
 {
-    using C = StreamCfg<MB, XR, BKS, NP>;
+    using C = StreamCfg<MB, XR, BKS, NP, NT>;
     constexpr int kCh = C::kChunks;
     constexpr int NR = C::NR;
+    constexpr int kWR = C::kWRows;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = gridDim.x;
@@ -1052,7 +1059,7 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
         const int item = blockIdx.x + it * G;
         const int mb = item / tiles_n;
         StreamItem s;
-        s.n0 = (item % tiles_n) * 16;
+        s.n0 = (item % tiles_n) * kWR;
         if (elist) {
             const int e = elist[mb];
             s.m0 = sh_off[e];
@@ -1086,7 +1093,7 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
 #pragma unroll
                 for (int j = 0; j < kI; ++j) {
                     const int r = ((first + j) * 64 + lane) / kCh;
-                    pend[j] = r >= 16 ? xidx[s.m0 + min(r - 16, xrows - 1)] : 0;
+                    pend[j] = r >= kWR ? xidx[s.m0 + min(r - kWR, xrows - 1)] : 0;
                 }
             };
             if constexpr (kIdx)
@@ -1098,7 +1105,10 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
                     k_stage = 0;
                     const StreamItem s = item_at(cur_it);
                     const int xrows = min(XR, s.row_hi - s.m0);
-                    rW = make_rsrc(s.Wb + (size_t)s.n0 * kSlab, wpk_bytes(N, K, 16));
+                    // W rows past N (a strip wider than what is left) load
+                    // nothing: their offsets aim past the end of the buffer
+                    const int wrows = min(kWR, N - s.n0);
+                    rW = make_rsrc(s.Wb + (size_t)s.n0 * kSlab, wpk_bytes(N, K, wrows));
                     rX = kIdx ? make_rsrc(x, (uint32_t)xn * rowb)
                               : make_rsrc(x + (size_t)s.m0 * K, (uint32_t)xrows * rowb);
 #pragma unroll
@@ -1106,16 +1116,18 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
                         const int u = (first + j) * 64 + lane;
                         const int r = u / kCh;
                         const int c = swz<kCh>(r, u % kCh);
-                        uint32_t row = r < 16 ? (uint32_t)r : (uint32_t)min(r - 16, xrows - 1);
+                        uint32_t row = r < kWR ? (uint32_t)r : (uint32_t)min(r - kWR, xrows - 1);
                         if constexpr (kIdx) {
-                            if (r >= 16) {
+                            if (r >= kWR) {
                                 const int t = pend[j];
                                 row = (uint32_t)(t < 0 ? 0 : (t >= xn ? xn - 1 : t));
                             }
                         }
                         // W: chunk c of the stage is chunk c % 8 of its slab c / 8
-                        voff[j] = r < 16 ? wpk_slab(kSlab * (c / 8), N) + wpk_row(r, c % 8)
-                                         : (r - 16 < xrows ? row * rowb + c * 16 : (uint32_t)(kIdx ? xn : xrows) * rowb);
+                        voff[j] = r < kWR ? (r < wrows ? wpk_slab(kSlab * (c / 8), N) + wpk_row(r, c % 8)
+                                                       : wpk_bytes(N, K, wrows))
+                                          : (r - kWR < xrows ? row * rowb + c * 16
+                                                             : (uint32_t)(kIdx ? xn : xrows) * rowb);
                     }
                     if constexpr (kIdx)
                         load_idx(cur_it + 1);
@@ -1125,7 +1137,7 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
                 for (int j = 0; j < kI; ++j) {
                     const int u0 = (first + j) * 64;
                     const int k = sp.k0 + k_stage * BKS;
-                    dma16(u0 < 16 * kCh ? rW : rX, voff[j], u0 < 16 * kCh ? wpk_slab(k, N) : (uint32_t)k * 2,
+                    dma16(u0 < kWR * kCh ? rW : rX, voff[j], u0 < kWR * kCh ? wpk_slab(k, N) : (uint32_t)k * 2,
                           dst + u0);
                 }
                 ++k_stage;
@@ -1155,24 +1167,34 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
         // read once the barrier says it has landed.
         const int ci = wave;
         const int rw = lane & 15;
-        const int rx = 16 + (MB == 1 ? min(rw, XR - 1) : 16 * ci + rw);
+        const int rx = kWR + (MB == 1 ? min(rw, XR - 1) : 16 * ci + rw);
         constexpr int kH = C::kSteps / 2;  // k-steps per half stage
-        uint4 a0[kH], b0[kH], a1[kH], b1[kH];
+        uint4 a0[kH * NT], b0[kH], a1[kH * NT], b1[kH];
         auto read = [&](int q, int h, uint4* a, uint4* b) {
             const uint4* st = ring + (q % NR) * C::kStageUnits;
 #pragma unroll
             for (int t = 0; t < kH; ++t) {
                 const int cl = 4 * (h * kH + t) + (lane >> 4);
-                a[t] = st[rw * kCh + swz<kCh>(rw, cl)];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int r = 16 * j + rw;
+                    a[t * NT + j] = st[r * kCh + swz<kCh>(r, cl)];
+                }
                 b[t] = st[rx * kCh + swz<kCh>(rx, cl)];
             }
         };
-        auto chain = [&](f32x4& acc, const uint4* a, const uint4* b) {
+        // the NT chains of a k-step side by side; each chain in ascending k
+        auto chain = [&](f32x4* acc, const uint4* a, const uint4* b) {
 #pragma unroll
             for (int t = 0; t < kH; ++t)
-                acc = mfma_step(a[t], b[t], acc);
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    acc[j] = mfma_step(a[t * NT + j], b[t], acc[j]);
         };
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (total > 0) {
             barrier_after_lds_reads();
             read(0, 0, a0, b0);
@@ -1188,25 +1210,29 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
             if ((q + 1) % nst == 0) {
                 const StreamItem s = item_at(q / nst);
                 const int m = s.m0 + 16 * ci + rw;
-                if (m < s.row_hi)
-                    emit4(y + (size_t)m * N + s.n0 + 4 * (lane >> 4), acc, sp.fold);
-                acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    if (m < s.row_hi && s.n0 + 16 * j < N)
+                        emit4(y + (size_t)m * N + s.n0 + 16 * j + 4 * (lane >> 4), acc[j], sp.fold);
+                    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
             }
         }
     }
 }
 
-template <int MB, int XR, int BKS, int NP, int kMode = kPlain>
+template <int MB, int XR, int BKS, int NP, int kMode = kPlain, int NT = 1>
 __global__ void __launch_bounds__((MB + NP) * 64)
     bigemm_stream(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                   float* __restrict__ y, int M, int N, int K, Split sp, float* part)
 {
-    using C = StreamCfg<MB, XR, BKS, NP>;
+    using C = StreamCfg<MB, XR, BKS, NP, NT>;
     __shared__ uint4 ring[C::NR * C::kStageUnits];
     y = cmp_split<kMode>(sp, y, part, M, N);
-    const int tiles_n = N / 16;
+    const int tiles_n = (N + 16 * NT - 1) / (16 * NT);
     const int mblocks = (M + 16 * MB - 1) / (16 * MB);
-    stream_body<MB, XR, BKS, NP>(ring, x, W, y, N, K, sp, tiles_n, mblocks * tiles_n, M, nullptr, nullptr);
+    stream_body<MB, XR, BKS, NP, false, NT>(ring, x, W, y, N, K, sp, tiles_n, mblocks * tiles_n, M, nullptr,
+                                            nullptr);
 }
 
 // Grouped: one m-block per expert whose row count c satisfies 0 < c <= cmax
@@ -1298,21 +1324,21 @@ hipError_t run_tiled4(const void* W, const void* x, int M, float* y, int N, int 
     return hipGetLastError();
 }
 
-template <int MB, int XR, int BKS, int NP>
+template <int MB, int XR, int BKS, int NP, int NT = 1>
 hipError_t run_stream(const void* W, const void* x, int M, float* y, int N, int K, Split sp,
                       int num_cus, hipStream_t stream, const LaunchExtra& ex = LaunchExtra())
 {
-    using C = StreamCfg<MB, XR, BKS, NP>;
-    const int items = ((M + 16 * MB - 1) / (16 * MB)) * (N / 16);
+    using C = StreamCfg<MB, XR, BKS, NP, NT>;
+    const int items = ((M + 16 * MB - 1) / (16 * MB)) * ((N + 16 * NT - 1) / (16 * NT));
     const int grid = items < num_cus ? items : num_cus;
     if (ex.rstd)
         return hipErrorInvalidValue;  // no normalising instance of this kernel
     if (ex.ysplits > 1)
-        hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP, kCmp>), dim3(grid, ex.ysplits), dim3(C::kThreads), 0,
-                           stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K,
+        hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP, kCmp, NT>), dim3(grid, ex.ysplits), dim3(C::kThreads),
+                           0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K,
                            sp, ex.part);
     else
-        hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP>), dim3(grid), dim3(C::kThreads), 0, stream,
+        hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP, kPlain, NT>), dim3(grid), dim3(C::kThreads), 0, stream,
                            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K, sp,
                            nullptr);
     return hipGetLastError();
@@ -1336,6 +1362,26 @@ hipError_t run_stream_k(const void* W, const void* x, int M, float* y, int N, in
                                                                                    stream, ex);
     return run_stream<MB, (XR < 8 ? 8 : XR), 64, stream_producers<MB, 64>()>(W, x, M, y, N, K, sp, num_cus, stream,
                                                                              ex);
+}
+
+// Wide strips (NT > 1): the widest stage, up to 256 values of k, of which
+// three fit the LDS budget and that divides the split; every wave that is not
+// a consumer produces.
+template <int MB, int NT>
+constexpr int wide_stage()
+{
+    return 3 * (16 * (MB + NT)) * 256 * 2 <= kStreamLdsBudget ? 256 : 128;
+}
+template <int MB, int NT>
+hipError_t run_stream_wide(const void* W, const void* x, int M, float* y, int N, int K, Split sp,
+                           int num_cus, hipStream_t stream, const LaunchExtra& ex = LaunchExtra())
+{
+    constexpr int XR = 16 * MB, NP = 8 - MB, B = wide_stage<MB, NT>();
+    if (sp.klen % B == 0)
+        return run_stream<MB, XR, B, NP, NT>(W, x, M, y, N, K, sp, num_cus, stream, ex);
+    if (B > 128 && sp.klen % 128 == 0)
+        return run_stream<MB, XR, 128, NP, NT>(W, x, M, y, N, K, sp, num_cus, stream, ex);
+    return run_stream<MB, XR, 64, NP, NT>(W, x, M, y, N, K, sp, num_cus, stream, ex);
 }
 
 // y += part[0] + part[1] + ... (in that order), 4 values per thread and step:
@@ -1526,6 +1572,10 @@ const char* dense_kernel_name_cs(DenseKernel k)
     case DenseKernel::kTiled256: return "bigemm_tiled<256x256>,concurrent splits";
     case DenseKernel::kTiled160x256: return "bigemm_tiled<160x256>,concurrent splits";
     case DenseKernel::kTiled192x256: return "bigemm_tiled<192x256>,concurrent splits";
+    case DenseKernel::kStream32x32: return "bigemm_stream<mb=2,nt=2>,concurrent splits";
+    case DenseKernel::kStream64x32: return "bigemm_stream<mb=4,nt=2>,concurrent splits";
+    case DenseKernel::kStream32x64: return "bigemm_stream<mb=2,nt=4>,concurrent splits";
+    case DenseKernel::kStream64x64: return "bigemm_stream<mb=4,nt=4>,concurrent splits";
     }
     return "?";
 }
@@ -1546,6 +1596,10 @@ const char* kernel_kind_name(int kind)
     case BI_KERNEL_TILED4_256X256: return "tiled4_256x256";
     case BI_KERNEL_TILED4_160X256: return "tiled4_160x256";
     case BI_KERNEL_TILED4_192X256: return "tiled4_192x256";
+    case BI_KERNEL_STREAM_MB2_N2: return "stream_mb2_n2";
+    case BI_KERNEL_STREAM_MB4_N2: return "stream_mb4_n2";
+    case BI_KERNEL_STREAM_MB2_N4: return "stream_mb2_n4";
+    case BI_KERNEL_STREAM_MB4_N4: return "stream_mb4_n4";
     }
     return "";
 }
@@ -1566,6 +1620,10 @@ const char* dense_kernel_name(DenseKernel k)
     case DenseKernel::kTiled256: return "bigemm_tiled<256x256>";
     case DenseKernel::kTiled160x256: return "bigemm_tiled<160x256>";
     case DenseKernel::kTiled192x256: return "bigemm_tiled<192x256>";
+    case DenseKernel::kStream32x32: return "bigemm_stream<mb=2,nt=2>";
+    case DenseKernel::kStream64x32: return "bigemm_stream<mb=4,nt=2>";
+    case DenseKernel::kStream32x64: return "bigemm_stream<mb=2,nt=4>";
+    case DenseKernel::kStream64x64: return "bigemm_stream<mb=4,nt=4>";
     }
     return "?";
 }
@@ -1588,6 +1646,14 @@ hipError_t launch_dense_split(const Plan& p, DenseKernel kind, const void* W, co
         return run_stream_k<2, 32>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ex);
     case DenseKernel::kStream64:
         return run_stream_k<4, 64>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ex);
+    case DenseKernel::kStream32x32:
+        return run_stream_wide<2, 2>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ex);
+    case DenseKernel::kStream64x32:
+        return run_stream_wide<4, 2>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ex);
+    case DenseKernel::kStream32x64:
+        return run_stream_wide<2, 4>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ex);
+    case DenseKernel::kStream64x64:
+        return run_stream_wide<4, 4>(W, x, M, y, p.n, p.k, sp, p.num_cus, stream, ex);
     case DenseKernel::kTiled256:
         return run_tiled4<8>(W, x, M, y, p.n, p.k, sp, stream, ex);
     case DenseKernel::kTiled128x256:
@@ -1695,6 +1761,10 @@ DenseKernel norm_kind(DenseKernel k)
     case DenseKernel::kStream16:
     case DenseKernel::kStream32:
     case DenseKernel::kStream64:
+    case DenseKernel::kStream32x32:
+    case DenseKernel::kStream64x32:
+    case DenseKernel::kStream32x64:
+    case DenseKernel::kStream64x64:
         return DenseKernel::kTiled64x32;
     case DenseKernel::kTiled128:  // two stages: too shallow to rewrite one ahead
     case DenseKernel::kTiled128x256:

@@ -43,11 +43,15 @@ import sys
 
 SPLIT_CHOICES = (1, 2, 4, 7, 8, 14, 16)
 MAX_SPLITS = 16
-STREAM_KINDS = ("stream_mb1", "stream_mb2", "stream_mb4")
+STREAM_KINDS = ("stream_mb1", "stream_mb2", "stream_mb4", "stream_mb2_n2", "stream_mb4_n2", "stream_mb2_n4",
+                "stream_mb4_n4")
 KERNEL_KINDS = ("stream_mb1", "stream_mb2", "stream_mb4", "tiled_64x32", "tiled_64x64", "tiled_128x64",
                 "tiled_128x64_deep", "tiled_128x128", "tiled_128x128_deep", "tiled4_128x256", "tiled4_256x256",
-                "tiled4_160x256", "tiled4_192x256")
-STREAM_LIMIT = 256  # streamers are candidates at M <= this
+                "tiled4_160x256", "tiled4_192x256", "stream_mb2_n2", "stream_mb4_n2", "stream_mb2_n4",
+                "stream_mb4_n4")
+STREAM_LIMIT = 256  # streamers are candidates at M <= this,
+WIDE_STREAM_LIMIT = 1024  # those over 32- and 64-column strips at M <= this
+WIDE_STREAM_KINDS = ("stream_mb2_n2", "stream_mb4_n2", "stream_mb2_n4", "stream_mb4_n4")
 MAX_TILINGS = 12
 INT32_MAX = 2 ** 31 - 1
 
@@ -88,7 +92,13 @@ def base_kind(kd: str) -> str:
 
 def kernel_candidates(m: int, kinds=KERNEL_KINDS):
     """Kernel kinds tried at M rows."""
-    return [kd for kd in kinds if m <= STREAM_LIMIT or base_kind(kd) not in STREAM_KINDS]
+    def fits(kd):
+        kd = base_kind(kd)
+        if kd in WIDE_STREAM_KINDS:
+            return m <= WIDE_STREAM_LIMIT
+        return m <= STREAM_LIMIT or kd not in STREAM_KINDS
+
+    return [kd for kd in kinds if fits(kd)]
 
 
 def tree_kinds(s: int, kinds=KERNEL_KINDS):

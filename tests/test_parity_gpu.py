@@ -113,6 +113,38 @@ def test_ragged_columns(gpu, n, ms):
         assert_bits_equal(yg[off[e]:off[e + 1]], yd, "grouped N=%d expert %d" % (n, e))
 
 
+WIDE_KINDS = ("stream_mb2_n2", "stream_mb4_n2", "stream_mb2_n4", "stream_mb4_n4")
+
+
+@pytest.mark.parametrize("k", [576, 1152, 1280])
+def test_wide_strips_ragged(gpu, k):
+    """The weight streamer over 32- and 64-column W strips, each kind forced
+    for every M.  N = 272 leaves a last strip of 16 columns, whose other W
+    rows load nothing and store nothing; K = 576, 1152 and 1280 run the 64-,
+    128- and 256-wide stages (the widest that divides K).  Every row equals,
+    bit for bit, the same row computed alone under the default pin, and every
+    element is within the oracle's bound."""
+    n = 272
+    w = synth.normal_bf16(70 + k, (n, k), 0.02)
+    ms = (1, 17, 40, 100, 300)
+    x = synth.normal_bf16(71 + k, (max(ms), k))
+    wd, xd = to_dev(w), to_dev(x)
+    g0 = gpu.Gemm(wd)
+    alone = torch.empty((max(ms), n), dtype=torch.float32, device=DEV)
+    for r in range(max(ms)):
+        g0(xd[r:r + 1], out=alone[r:r + 1])
+    ref = bits32(alone)
+    yr, a = oracle.gemm_f64(x, w)
+    for kind in WIDE_KINDS:
+        g = gpu.Gemm(wd, pin={"splits": 1, "stream_max_m": 0, "tiling": [(None, kind)]})
+        for m in ms:
+            y = g(xd[:m])
+            what = "%s K=%d M=%d" % (kind, k, m)
+            assert_bits_equal(bits32(y), ref[:m], what)
+            assert_parity(y.cpu().numpy(), yr[:m], a[:m], what)
+        g.close()
+
+
 @pytest.mark.parametrize("smax", [0, 4096])
 def test_forced_paths_parity(gpu, smax):
     """Both kernel families on their own at awkward sizes."""

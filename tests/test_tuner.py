@@ -29,7 +29,11 @@ def test_legal_splits():
 def test_kernel_candidates():
     assert tuner.kernel_candidates(1) == list(tuner.KERNEL_KINDS)
     assert tuner.kernel_candidates(256) == list(tuner.KERNEL_KINDS)
-    big = tuner.kernel_candidates(257)
+    mid = tuner.kernel_candidates(257)
+    assert set(k for k in mid if k in tuner.STREAM_KINDS) == set(tuner.WIDE_STREAM_KINDS)
+    assert "tiled4_256x256" in mid and "stream_mb1" not in mid
+    assert tuner.kernel_candidates(1024) == mid
+    big = tuner.kernel_candidates(1025)
     assert not any(k in tuner.STREAM_KINDS for k in big) and "tiled4_256x256" in big
 
 
