@@ -1181,7 +1181,11 @@ def main(argv=None):
         achieved = d["flops"] / (d["ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = read_traffic(dom)
+    # the committed counter profiles were taken on the default workload's
+    # sweep (llama8b_down, every M): another workload gets null, not that
+    # sweep's figures for a kernel of the same name
+    profiled = args.workload == "llama8b_down" and not args.m
+    roof["traffic"] = read_traffic(dom) if profiled else None
     roof["kernel"] = dom
     roof["launches_per_step"] = d["launches"]
     roof["avg_launch_us"] = d["ms"] * 1e3 / d["launches"]
@@ -1189,10 +1193,10 @@ def main(argv=None):
     # the MFMA peak scales with the engine clock: the same fraction against
     # the peak at the clock the kernel sustains (committed rocprof counters of
     # the current kernels; null otherwise)
-    clock = read_clock(dom)
+    clock = read_clock(dom) if profiled else None
     roof["sustained_clock_ghz"] = clock
     roof["clock_source"] = ("rocprof GRBM_GUI_ACTIVE / dispatch duration, %s" % os.path.relpath(CLOCK_FILE, ROOT)
-                            if clock else "no current counter profile")
+                            if clock else "no current counter profile of this workload")
     if clock and roof["bound"] == "mfma":
         peak_at_clock = PEAK_BF16_TFLOPS * clock / PEAK_CLOCK_GHZ
         roof["peak_at_sustained_clock"] = round(peak_at_clock, 1)
