@@ -591,28 +591,43 @@ __device__ __forceinline__ void tile_of_block(int b, int nblocks, int tiles_m, i
 }
 
 // Block -> tile for the four-wave kernels: the tile grid is cut into 8
-// rectangles, 4 along m by 2 along n, and XCD x (which hardware hands block
-// b when b % 8 == x) takes rectangle (x % 4, x / 4), walking groups of 4 of
-// its m-blocks column by column.  So each half of the W columns is read by
-// one set of four XCDs (x / 4), and the four XCDs of a set share those W
-// tiles while each keeps its own x rows; with the order of tile_of_block
-// every XCD reads the same W half at once.  Measured on the down-proj: about
-// 3% faster at M = 4096 and 8192.  Grids that do not cut evenly use
-// tile_of_block.
+// rectangles, MR along m by 8 / MR along n, and XCD x (which hardware hands
+// block b when b % 8 == x) takes rectangle (x % MR, x / MR), walking groups
+// of 4 of its m-blocks column by column.  With MR = 4, each half of the W
+// columns is read by one set of four XCDs (x / 4), and the four XCDs of a
+// set share those W tiles while each keeps its own x rows; with the order of
+// tile_of_block every XCD reads the same W half at once (measured on the
+// down-proj: about 3% faster at M = 4096 and 8192).  What an XCD's L2 fetches
+// in a round is the x and W panels its rectangle's blocks touch: with 32
+// blocks per XCD, 4 x panels and 8 W panels for MR = 4, 8 and 4 for MR = 2.
+// With 256-row blocks both come to 12 panels of the same size; with 128-row
+// blocks an x panel is half a W panel, and MR = 2 fetches 20% fewer bytes.
+// Grids that do not cut evenly use tile_of_block.
+template <int MR>
 __device__ __forceinline__ void tile_of_block_rect(int b, int nblocks, int tiles_m, int tiles_n, int* tm, int* tn)
 {
-    if (tiles_m % 4 != 0 || tiles_n % 2 != 0 || nblocks != tiles_m * tiles_n) {
+    constexpr int NR = 8 / MR;
+    if (tiles_m % MR != 0 || tiles_n % NR != 0 || nblocks != tiles_m * tiles_n) {
         tile_of_block(b, nblocks, tiles_m, tiles_n, 4, tm, tn);
         return;
     }
     const int xcd = b % 8, i = b / 8;
-    const int rm = tiles_m / 4, rn = tiles_n / 2;
+    const int rm = tiles_m / MR, rn = tiles_n / NR;
     const int gm = rm < 4 ? rm : 4;  // rm is a multiple of gm: 1, 2, 3 or a multiple of 4 ...
     const int rows = rm % gm == 0 ? gm : 1;  // ... else walk one m-block at a time
     const int span = rows * rn, g = i / span, r = i % span;
-    *tm = (xcd % 4) * rm + g * rows + r % rows;
-    *tn = (xcd / 4) * rn + r / rows;
+    *tm = (xcd % MR) * rm + g * rows + r % rows;
+    *tn = (xcd / MR) * rn + r / rows;
 }
+
+// Rectangles along m for the four-wave kernel with XT x tiles per wave
+// (blocks of 32 XT rows): 2 when a block's x panel is smaller than its W
+// panel, else 4.  At M = 2048 on the down-proj (128x256 blocks) the panel
+// count gives 470 MB of L2 fills per launch with MR = 2 against 587 MB (as
+// counted) with MR = 4; the call timed 197.9-199.2 us against 199.2-201.9,
+// interleaved on one box: each CU's load path, not the fabric, bounds it.
+template <int XT>
+constexpr int rect_m() { return XT < 8 ? 2 : 4; }
 
 template <int BM, int BN, int WM, int WN, int BK, int NS, int kMode = kPlain>
 __global__ void __launch_bounds__(WM * WN * 64)
@@ -894,7 +909,7 @@ __global__ void __launch_bounds__(256)
     __shared__ uint4 lds[3 * 256 * 8 + 2 * 32 * XT * 8];
     y = cmp_split<kMode>(sp, y, part, M, N);
     int tm, tn;
-    tile_of_block_rect(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
+    tile_of_block_rect<rect_m<XT>()>(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
     tiled4_block<XT>(lds, x, W, y, tm * 32 * XT, M, tn * 256, N, K, sp);
 }
 

@@ -62,6 +62,18 @@ def test_dense_run_graph_and_stream(gpu, m):
     check_graph_and_stream(lambda: g(x, out=y), [y], "bi_gemm_run M=%d (%s)" % (m, g.kernel_name(m)))
 
 
+@pytest.mark.parametrize("kind", ["stream_mb2_n2", "stream_mb4_n4"])
+def test_wide_strip_streamer_graph(gpu, kind):
+    """The weight streamer over 32- and 64-column strips, forced by the pin's
+    tiling, captured and replayed, and on a side stream."""
+    n, k = 2048, 2048
+    g = gpu.Gemm(to_dev(synth.normal_bf16(504, (n, k), 0.02)),
+                 pin={"splits": 1, "stream_max_m": 0, "tiling": [(None, kind)]})
+    x = to_dev(synth.normal_bf16(505, (100, k)))
+    y = torch.empty((100, n), dtype=torch.float32, device=DEV)
+    check_graph_and_stream(lambda: g(x, out=y), [y], "bi_gemm_run %s (%s)" % (kind, g.kernel_name(100)))
+
+
 def test_split_tree_graph(gpu):
     """An S = 4 tree enqueues four kernels; all are captured in order."""
     n, k = 1024, 4096
