@@ -14,7 +14,8 @@ serving the weights to the decode-size calls, the calls rotate over copies of
 W totalling at least 1 GiB (identical values, separate memory).
 
 Also reported: the dominant kernel's roofline (achieved vs MI355X peak, from
-HIP events around its launches in the timed region, the only events there),
+HIP events around its runs of consecutive launches in the timed region, the
+only events there),
 per-M times (events around every launch, in as many instrumented steps run
 before the timed region; the events around single launches are created
 without the system-scope fence that a default event's record performs, an L2
@@ -1108,19 +1109,22 @@ def main(argv=None):
     run = lib.bi_gemm_run
     call_no = [0]
 
-    def step(events=None, timed=None):
-        # events[j]: the event pair around launch j, for the launches j in timed
+    def step(events=None, spans=None):
+        # events[i]: the event pair around the launches of span i, spans the
+        # (first, last) launch indices of each span (None: every launch its
+        # own span)
+        first = {a: i for i, (a, _) in enumerate(spans)} if spans is not None else None
+        last = {b: i for i, (_, b) in enumerate(spans)} if spans is not None else None
         for j, m in enumerate(ms):
             h = hps[call_no[0] % copies]
             call_no[0] += 1
-            on = events is not None and (timed is None or j in timed)
-            if on:
-                events[j][0].record()
+            if events is not None and (first is None or j in first):
+                events[j if first is None else first[j]][0].record()
             st = run(h, xp, m, yps[m], stream)
             if st != 0:
                 bg.check(st)
-            if on:
-                events[j][1].record()
+            if events is not None and (last is None or j in last):
+                events[j if last is None else last[j]][1].record()
 
     def new_events():
         return [[[LaunchEvent(), LaunchEvent()] for _ in ms]
@@ -1151,29 +1155,39 @@ def main(argv=None):
         d["launches"] += 1
         d["ms_probe"] = d.get("ms_probe", 0.0) + per_call_ms[m]
     dom = max(by_kernel, key=lambda kname: by_kernel[kname]["ms_probe"])
-    dom_calls = {j for j, m in enumerate(ms) if names[m] == dom}
+    dom_calls = [j for j, m in enumerate(ms) if names[m] == dom]
+    # its launches as runs of consecutive calls, one event pair around each
+    # run (every pair leaves a gap of a few us before the next launch)
+    dom_spans = []
+    for j in dom_calls:
+        if dom_spans and dom_spans[-1][1] == j - 1:
+            dom_spans[-1] = (dom_spans[-1][0], j)
+        else:
+            dom_spans.append((j, j))
 
-    # timed region: K steps, events around the dominant kernel's launches
-    # (on the launch stream) for its roofline
+    # timed region: K steps, events around the dominant kernel's runs of
+    # launches (on the launch stream) for its roofline
     ev = new_events()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for s in range(args.steps):
-        step(ev[s], dom_calls)
+        step(ev[s], dom_spans)
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    dom_call_ms = {j: float(np.median([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
-                   for j in dom_calls}
+    # per step: the dominant kernel's time, the sum of its spans; the median
+    # over the timed steps
+    dom_ms = float(np.median([sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for i in range(len(dom_spans)))
+                              for s in range(args.steps)]))
 
     step_flops = sum(flops.values())
     ms_per_step = total_ms / args.steps
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
     d = by_kernel[dom]
-    d["ms"] = sum(dom_call_ms.values())
+    d["ms"] = dom_ms
     if "stream" in dom:
         achieved = d["bytes"] / (d["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -1189,7 +1203,10 @@ def main(argv=None):
     roof["kernel"] = dom
     roof["launches_per_step"] = d["launches"]
     roof["avg_launch_us"] = d["ms"] * 1e3 / d["launches"]
-    roof["launch_us_statistic"] = "median over the timed steps, per launch (its events are the only ones there)"
+    roof["launch_us_statistic"] = ("the kernel's time per step (an event pair around each run of its consecutive "
+                                   "launches, the only events in the timed region), median over the timed steps, "
+                                   "divided by its launches per step")
+    roof["event_spans_per_step"] = len(dom_spans)
     # the MFMA peak scales with the engine clock: the same fraction against
     # the peak at the clock the kernel sustains (committed rocprof counters of
     # the current kernels; null otherwise)
