@@ -68,10 +68,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // 16 bytes per lane from the buffer at voff + soff straight into LDS: lane
 // L's bytes land at lds_base + 16 L (lds_base is wave-uniform; it goes to M0).
+// Cache-policy operand of a load marking it non-temporal (the nt bit).  A
+// line read once then does not displace cached lines that will be read or
+// written again: in particular it leaves in the Infinity Cache the output an
+// earlier large call has just written, which the same stream would otherwise
+// write back to HBM while these loads run.
+constexpr int kCachePolicyNT = 2;
+template <int kAux = 0>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                       const void* lds_base)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, kAux);
 }
 
 // The same load, written out.  The compiler then does not see a store into
@@ -157,9 +164,10 @@ __device__ __forceinline__ void emit4(float* p, const f32x4& v, int fold)
 // non-invariant comparison path (bi_gemm_run_splitk), where the caller picks
 // the split count per call.
 // What a dense kernel instance does: the product GEMM, the comparison
-// path's concurrent split-K, or the product GEMM of RMSNorm'd rows (x raw,
-// normalised in LDS before the MFMAs).
-enum Mode { kPlain = 0, kCmp = 1, kNormX = 2 };
+// path's concurrent split-K, the product GEMM of RMSNorm'd rows (x raw,
+// normalised in LDS before the MFMAs), or (streaming kernel) the product GEMM
+// of a call whose W is read exactly once, with non-temporal W loads.
+enum Mode { kPlain = 0, kCmp = 1, kNormX = 2, kStreamOnce = 3 };
 
 template <int kMode>
 __device__ __forceinline__ float* cmp_split(Split& sp, float* y, float* part, int M, int N)
@@ -1049,7 +1057,8 @@ struct StreamItem {
     const uint16_t* Wb;
 };
 
-template <int MB, int XR, int BKS, int NP, bool kIdx = false, int NT = 1>
+// kNtW: W loads are non-temporal (for calls that read every W line once).
+template <int MB, int XR, int BKS, int NP, bool kIdx = false, int NT = 1, bool kNtW = false>
 __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ W, float* __restrict__ y,
                                             int N, int K, Split sp, int tiles_n, int nitems,
@@ -1152,8 +1161,10 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
                 for (int j = 0; j < kI; ++j) {
                     const int u0 = (first + j) * 64;
                     const int k = sp.k0 + k_stage * BKS;
-                    dma16(u0 < kWR * kCh ? rW : rX, voff[j], u0 < kWR * kCh ? wpk_slab(k, N) : (uint32_t)k * 2,
-                          dst + u0);
+                    if (u0 < kWR * kCh)
+                        dma16<kNtW ? kCachePolicyNT : 0>(rW, voff[j], wpk_slab(k, N), dst + u0);
+                    else
+                        dma16(rX, voff[j], (uint32_t)k * 2, dst + u0);
                 }
                 ++k_stage;
             };
@@ -1246,8 +1257,8 @@ __global__ void __launch_bounds__((MB + NP) * 64)
     y = cmp_split<kMode>(sp, y, part, M, N);
     const int tiles_n = (N + 16 * NT - 1) / (16 * NT);
     const int mblocks = (M + 16 * MB - 1) / (16 * MB);
-    stream_body<MB, XR, BKS, NP, false, NT>(ring, x, W, y, N, K, sp, tiles_n, mblocks * tiles_n, M, nullptr,
-                                            nullptr);
+    stream_body<MB, XR, BKS, NP, false, NT, kMode == kStreamOnce>(ring, x, W, y, N, K, sp, tiles_n,
+                                                                  mblocks * tiles_n, M, nullptr, nullptr);
 }
 
 // Grouped: one m-block per expert whose row count c satisfies 0 < c <= cmax
@@ -1273,8 +1284,9 @@ __global__ void __launch_bounds__((MB + NP) * 64)
     }
     __syncthreads();
     const int tiles_n = N / 16;
-    stream_body<MB, XR, BKS, NP, kIdx>(ring, x, W, y, N, K, sp, tiles_n, count * tiles_n, 0, sh_off, elist, xidx,
-                                       xn);
+    // one m-block per expert: every W line the call loads is read once
+    stream_body<MB, XR, BKS, NP, kIdx, 1, true>(ring, x, W, y, N, K, sp, tiles_n, count * tiles_n, 0, sh_off,
+                                                elist, xidx, xn);
 }
 
 // ---------------------------------------------------------------------------
@@ -1352,10 +1364,24 @@ hipError_t run_stream(const void* W, const void* x, int M, float* y, int N, int 
         hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP, kCmp, NT>), dim3(grid, ex.ysplits), dim3(C::kThreads),
                            0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K,
                            sp, ex.part);
-    else
+    else {
+        // one 16-row m-block: each W line is read once, by one item, so the
+        // W loads are non-temporal (measured on the down-proj right after its
+        // M = 8192 call: M = 1 24.3 -> 20.6 us; on the 70B shard after
+        // M = 16384: M = 1 20.5 -> 11.9 us).  Wider m-blocks and strips keep
+        // the default policy (at M = 32 non-temporal W loads were 1% slower).
+        if constexpr (MB == 1 && NT == 1) {
+            if (M <= 16) {
+                hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP, kStreamOnce, NT>), dim3(grid), dim3(C::kThreads),
+                                   0, stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M,
+                                   N, K, sp, nullptr);
+                return hipGetLastError();
+            }
+        }
         hipLaunchKernelGGL((bigemm_stream<MB, XR, BKS, NP, kPlain, NT>), dim3(grid), dim3(C::kThreads), 0, stream,
                            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, M, N, K, sp,
                            nullptr);
+    }
     return hipGetLastError();
 }
 
