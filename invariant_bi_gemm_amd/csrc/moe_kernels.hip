@@ -271,6 +271,18 @@ __global__ void __launch_bounds__(256)
 // weight rows are packed 16 gate rows then the 16 matching up rows): g =
 // h[r][32(i/16) + i%16], u 16 columns after it.
 // ---------------------------------------------------------------------------
+// A 16-byte load with the non-temporal hint, for rows a kernel reads once
+// (the up projection's fp32 product in SwiGLU, the expert outputs in the
+// combine): streaming them then does not evict what stays in use.  Measured
+// on the layer at T = 4096: the combine 55.0 -> 48.8 us, interleaved on one
+// box.
+__device__ __forceinline__ float4 ld_once(const float4* p)
+{
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+    return float4{v[0], v[1], v[2], v[3]};
+}
+
 template <bool kInterleaved>
 __global__ void __launch_bounds__(256)
     swiglu(const float* __restrict__ h, int R, int I, uint16_t* __restrict__ a)
@@ -282,8 +294,8 @@ __global__ void __launch_bounds__(256)
         const int c = (int)(i % q4) * 4;
         const int cg = kInterleaved ? 32 * (c / 16) + c % 16 : c;
         const int cu = kInterleaved ? cg + 16 : I + c;
-        const float4 g = *reinterpret_cast<const float4*>(h + (size_t)r * 2 * I + cg);
-        const float4 u = *reinterpret_cast<const float4*>(h + (size_t)r * 2 * I + cu);
+        const float4 g = ld_once(reinterpret_cast<const float4*>(h + (size_t)r * 2 * I + cg));
+        const float4 u = ld_once(reinterpret_cast<const float4*>(h + (size_t)r * 2 * I + cu));
         const float gg[4] = {g.x, g.y, g.z, g.w};
         const float uu[4] = {u.x, u.y, u.z, u.w};
         *reinterpret_cast<uint2*>(a + (size_t)r * I + c) = bi::swiglu4(gg, uu);
@@ -340,8 +352,8 @@ __global__ void __launch_bounds__(256)
                 const int r = j0 + u < k ? s_row[j0 + u] : -1;
                 ok[u] = r >= 0 && r < R;
                 const float* row = o + (size_t)(ok[u] ? r : 0) * H + c;
-                v0[u] = ok[u] ? *reinterpret_cast<const float4*>(row) : float4{0.f, 0.f, 0.f, 0.f};
-                v1[u] = ok[u] && hi ? *reinterpret_cast<const float4*>(row + 256 * 4) : float4{0.f, 0.f, 0.f, 0.f};
+                v0[u] = ok[u] ? ld_once(reinterpret_cast<const float4*>(row)) : float4{0.f, 0.f, 0.f, 0.f};
+                v1[u] = ok[u] && hi ? ld_once(reinterpret_cast<const float4*>(row + 256 * 4)) : float4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u)
