@@ -747,16 +747,17 @@ const char* bi_rmsnorm_gemm_kernel_name(bi_gemm_t hh, int M)
 namespace {
 
 // y: the product (fp32 [R, N]); or, for a gated handle, a: the product with
-// SwiGLU applied (bf16 [R, N / 2]), y then NULL.
+// SwiGLU applied (bf16 [R, N / 2]), y then NULL, with max_rows the caller's
+// bound on any expert's rows (grouped_swiglu_fits).
 bi_status_t grouped_run(bi_gemm_t hh, const void* x, int xn, const int32_t* xidx, const int32_t* expert_offsets,
-                        int R, float* y, void* stream, void* a = nullptr)
+                        int R, float* y, void* stream, void* a = nullptr, int max_rows = 1 << 30)
 {
     bi_gemm* h = handle_of(hh);
     if (!h)
         return fail(BI_ERR_INVALID_ARGUMENT, "invalid handle");
     if (h->plan.experts == 0)
         return fail(BI_ERR_INVALID_ARGUMENT, "dense handle passed to bi_grouped_gemm_run");
-    if (a && (h->plan.gated_i == 0 || !bigemm::grouped_swiglu_fits(h->plan, R)))
+    if (a && (h->plan.gated_i == 0 || !bigemm::grouped_swiglu_fits(h->plan, R, max_rows)))
         return fail(BI_ERR_INVALID_ARGUMENT, "the fused SwiGLU needs a gated handle and a call it fits");
     if (R < 0)
         return fail(BI_ERR_INVALID_ARGUMENT, "R must be >= 0");
@@ -781,7 +782,7 @@ bi_status_t grouped_run(bi_gemm_t hh, const void* x, int xn, const int32_t* xidx
     bi_status_t st = check_run_device(h);
     if (st != BI_OK)
         return st;
-    hipError_t e = a ? bigemm::launch_grouped_swiglu(h->plan, h->W, x, expert_offsets, R, a, xidx, xn,
+    hipError_t e = a ? bigemm::launch_grouped_swiglu(h->plan, h->W, x, expert_offsets, R, a, xidx, xn, max_rows,
                                                      static_cast<hipStream_t>(stream))
                      : bigemm::launch_grouped(h->plan, h->W, x, expert_offsets, R, y, xidx, xn,
                                               static_cast<hipStream_t>(stream));
@@ -882,20 +883,22 @@ bi_status_t create_gated(int E, int I, int K, const void* W, bi_gemm_t* out)
     return create_common(E, 2 * I, K, W, nullptr, out, I);
 }
 
-bool swiglu_fits(bi_gemm_t hh, int R)
+bool swiglu_fits(bi_gemm_t hh, int R, int max_rows)
 {
     bi_gemm* h = handle_of(hh);
-    return h && h->plan.gated_i > 0 && grouped_swiglu_fits(h->plan, R);
+    return h && h->plan.gated_i > 0 && grouped_swiglu_fits(h->plan, R, max_rows);
 }
 
 bi_status_t run_swiglu_indexed(bi_gemm_t hh, const void* x, int x_rows, const int32_t* row_index,
-                               const int32_t* expert_offsets, int R, void* a, void* stream)
+                               const int32_t* expert_offsets, int R, int max_rows, void* a, void* stream)
 {
     if (R > 0 && !row_index)
         return fail(BI_ERR_INVALID_ARGUMENT, "row_index is NULL");
     if (R > 0 && !a)
         return fail(BI_ERR_INVALID_ARGUMENT, "a is NULL");
-    return grouped_run(hh, x, x_rows, R > 0 ? row_index : nullptr, expert_offsets, R, nullptr, stream, a);
+    if (max_rows < 1)
+        return fail(BI_ERR_INVALID_ARGUMENT, "max_rows must be >= 1");
+    return grouped_run(hh, x, x_rows, R > 0 ? row_index : nullptr, expert_offsets, R, nullptr, stream, a, max_rows);
 }
 
 }  // namespace bigemm

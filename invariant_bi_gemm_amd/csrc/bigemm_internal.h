@@ -103,13 +103,16 @@ const char* dense_norm_kernel_name(const Plan& p, int M);
 hipError_t launch_grouped(const Plan& p, const void* W, const void* x,
                           const int32_t* offsets, int R, float* y, const int32_t* xidx, int xn,
                           hipStream_t stream);
-// A gated handle's product with SwiGLU in the four-wave kernel's epilogue:
-// a [R, gated_i] bf16, a[r][c] = swiglu_bf16(gate, up) of the row's product
-// columns c and gated_i + c.  Only when grouped_swiglu_fits (one split, and
-// R large enough that every expert runs in the four-wave kernel).
-bool grouped_swiglu_fits(const Plan& p, int R);
+// A gated handle's product with SwiGLU in a kernel's epilogue: a [R,
+// gated_i] bf16, a[r][c] = swiglu_bf16(gate, up) of the row's product columns
+// c and gated_i + c.  Only when grouped_swiglu_fits (one split, and either
+// every expert has at most max_rows <= 16 rows -- the streaming kernel over
+// 32-row strips; an expert with more rows would be left unwritten, so the
+// caller must know the bound -- or R large enough that every expert runs in
+// the four-wave kernel).  x rows always through xidx.
+bool grouped_swiglu_fits(const Plan& p, int R, int max_rows);
 hipError_t launch_grouped_swiglu(const Plan& p, const void* W, const void* x, const int32_t* offsets, int R,
-                                 void* a, const int32_t* xidx, int xn, hipStream_t stream);
+                                 void* a, const int32_t* xidx, int xn, int max_rows, hipStream_t stream);
 
 // The MoE layer's gated up projection (bigemm_api.cpp): a grouped handle over
 // W [E, 2I, K] (gate rows 0..I-1, up rows I..2I-1) whose weights are packed
@@ -118,8 +121,8 @@ hipError_t launch_grouped_swiglu(const Plan& p, const void* W, const void* x, co
 // bi_grouped_gemm_run and _run_indexed work on it as on any grouped handle),
 // and its product with SwiGLU applied (a [R, I] bf16) when the call fits.
 bi_status_t create_gated(int E, int I, int K, const void* W, bi_gemm_t* out);
-bool swiglu_fits(bi_gemm_t h, int R);
+bool swiglu_fits(bi_gemm_t h, int R, int max_rows);
 bi_status_t run_swiglu_indexed(bi_gemm_t h, const void* x, int x_rows, const int32_t* row_index,
-                               const int32_t* expert_offsets, int R, void* a, void* stream);
+                               const int32_t* expert_offsets, int R, int max_rows, void* a, void* stream);
 
 }  // namespace bigemm

@@ -1058,7 +1058,11 @@ struct StreamItem {
 };
 
 // kNtW: W loads are non-temporal (for calls that read every W line once).
-template <int MB, int XR, int BKS, int NP, bool kIdx = false, int NT = 1, bool kNtW = false>
+// kSwiGLU (NT = 2, one split): W is a gated projection packed with the
+// gate/up row interleave (bigemm_pack_w), so a 32-row strip holds 16 gate
+// columns and their 16 up columns; the epilogue writes bf16 SwiGLU of each
+// pair, a [rows, N / 2] bf16 at y, instead of the fp32 product.
+template <int MB, int XR, int BKS, int NP, bool kIdx = false, int NT = 1, bool kNtW = false, bool kSwiGLU = false>
 __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ W, float* __restrict__ y,
                                             int N, int K, Split sp, int tiles_n, int nitems,
@@ -1236,11 +1240,24 @@ __device__ __forceinline__ void stream_body(uint4* ring, const uint16_t* __restr
             if ((q + 1) % nst == 0) {
                 const StreamItem s = item_at(q / nst);
                 const int m = s.m0 + 16 * ci + rw;
+                if constexpr (kSwiGLU) {
+                    static_assert(NT == 2, "a gate tile and its up tile");
+                    // gate columns n0/2 .. n0/2+15 of the strip; 4 per lane
+                    if (m < s.row_hi && s.n0 < N) {
+                        const float gg[4] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
+                        const float uu[4] = {acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
+                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + (size_t)m * (N / 2) + s.n0 / 2 +
+                                                  4 * (lane >> 4)) = bi::swiglu4(gg, uu);
+                    }
+                    acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                } else {
 #pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    if (m < s.row_hi && s.n0 + 16 * j < N)
-                        emit4(y + (size_t)m * N + s.n0 + 16 * j + 4 * (lane >> 4), acc[j], sp.fold);
-                    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int j = 0; j < NT; ++j) {
+                        if (m < s.row_hi && s.n0 + 16 * j < N)
+                            emit4(y + (size_t)m * N + s.n0 + 16 * j + 4 * (lane >> 4), acc[j], sp.fold);
+                        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
                 }
             }
         }
@@ -1262,14 +1279,15 @@ __global__ void __launch_bounds__((MB + NP) * 64)
 }
 
 // Grouped: one m-block per expert whose row count c satisfies 0 < c <= cmax
-// (cmax <= XR).  kIdx: x rows are read through xidx.
-template <int MB, int XR, int BKS, int NP, bool kIdx>
+// (cmax <= XR).  kIdx: x rows are read through xidx.  NT = 2 with kSwiGLU:
+// the gated projection's SwiGLU, bf16 [R, N / 2] at y (stream_body).
+template <int MB, int XR, int BKS, int NP, bool kIdx, int NT = 1, bool kSwiGLU = false>
 __global__ void __launch_bounds__((MB + NP) * 64)
     bigemm_stream_grouped(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
                           float* __restrict__ y, const int32_t* __restrict__ off, int E, int R,
                           int N, int K, Split sp, int cmax, const int32_t* __restrict__ xidx, int xn)
 {
-    using C = StreamCfg<MB, XR, BKS, NP>;
+    using C = StreamCfg<MB, XR, BKS, NP, NT>;
     __shared__ uint4 ring[C::NR * C::kStageUnits];
     __shared__ int sh_off[kMaxExperts + 1];
     __shared__ int first[kMaxExperts + 1];
@@ -1283,10 +1301,10 @@ __global__ void __launch_bounds__((MB + NP) * 64)
             elist[first[e]] = e;
     }
     __syncthreads();
-    const int tiles_n = N / 16;
+    const int tiles_n = (N + 16 * NT - 1) / (16 * NT);
     // one m-block per expert: every W line the call loads is read once
-    stream_body<MB, XR, BKS, NP, kIdx, 1, true>(ring, x, W, y, N, K, sp, tiles_n, count * tiles_n, 0, sh_off,
-                                                elist, xidx, xn);
+    stream_body<MB, XR, BKS, NP, kIdx, NT, true, kSwiGLU>(ring, x, W, y, N, K, sp, tiles_n, count * tiles_n, 0,
+                                                          sh_off, elist, xidx, xn);
 }
 
 // ---------------------------------------------------------------------------
@@ -1766,17 +1784,47 @@ GroupedSplit grouped_split(const Plan& p, int R)
 
 }  // namespace
 
-bool grouped_swiglu_fits(const Plan& p, int R)
+bool grouped_swiglu_fits(const Plan& p, int R, int max_rows)
 {
+    if (p.gated_i == 0 || p.splits != 1)
+        return false;
+    if (max_rows <= kTile)
+        return true;  // every expert streams (stream_swiglu)
     const GroupedSplit g = grouped_split(p, R);
-    return p.gated_i > 0 && p.splits == 1 && g.smax == 0 && g.big;
+    return g.smax == 0 && g.big;
 }
 
-hipError_t launch_grouped_swiglu(const Plan& p, const void* W, const void* x, const int32_t* offsets, int R,
-                                 void* a, const int32_t* xidx, int xn, hipStream_t stream)
+namespace {
+
+// The gated projection's SwiGLU when every expert has at most 16 rows: the
+// streaming kernel over 32-row strips (a gate tile and its up tile per
+// consumer), indexed x rows, the widest stage up to 256 that divides K.
+template <int BKS>
+hipError_t run_stream_swiglu(const void* W, const void* x, const int32_t* off, int E, int R, void* a, int N, int K,
+                             int num_cus, const int32_t* xidx, int xn, hipStream_t stream)
 {
-    if (!grouped_swiglu_fits(p, R))
+    constexpr int NP = stream_producers<1, BKS>();
+    using C = StreamCfg<1, 16, BKS, NP, 2>;
+    hipLaunchKernelGGL((bigemm_stream_grouped<1, 16, BKS, NP, true, 2, true>), dim3(num_cus), dim3(C::kThreads), 0,
+                       stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
+                       static_cast<float*>(a), off, E, R, N, K, Split{0, K, 0}, kTile, xidx, xn);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_grouped_swiglu(const Plan& p, const void* W, const void* x, const int32_t* offsets, int R,
+                                 void* a, const int32_t* xidx, int xn, int max_rows, hipStream_t stream)
+{
+    if (!grouped_swiglu_fits(p, R, max_rows) || !xidx)
         return hipErrorInvalidValue;
+    if (max_rows <= kTile) {
+        if (p.k % 256 == 0)
+            return run_stream_swiglu<256>(W, x, offsets, p.experts, R, a, p.n, p.k, p.num_cus, xidx, xn, stream);
+        if (p.k % 128 == 0)
+            return run_stream_swiglu<128>(W, x, offsets, p.experts, R, a, p.n, p.k, p.num_cus, xidx, xn, stream);
+        return run_stream_swiglu<64>(W, x, offsets, p.experts, R, a, p.n, p.k, p.num_cus, xidx, xn, stream);
+    }
     // one split, no streaming experts: every expert, whole, in the four-wave kernel
     return run_tiled4_grouped(W, x, offsets, p.experts, R, static_cast<float*>(a), p.n, p.k, Split{0, p.k, 0}, 0,
                               p.num_cus, xidx, xn, stream, true);

@@ -14,6 +14,11 @@ constexpr int kMaxTopK = 64;
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                        hipStream_t stream);
+// Both of the above in one launch, for 1 <= T <= kRouteMaxTokens: the same
+// ids, weights, offsets, rows and row_of.
+constexpr int kRouteMaxTokens = 8;
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* offsets,
+                        int32_t* tok, int32_t* row_of, hipStream_t stream);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* tok,
                           int32_t* row_of, hipStream_t stream);
 hipError_t launch_gather(const void* src, int nsrc, const int32_t* idx, int R, int K, void* dst,

@@ -39,15 +39,13 @@ __device__ __forceinline__ uint32_t order_key(float v)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Token t's top-k (one wave): lane j < k ends with the expert of rank j in
+// *e_out and its weight in *w_out.  Shared by moe_topk and moe_route, so both
+// give the same bits.
 template <int PL>  // logits per lane: E <= 64 * PL
-__global__ void __launch_bounds__(256)
-    moe_topk(const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
-             float* __restrict__ w)
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int k, int lane,
+                                           int* e_out, float* w_out)
 {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    if (t >= T)
-        return;  // whole waves only: t is the same for all 64 lanes
     float v[PL];
     uint32_t key[PL];  // 0 for slots past E: below every real key
 #pragma unroll
@@ -125,9 +123,25 @@ __global__ void __launch_bounds__(256)
     float s = 0.f;
     for (int j = 0; j < k; ++j)
         s = s + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), j));
+    *e_out = my_e;
+    *w_out = z / s;
+}
+
+template <int PL>  // logits per lane: E <= 64 * PL
+__global__ void __launch_bounds__(256)
+    moe_topk(const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+             float* __restrict__ w)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (t >= T)
+        return;  // whole waves only: t is the same for all 64 lanes
+    int e;
+    float ww;
+    topk_token<PL>(logits, t, E, k, lane, &e, &ww);
     if (lane < k) {
-        ids[(size_t)t * k + lane] = my_e;
-        w[(size_t)t * k + lane] = z / s;
+        ids[(size_t)t * k + lane] = e;
+        w[(size_t)t * k + lane] = ww;
     }
 }
 
@@ -244,6 +258,63 @@ __global__ void __launch_bounds__(kPermThreads)
                 ++r;
             }
         run += total;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Routing and grouping of a small batch in one launch (T <= kRouteMaxTokens,
+// one wave per token): each wave runs topk_token -- the code of moe_topk, so
+// the same ids and weights bit for bit -- and keeps the token's ids in LDS;
+// then the grouping of moe_permute over those T*k pairs: expert e's first row
+// is the number of pairs with a valid id below e, and a pair's row within its
+// expert the number of earlier pairs (in t*k + j order) with the same id.
+// Integer counts only, so offsets, rows and row_of are moe_permute's.
+// ---------------------------------------------------------------------------
+constexpr int kRouteThreads = 64 * kRouteMaxTokens;
+
+template <int PL>
+__global__ void __launch_bounds__(kRouteThreads)
+    moe_route(const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+              float* __restrict__ w, int32_t* __restrict__ offsets, int32_t* __restrict__ tok,
+              int32_t* __restrict__ row_of)
+{
+    __shared__ int s_id[kRouteMaxTokens * kMaxTopK];
+    __shared__ int s_first[kMaxExperts + 1];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int t = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = T * k;
+    if (t < T) {
+        int e;
+        float ww;
+        topk_token<PL>(logits, t, E, k, lane, &e, &ww);
+        if (lane < k) {
+            ids[(size_t)t * k + lane] = e;
+            w[(size_t)t * k + lane] = ww;
+            s_id[t * k + lane] = e;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e <= E; e += kRouteThreads) {
+        int c = 0;
+        for (int i = 0; i < n; ++i) {
+            const int x = s_id[i];
+            c += x >= 0 && x < e;
+        }
+        s_first[e] = c;
+        offsets[e] = c;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += kRouteThreads) {
+        const int x = s_id[i];
+        if (x < 0 || x >= E) {
+            row_of[i] = -1;
+            continue;
+        }
+        int r = s_first[x];
+        for (int j = 0; j < i; ++j)
+            r += s_id[j] == x;
+        tok[r] = i / k;
+        row_of[i] = r;
     }
 }
 
@@ -398,6 +469,25 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
         hipLaunchKernelGGL(moe_topk<8>, grid, block, 0, stream, logits, T, E, k, ids, w);
     else
         hipLaunchKernelGGL(moe_topk<16>, grid, block, 0, stream, logits, T, E, k, ids, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* offsets,
+                        int32_t* tok, int32_t* row_of, hipStream_t stream)
+{
+    if (T < 1 || T > kRouteMaxTokens)
+        return hipErrorInvalidValue;
+    const dim3 grid(1), block(kRouteThreads);
+    if (E <= 64)
+        hipLaunchKernelGGL(moe_route<1>, grid, block, 0, stream, logits, T, E, k, ids, w, offsets, tok, row_of);
+    else if (E <= 128)
+        hipLaunchKernelGGL(moe_route<2>, grid, block, 0, stream, logits, T, E, k, ids, w, offsets, tok, row_of);
+    else if (E <= 256)
+        hipLaunchKernelGGL(moe_route<4>, grid, block, 0, stream, logits, T, E, k, ids, w, offsets, tok, row_of);
+    else if (E <= 512)
+        hipLaunchKernelGGL(moe_route<8>, grid, block, 0, stream, logits, T, E, k, ids, w, offsets, tok, row_of);
+    else
+        hipLaunchKernelGGL(moe_route<16>, grid, block, 0, stream, logits, T, E, k, ids, w, offsets, tok, row_of);
     return hipGetLastError();
 }
 

@@ -403,10 +403,13 @@ def test_layer_parity(gpu, layer, tokens):
     assert rel <= 2.0 ** -12, "layer T=%d: median error %.3e of the rms" % (tokens, rel)
 
 
-# 255 and 256 tokens sit either side of 16 rows per expert (8 rows a token,
-# 128 experts), where the four-wave kernel takes every expert and the up
-# projection starts applying SwiGLU in its epilogue
-@pytest.mark.parametrize("tokens", [7, 255, 256, 1024, 4096])
+# 8 and 9 tokens sit either side of the one-launch routing and grouping;
+# 16 and 17 either side of the bound on an expert's rows (a token routes to
+# 8 distinct experts, so an expert has at most T rows) under which the
+# streaming kernel takes every expert and applies SwiGLU in its epilogue;
+# 255 and 256 either side of 16 rows per expert (8 rows a token, 128
+# experts), where the four-wave kernel takes every expert and applies it
+@pytest.mark.parametrize("tokens", [1, 7, 8, 9, 16, 17, 255, 256, 1024, 4096])
 def test_layer_equals_its_steps(gpu, layer, tokens):
     x = to_dev(synth.normal_bf16(400 + tokens, (tokens, H)))
     y = bits32(layer["layer"](x))
