@@ -31,9 +31,13 @@ KERNELS = {"_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi8ELi0E": [64],
            "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi5ELi1E": [40],
            "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi6ELi0E": [48],
            "_ZN6bigemm12_GLOBAL__N_113bigemm_tiled4ILi6ELi1E": [48],
-           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb0ELb0E": [64, 32],
-           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1ELb0E": [64, 32],
-           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1ELb1E": [64, 32]}
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb0ELb0ELb0E": [64, 32],
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1ELb0ELb0E": [64, 32],
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1ELb1ELb0E": [64, 32],
+           # the same with non-temporal W loads
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb0ELb0ELb1E": [64, 32],
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1ELb0ELb1E": [64, 32],
+           "_ZN6bigemm12_GLOBAL__N_121bigemm_tiled4_groupedILb1ELb1ELb1E": [64, 32]}
 MFMA_AGPR = re.compile(r"v_mfma_f32_16x16x32_bf16 a\[\d+:\d+\], v\[\d+:\d+\], v\[\d+:\d+\], (a\[\d+:\d+\]|0)$")
 AGPR = re.compile(r"\ba\d+\b|\ba\[\d+:\d+\]")
 

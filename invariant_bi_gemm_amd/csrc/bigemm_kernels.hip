@@ -95,11 +95,18 @@ __device__ __forceinline__ sgpr4 rsrc_words(const void* base, uint32_t bytes)
                  __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
                  __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
 }
+// kNt: the load carries the non-temporal bit (data read once).
+template <bool kNt = false>
 __device__ __forceinline__ void dma16_asm(const sgpr4& r, uint32_t voff, uint32_t soff, const void* lds_base)
 {
     const uint32_t m0v = (uint32_t)(uintptr_t)((lds_void*)lds_base);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0v)
-                 : "memory");
+    if constexpr (kNt)
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(r), "s"(soff),
+                     "{m0}"(m0v)
+                     : "memory");
+    else
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0v)
+                     : "memory");
 }
 
 // Packed weights.  A handle holds W (per expert) slab-major: slab s is the
@@ -743,7 +750,7 @@ constexpr int tiled4_read_at(int T)
 // (bigemm_pack_w), so W tiles 2t and 2t+1 of a wave hold 16 gate columns and
 // their up columns; the epilogue writes bf16 SwiGLU of each pair, a
 // [rows, N / 2] bf16 at y, instead of the fp32 product.
-template <int XT, bool kIdx = false, bool kSwiGLU = false>
+template <int XT, bool kIdx = false, bool kSwiGLU = false, bool kNtW = false>
 __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restrict__ x,
                                               const uint16_t* __restrict__ Wb, float* __restrict__ y, int m0,
                                               int row_hi, int n0, int N, int K, Split sp,
@@ -786,7 +793,7 @@ __device__ __forceinline__ void tiled4_block(uint4* lds, const uint16_t* __restr
         }
     }
     auto issueW = [&](int j, int t, int wbuf) {
-        dma16_asm(aW, voff[j], wpk_slab(sp.k0 + t * BK, N), lds + wbuf * kPart + (wave * 8 + j) * 64);
+        dma16_asm<kNtW>(aW, voff[j], wpk_slab(sp.k0 + t * BK, N), lds + wbuf * kPart + (wave * 8 + j) * 64);
     };
     auto issueX = [&](int j, int t, int xbuf) {
         dma16_asm(aX, voff[8 + j], (uint32_t)(sp.k0 + t * BK) * 2, lds + kXBase + xbuf * kXPart + (wave * XT + j) * 64);
@@ -926,7 +933,7 @@ __global__ void __launch_bounds__(256)
 // 128x256 block.  The tiles are cut into 8 contiguous ranges, one per XCD,
 // as in bigemm_tiled_grouped.  kIdx: x rows are read through xidx.
 // kSwiGLU: a gated projection's SwiGLU, bf16 [R, N / 2] at y (tiled4_block).
-template <bool kIdx, bool kSwiGLU = false>
+template <bool kIdx, bool kSwiGLU = false, bool kNtW = false>
 __global__ void __launch_bounds__(256)
     bigemm_tiled4_grouped(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ y,
                           const int32_t* __restrict__ off, int E, int R, int N, int K, Split sp, int tiles_n,
@@ -942,11 +949,11 @@ __global__ void __launch_bounds__(256)
         const int e = big_slot(off, E, R, cmin, t / tiles_n, &m0, &hi);
         barrier_after_lds_reads();  // every wave is done with the previous tile's stages
         if (hi - m0 <= 128)
-            tiled4_block<4, kIdx, kSwiGLU>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K, sp,
-                                           xidx, xn);
+            tiled4_block<4, kIdx, kSwiGLU, kNtW>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K,
+                                                 sp, xidx, xn);
         else
-            tiled4_block<8, kIdx, kSwiGLU>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K, sp,
-                                           xidx, xn);
+            tiled4_block<8, kIdx, kSwiGLU, kNtW>(lds, x, W + (size_t)e * N * K, y, m0, hi, (t % tiles_n) * 256, N, K,
+                                                 sp, xidx, xn);
     }
 }
 
@@ -1504,29 +1511,48 @@ hipError_t run_tiled_grouped(const void* W, const void* x, const int32_t* off, i
 
 // The 256-row blocks of the experts with more than cmin rows: one block
 // per CU (its LDS holds one), a multiple of 8.
+template <bool kIdx, bool kSwiGLU>
+hipError_t run_tiled4_grouped_nt(const void* W, const void* x, const int32_t* off, int E, int R, float* y, int N,
+                                 int K, Split sp, int cmin, int grid, int tiles_n, const int32_t* xidx, int xn,
+                                 bool nt, hipStream_t stream)
+{
+    if (nt)
+        hipLaunchKernelGGL((bigemm_tiled4_grouped<kIdx, kSwiGLU, true>), dim3(grid), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, off, E, R, N, K,
+                           sp, tiles_n, cmin, xidx, xn);
+    else
+        hipLaunchKernelGGL((bigemm_tiled4_grouped<kIdx, kSwiGLU, false>), dim3(grid), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, off, E, R, N, K,
+                           sp, tiles_n, cmin, xidx, xn);
+    return hipGetLastError();
+}
+
+// Non-temporal W loads when the experts average under 128 rows, so that each
+// of an expert's W tiles is read by a single block (and once), and a tile
+// streams at least 1 MB of W (K >= 2048).  Measured on the MoE shapes at
+// 2048 rows (16 per expert): the up projection (K = 2048) 157.7 -> 146.5 us,
+// the down projection (K = 768) 81.9 -> 84.5 us; at 32768 rows, where about
+// half the experts take two blocks, 296 -> 340 us and 187 -> 198 us.
+bool grouped_nt_w(int E, int R, int K) { return R < 128 * E && K >= 2048; }
+
 hipError_t run_tiled4_grouped(const void* W, const void* x, const int32_t* off, int E, int R, float* y, int N,
                               int K, Split sp, int cmin, int num_cus, const int32_t* xidx, int xn,
                               hipStream_t stream, bool swiglu = false)
 {
     const int tiles_n = (N + 255) / 256;
     const int grid = (num_cus + 7) / 8 * 8;
+    const bool nt = grouped_nt_w(E, R, K);
     if (swiglu) {  // the MoE layer's gated up projection: rows always indexed
         if (!xidx)
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL((bigemm_tiled4_grouped<true, true>), dim3(grid), dim3(256), 0, stream,
-                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, off, E, R, N, K,
-                           sp, tiles_n, cmin, xidx, xn);
-        return hipGetLastError();
+        return run_tiled4_grouped_nt<true, true>(W, x, off, E, R, y, N, K, sp, cmin, grid, tiles_n, xidx, xn, nt,
+                                                 stream);
     }
     if (xidx)
-        hipLaunchKernelGGL(bigemm_tiled4_grouped<true>, dim3(grid), dim3(256), 0, stream,
-                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, off, E, R, N, K,
-                           sp, tiles_n, cmin, xidx, xn);
-    else
-        hipLaunchKernelGGL(bigemm_tiled4_grouped<false>, dim3(grid), dim3(256), 0, stream,
-                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), y, off, E, R, N, K,
-                           sp, tiles_n, cmin, xidx, xn);
-    return hipGetLastError();
+        return run_tiled4_grouped_nt<true, false>(W, x, off, E, R, y, N, K, sp, cmin, grid, tiles_n, xidx, xn, nt,
+                                                  stream);
+    return run_tiled4_grouped_nt<false, false>(W, x, off, E, R, y, N, K, sp, cmin, grid, tiles_n, xidx, xn, nt,
+                                               stream);
 }
 
 // The tiled block shapes, largest first.  A shape comes in two depths: a
