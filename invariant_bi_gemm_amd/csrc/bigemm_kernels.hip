@@ -379,7 +379,9 @@ struct TiledCfg {
 // r = rstd[row] and g the gain of the stage's k range.  Each thread rewrites
 // one row's chunks, the same logical chunks in every wave, so the gain
 // arrives through scalar loads.
-template <int BM, int BN, int WM, int WN, int BK, int NS, bool kIdx = false, bool kNorm = false>
+// kNtW: the W loads are non-temporal (a call whose W strips are each read by
+// one block: a single m-block).
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool kIdx = false, bool kNorm = false, bool kNtW = false>
 __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ Wb,
                                             float* __restrict__ y, int m0, int row_hi, int n0,
@@ -435,8 +437,10 @@ __device__ __forceinline__ void tiled_block(uint4* lds, const uint16_t* __restri
         for (int j = 0; j < C::kInstr; ++j) {
             const int u0 = (wave * C::kInstr + j) * 64;
             const int k = sp.k0 + s * BK;
-            dma16(u0 < BN * kCh ? rW : rX, voff[j], u0 < BN * kCh ? wpk_slab(k, N) : (uint32_t)k * 2,
-                  lds + buf * C::kStageUnits + u0);
+            if (u0 < BN * kCh)
+                dma16<kNtW ? kCachePolicyNT : 0>(rW, voff[j], wpk_slab(k, N), lds + buf * C::kStageUnits + u0);
+            else
+                dma16(rX, voff[j], (uint32_t)k * 2, lds + buf * C::kStageUnits + u0);
         }
     };
 
@@ -655,8 +659,9 @@ __global__ void __launch_bounds__(WM * WN * 64)
     y = cmp_split<kMode>(sp, y, part, M, N);
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &tm, &tn);
-    tiled_block<BM, BN, WM, WN, BK, NS, false, kMode == kNormX>(lds, x, W, y, tm * BM, M, tn * BN, N, K, sp,
-                                                               nullptr, 0, rstd, gain);
+    tiled_block<BM, BN, WM, WN, BK, NS, false, kMode == kNormX, kMode == kStreamOnce>(lds, x, W, y, tm * BM, M,
+                                                                                     tn * BN, N, K, sp, nullptr, 0,
+                                                                                     rstd, gain);
 }
 
 // ---------------------------------------------------------------------------
@@ -1351,7 +1356,12 @@ hipError_t run_tiled(const void* W, const void* x, int M, float* y, int N, int K
                                stream, xx, ww, y, M, N, K, sp, tiles_m, tiles_n, 4, nullptr, ex.rstd, g);
         else
             return hipErrorInvalidValue;  // too shallow to normalise its tiles
-    } else
+    } else if (tiles_m == 1)
+        // one m-block: each W strip is read by one block, once (non-temporal
+        // loads; see the weight streamer's single-m-block calls)
+        hipLaunchKernelGGL((bigemm_tiled<BM, BN, WM, WN, BK, NS, kStreamOnce>), dim3(nblocks), dim3(C::kThreads), 0,
+                           stream, xx, ww, y, M, N, K, sp, tiles_m, tiles_n, 4, nullptr, nullptr, nullptr);
+    else
         hipLaunchKernelGGL((bigemm_tiled<BM, BN, WM, WN, BK, NS>), dim3(nblocks), dim3(C::kThreads), 0, stream, xx,
                            ww, y, M, N, K, sp, tiles_m, tiles_n, 4, nullptr, nullptr, nullptr);
     return hipGetLastError();
