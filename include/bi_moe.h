@@ -118,9 +118,12 @@ bi_status_t bi_moe_create(int E, int k, int H, int I, const void *W_router, cons
  * x and the weights only: the steps above, bit for bit as the step functions
  * and bi_grouped_gemm_run compute them.  (The layer packs W_up with its gate
  * and up rows interleaved 16 at a time; when the rows average at least 16 per
- * expert the up projection's epilogue applies SwiGLU in registers and writes
- * a directly.  Each product element keeps its tree and SwiGLU its arithmetic,
- * so neither changes a bit.)  One handle runs one call at a time: its
+ * expert, or no expert can have more than 16 rows (T <= 16: a token's k
+ * experts are distinct), the up projection's epilogue applies SwiGLU in
+ * registers and writes a directly; for T <= 8 one kernel does the top-k and
+ * the grouping.  Each product element keeps its tree, SwiGLU its arithmetic
+ * and the top-k and grouping their results, so none changes a bit.)  One
+ * handle runs one call at a time: its
  * workspace is shared by the calls, so calls on one handle must not overlap.
  */
 bi_status_t bi_moe_run(bi_moe_t h, const void *x, int T, float *y, void *stream);
