@@ -94,7 +94,10 @@ def test_grouped_run_graph_and_stream(gpu, t):
     check_graph_and_stream(lambda: gg(x, offd, out=y), [y], "grouped T=%d" % t)
 
 
-@pytest.mark.parametrize("t", [3, 512])
+# T = 3: routing and grouping in one kernel, SwiGLU in the streaming up
+# projection; T = 12: the two routing kernels, the same up projection;
+# T = 512: the four-wave up projection's SwiGLU epilogue
+@pytest.mark.parametrize("t", [3, 12, 512])
 def test_moe_layer_graph_and_stream(gpu, t):
     E, H, I, k = 16, 512, 256, 4
     wr = to_dev(synth.normal_bf16(510, (E, H), 0.02))
