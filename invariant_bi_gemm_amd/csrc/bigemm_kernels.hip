@@ -26,7 +26,9 @@
 //   bigemm_stream  small M: a persistent, warp-specialised weight streamer.
 //                  Up to seven producer waves keep a deep LDS ring of W (and
 //                  x) full with direct buffer->LDS loads; consumer waves run
-//                  the MFMA chain of one 16-column tile.  HBM bound.
+//                  the MFMA chains of a 16-, 32- or 64-column W strip.  HBM
+//                  bound; a call with one 16-row m-block reads each W line
+//                  once and loads W non-temporally.
 // Each has a grouped (MoE) variant whose per-expert row counts stay on the
 // device.  Every kernel reads W from the handle's packed copy (slab-major,
 // made at create by bigemm_pack_w); x and y are row-major.
